@@ -1,0 +1,216 @@
+"""Benchmark: decode of a LLaMA-2-70B-shaped model, layer by layer, on one
+MI355X.
+
+Workload: 80 layers, each with q,o 8192x8192, k,v 1024x8192, gate,up
+28672x8192, down 8192x28672 as Int8 codes (round(N(0, sigma)) clipped, sigma
+~ U[0.8, 3.0] per layer and tensor) plus per-row fp32 scales. Every layer is
+compressed (64-lane interleaved rANS, 65,536-symbol chunks) and all 80 stay
+resident in HBM; one step decodes all 80 layers, one launch per layer, into
+one reused bf16 layer buffer (decode happens before each block runs:
+EntQuant, "Float8@2bits ...", technical summary §2 "Decodificación en Tiempo
+de Inferencia"; per-block batching: DFloat11 write-up, "Descompresión por
+bloque transformer").
+
+Prints one JSON line (rank 0): decoded params/s over the timed steps, the
+roofline of the decode kernel (algorithmic bytes per launch / mean launch
+time from HIP events on the launch stream, against MI355X's 8 TB/s), and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decoded params/s and achieved HBM GB/s (% of peak) for 70B-shaped layer decode"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=80,
+                    help="layers in the model (80 is the workload; fewer only for quick checks)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tensors", type=int, default=5,
+                    help="tensors of layer 0 the oracle decodes for the CPU baseline")
+    ap.add_argument("--threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the decode has no cross-GPU step -- see DESIGN.md for how it shards", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    nthreads = args.threads or synth.default_threads()
+
+    # ---------------------------------------------------------------- setup
+    t0 = time.time()
+    plans, blobs, scales = [], [], []
+    params_per_layer = 0
+    layer_blob_bytes = []
+    cpu_sample = None
+    for layer in range(args.layers):
+        specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
+        b = E.encode_batch(specs, n_threads=nthreads)
+        blob = torch.from_numpy(b.blob).to(dev)
+        sc = torch.from_numpy(np.concatenate([s["scales"] for s in specs])).to(dev)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+        plans.append(p)
+        blobs.append(blob)
+        scales.append(sc)
+        layer_blob_bytes.append(int(b.blob.size))
+        params_per_layer = b.out_elems
+        if layer == 0 and not args.no_cpu_baseline:
+            cpu_sample = (specs[:args.cpu_sample_tensors], b)
+        if layer % 10 == 0 or layer == args.layers - 1:
+            log(f"layer {layer} ready ({time.time() - t0:.1f}s, {b.blob.size / 1e6:.1f} MB "
+                f"compressed, {8.0 * b.blob.size / b.out_elems:.3f} bits/param)")
+    torch.cuda.synchronize()
+    n_chunks_layer = int(plans[0].n_chunks)
+    scale_bytes_layer = int(scales[0].numel()) * 4
+    out = torch.empty(params_per_layer, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for layer in range(args.layers):
+            if events is not None:
+                events[layer][0].record(stream)
+            E.decode(plans[layer], blobs[layer], out, E.OUT_BF16, scales[layer], None, stream)
+            if events is not None:
+                events[layer][1].record(stream)
+
+    # ---------------------------------------------------------------- timing
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(args.layers)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    launch_ms = np.array([[e[0].elapsed_time(e[1]) for e in ev[s]] for s in range(args.steps)])
+    ms_per_step = total_ms / args.steps
+    params_total = params_per_layer * args.layers
+    value = params_total / (ms_per_step / 1e3)
+
+    # algorithmic bytes of one launch (one layer): compressed payload (states,
+    # words, padding) + scales read + bf16 written
+    blob_mean = float(np.mean(layer_blob_bytes))
+    alg_bytes_layer = blob_mean + scale_bytes_layer + 2.0 * params_per_layer
+    mean_launch_s = float(launch_ms.mean()) / 1e3
+    achieved_gbs = alg_bytes_layer / mean_launch_s / 1e9
+    log(f"{args.steps} steps x {args.layers} layers: {ms_per_step:.3f} ms/step "
+        f"(wall {1e3 * t_wall / args.steps:.3f}), launch mean {1e3 * mean_launch_s:.1f} us "
+        f"p10 {1e3 * np.percentile(launch_ms, 10) / 1e3:.1f} p90 "
+        f"{1e3 * np.percentile(launch_ms, 90) / 1e3:.1f} us, {achieved_gbs:.0f} GB/s")
+
+    # ---------------------------------------------------------- CPU baseline
+    cpu = None
+    if cpu_sample is not None:
+        cpu = cpu_baseline(cpu_sample, plans[0], blobs[0], scales[0], out, stream)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f32->bf16",
+        "data": "synthetic (seeded int8 codes of the stated distribution; no trained weights)",
+        "config": {
+            "workload": "llama2-70b-shaped layer-by-layer decode, int8 rANS codes -> bf16 with per-row fp32 scale",
+            "layers": args.layers,
+            "params_per_layer": params_per_layer,
+            "chunk_symbols": 65536,
+            "chunks_per_layer": n_chunks_layer,
+            "compressed_bytes_per_layer": blob_mean,
+            "bits_per_param": 8.0 * blob_mean / params_per_layer,
+            "algorithmic_bytes_per_layer": alg_bytes_layer,
+            "hbm_gbs_whole_step": alg_bytes_layer * args.layers / (ms_per_step / 1e3) / 1e9,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
+    """The oracle (single-threaded C) decoding + dequantising the first
+    tensors of layer 0 from the same compressed bytes, timed on this host.
+    Its output is also compared with the GPU's for those tensors."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import oracle
+
+    specs, b = sample
+    E.decode(plan0, blob0, out_gpu, E.OUT_BF16, scales0, None, stream)
+    torch.cuda.synchronize()
+    n_sample = sum(s["rows"] * s["cols"] for s in specs)
+    gpu = out_gpu[:n_sample].cpu().numpy().view(np.uint16)
+    t = time.perf_counter()
+    outs = []
+    for ti, sp in enumerate(specs):
+        sel = b.chunks["tensor"] == ti
+        ch = b.chunks[sel]
+        desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"], ch["elem_offset"]],
+                        axis=1).astype(np.uint64)
+        sym, st = oracle.decode_tensor(b.blob, desc, b.freq[ti], sp["rows"] * sp["cols"])
+        assert np.all(st == 0)
+        outs.append(oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"]))
+    dt = time.perf_counter() - t
+    ok = bool(np.array_equal(np.concatenate(outs), gpu))
+    log(f"cpu oracle: {n_sample} params in {dt:.2f}s ({n_sample / dt / 1e6:.1f} M params/s); "
+        f"matches GPU: {ok}")
+    if not ok:
+        raise SystemExit("GPU output differs from the oracle on the CPU-baseline sample")
+    return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, first {len(specs)} tensors ({n_sample} params): single-threaded "
+                      "C oracle rANS decode + fp32 dequant + RNE bf16 from the same compressed bytes"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+"""Entropy-coded weight decoding on AMD MI355X (gfx950).
+
+A thin ctypes binding of ``libentq.so`` (built from ``csrc/`` by
+``build.build()``): argument marshalling only. Every step of the decode runs
+in the library's HIP kernels; the host encoder is the library's multi-threaded
+C++. PyTorch supplies device memory and streams. There is no fallback: if
+the library is missing, importing the decode entry points fails loudly.
+
+Entry points (the C ABI in include/entq.h, same names):
+  plan(...)               -> Plan     validate a batch, build device tables
+  decode(...)                         rANS decode to codes or bf16 (fused
+                                      per-row fp32 scale, RNE)
+  decode_bf16_split(...)              exponent stream + raw sign/mantissa
+                                      bytes -> bit-exact bf16
+  count_symbols, build_freq, encode_tensor, bf16_split   host encoder
+  encode_batch(...)       -> Batch    convenience: a list of tensors -> blob,
+                                      tables, chunk index
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libentq.so")
+
+KIND_INT8, KIND_E4M3, KIND_BF16EXP = 0, 1, 2
+OUT_CODES, OUT_BF16 = 0, 1
+CHUNK_OK, CHUNK_BAD_STATE, CHUNK_BAD_WORDS = 0, 1, 2
+PROB_SCALE = 4096
+
+TENSOR_DESC = np.dtype([("kind", "<u4"), ("rows", "<u4"), ("cols", "<u4"),
+                        ("chunk_symbols", "<u4"), ("n_symbols", "<u8"),
+                        ("out_elem_offset", "<u8"), ("scale_row_offset", "<u8")])
+CHUNK_DESC = np.dtype([("tensor", "<u4"), ("n_symbols", "<u4"), ("n_words", "<u4"),
+                       ("reserved", "<u4"), ("byte_offset", "<u8"), ("elem_offset", "<u8")])
+assert TENSOR_DESC.itemsize == 40 and CHUNK_DESC.itemsize == 32
+
+
+class EntqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_str(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libentq.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "entropy_coded_weight_amd.build.build() (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        vp, u64, i64 = c.c_void_p, c.c_uint64, c.c_int64
+        sigs = {
+            "entq_plan_workspace_bytes": (c.c_size_t, [c.c_int, i64]),
+            "entq_plan": (c.c_int, [vp, c.c_int, vp, vp, i64, u64, vp, c.c_size_t, vp,
+                                    c.POINTER(vp)]),
+            "entq_decode": (c.c_int, [vp, vp, vp, c.c_int, vp, vp, vp]),
+            "entq_decode_bf16_split": (c.c_int, [vp, vp, vp, vp, vp, vp]),
+            "entq_plan_destroy": (None, [vp]),
+            "entq_status_str": (c.c_char_p, [c.c_int]),
+            "entq_plan_info": (c.c_int, [vp, vp, vp, vp, vp, vp]),
+            "entq_count_symbols": (c.c_int, [vp, u64, vp, c.c_int]),
+            "entq_build_freq": (c.c_int, [vp, vp]),
+            "entq_encode_bound": (u64, [u64, c.c_uint32]),
+            "entq_encode_tensor": (c.c_int, [vp, u64, c.c_uint32, vp, c.c_uint32, u64, vp, u64,
+                                             vp, vp, c.c_int]),
+            "entq_bf16_split": (c.c_int, [vp, u64, vp, vp, c.c_int]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decode_bf16_split",
+            "entq_plan_destroy", "entq_status_str", "entq_plan_info", "entq_count_symbols",
+            "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split"]
+
+
+def _str(status: int) -> str:
+    try:
+        return lib().entq_status_str(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "unknown"
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise EntqError(status, what)
+
+
+def _ptr(a) -> int:
+    """Address of a numpy array or a torch tensor (host or device)."""
+    if a is None:
+        return 0
+    if isinstance(a, np.ndarray):
+        assert a.flags["C_CONTIGUOUS"]
+        return a.ctypes.data
+    assert a.is_contiguous()
+    return a.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# --------------------------------------------------------------------------
+# plan and decode
+# --------------------------------------------------------------------------
+
+class Plan:
+    """A validated batch with its device workspace (a torch uint8 tensor that
+    this object keeps alive)."""
+
+    def __init__(self, tensors: np.ndarray, freq_tables: np.ndarray, chunk_index: np.ndarray,
+                 blob_bytes: int, device="cuda", stream=None):
+        import torch
+        tensors = np.ascontiguousarray(tensors, dtype=TENSOR_DESC)
+        chunk_index = np.ascontiguousarray(chunk_index, dtype=CHUNK_DESC)
+        freq_tables = np.ascontiguousarray(freq_tables, dtype=np.uint16).reshape(-1, 256)
+        assert freq_tables.shape[0] == tensors.shape[0]
+        n_t, n_c = int(tensors.shape[0]), int(chunk_index.shape[0])
+        ws_bytes = int(lib().entq_plan_workspace_bytes(n_t, n_c))
+        raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=device)
+        shift = (-raw.data_ptr()) % 256
+        self.workspace = raw[shift:shift + ws_bytes]
+        self._raw = raw
+        h = ctypes.c_void_p()
+        st = lib().entq_plan(_ptr(tensors) if n_t else None, n_t,
+                             _ptr(freq_tables) if n_t else None,
+                             _ptr(chunk_index) if n_c else None, n_c, int(blob_bytes),
+                             self.workspace.data_ptr(), ws_bytes, _stream(stream),
+                             ctypes.byref(h))
+        _check(st, "entq_plan")
+        self._h = h
+        self.n_tensors, self.n_chunks = n_t, n_c
+        self.tensors = tensors
+        self.blob_bytes = int(blob_bytes)
+        oe, sr, nc, nt_, bb = (ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_int64(),
+                               ctypes.c_int(), ctypes.c_uint64())
+        _check(lib().entq_plan_info(h, ctypes.byref(oe), ctypes.byref(sr), ctypes.byref(nc),
+                                    ctypes.byref(nt_), ctypes.byref(bb)), "entq_plan_info")
+        self.out_elems, self.scale_rows = int(oe.value), int(sr.value)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().entq_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def plan(tensors, freq_tables, chunk_index, blob_bytes, device="cuda", stream=None) -> Plan:
+    return Plan(tensors, freq_tables, chunk_index, blob_bytes, device, stream)
+
+
+def decode(p: Plan, compressed, out, out_kind: int, scales=None, chunk_status=None,
+           stream=None):
+    """Enqueue the decode of every chunk of ``p`` on ``stream``. All buffers
+    are device tensors: compressed (uint8, the blob), out (uint8 for
+    OUT_CODES, bf16/int16/uint16 for OUT_BF16), scales (float32),
+    chunk_status (int32 [n_chunks]) or None."""
+    st = lib().entq_decode(p.handle, _ptr(compressed), _ptr(out), int(out_kind),
+                           _ptr(scales) or None, _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode")
+
+
+def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):
+    st = lib().entq_decode_bf16_split(p.handle, _ptr(exp_stream), _ptr(signmant), _ptr(out),
+                                      _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_bf16_split")
+
+
+# --------------------------------------------------------------------------
+# host encoder
+# --------------------------------------------------------------------------
+
+def count_symbols(symbols: np.ndarray, n_threads: int | None = None) -> np.ndarray:
+    symbols = np.ascontiguousarray(symbols).view(np.uint8).ravel()
+    counts = np.zeros(256, np.uint64)
+    _check(lib().entq_count_symbols(_ptr(symbols) if symbols.size else None, symbols.size,
+                                    _ptr(counts), n_threads or default_threads()),
+           "entq_count_symbols")
+    return counts
+
+
+def build_freq(counts: np.ndarray) -> np.ndarray:
+    counts = np.ascontiguousarray(counts, dtype=np.uint64)
+    freq = np.zeros(256, np.uint16)
+    _check(lib().entq_build_freq(_ptr(counts), _ptr(freq)), "entq_build_freq")
+    return freq
+
+
+def encode_tensor(symbols: np.ndarray, chunk_symbols: int, freq: np.ndarray, tensor_id: int = 0,
+                  base_offset: int = 0, n_threads: int | None = None):
+    """Returns (region bytes uint8, chunk descriptors CHUNK_DESC)."""
+    symbols = np.ascontiguousarray(symbols).view(np.uint8).ravel()
+    freq = np.ascontiguousarray(freq, dtype=np.uint16)
+    n = symbols.size
+    cap = int(lib().entq_encode_bound(n, chunk_symbols))
+    out = np.empty(max(cap, 16), np.uint8)
+    k = -(-n // chunk_symbols)
+    chunks = np.zeros(max(k, 1), CHUNK_DESC)
+    written = ctypes.c_uint64()
+    _check(lib().entq_encode_tensor(_ptr(symbols) if n else None, n, chunk_symbols, _ptr(freq),
+                                    tensor_id, base_offset, _ptr(out), out.size, _ptr(chunks),
+                                    ctypes.byref(written), n_threads or default_threads()),
+           "entq_encode_tensor")
+    return out[:written.value], chunks[:k]
+
+
+def bf16_split(words: np.ndarray, n_threads: int | None = None):
+    words = np.ascontiguousarray(words).view(np.uint16).ravel()
+    e = np.empty(words.size, np.uint8)
+    sm = np.empty(words.size, np.uint8)
+    _check(lib().entq_bf16_split(_ptr(words) if words.size else None, words.size,
+                                 _ptr(e) if words.size else None,
+                                 _ptr(sm) if words.size else None,
+                                 n_threads or default_threads()), "entq_bf16_split")
+    return e, sm
+
+
+@dataclass
+class Batch:
+    """A batch of tensors in compressed form, as entq_plan consumes it."""
+    blob: np.ndarray            # uint8, all chunk regions
+    tensors: np.ndarray         # TENSOR_DESC
+    freq: np.ndarray            # uint16 [n_tensors, 256]
+    chunks: np.ndarray          # CHUNK_DESC
+
+    @property
+    def out_elems(self) -> int:
+        t = self.tensors
+        return int((t["out_elem_offset"] + t["n_symbols"]).max()) if t.size else 0
+
+    @property
+    def scale_rows(self) -> int:
+        t = self.tensors
+        return int((t["scale_row_offset"] + t["rows"]).max()) if t.size else 0
+
+
+def encode_batch(specs, n_threads: int | None = None) -> Batch:
+    """specs: list of dicts {kind, rows, cols, chunk_symbols, symbols (uint8
+    codes or exponent bytes, rows*cols)}. Tensors are laid out one after the
+    other in the output and in the scale array; each gets its own table."""
+    regions, descs = [], []
+    tens = np.zeros(len(specs), TENSOR_DESC)
+    freqs = np.zeros((len(specs), 256), np.uint16)
+    off = out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        sym = np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()
+        rows, cols, C = int(sp["rows"]), int(sp["cols"]), int(sp["chunk_symbols"])
+        assert sym.size == rows * cols
+        f = build_freq(count_symbols(sym, n_threads))
+        if sym.size == 0:
+            f[0] = PROB_SCALE
+        r, ch = encode_tensor(sym, C, f, t, off, n_threads)
+        regions.append(r)
+        descs.append(ch)
+        off += r.size
+        tens[t] = (int(sp["kind"]), rows, cols, C, sym.size, out_off, scale_off)
+        freqs[t] = f
+        out_off += sym.size
+        scale_off += rows
+    blob = np.concatenate(regions) if regions else np.zeros(0, np.uint8)
+    chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
+    return Batch(blob, tens, freqs, chunks)

@@ -1,0 +1,84 @@
+// entq_internal.h -- layouts shared by the host plan builder and the HIP
+// kernels of libentq (never by the CPU oracle).
+#pragma once
+
+#include <stdint.h>
+
+#include "entq.h"
+
+namespace entq {
+
+constexpr uint32_t kProbBits = 12;
+constexpr uint32_t kProbScale = 1u << kProbBits;   // M
+constexpr uint32_t kLanes = 64;                    // interleaved states per chunk
+constexpr uint32_t kStateLow = 1u << 16;           // L
+constexpr uint32_t kStateBytes = 4 * kLanes;       // states at the start of a region
+constexpr uint32_t kMaxChunkSymbols = 1u << 20;
+
+// Workgroup shape of the decode kernels: kWaves waves, each decoding one
+// chunk; all chunks of a workgroup belong to one tensor so they share the
+// slot table held in LDS.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
+// Slot table entry, one per slot (4096 per tensor), 8 bytes:
+//   lo = f | sym << 24   (f = frequency of the owning symbol, 1..4096, in
+//                         bits 0..12; bits 13..23 are zero so that a 24-bit
+//                         multiply by lo multiplies by f alone)
+//   hi = slot - cum[sym] (the additive term of the decode step)
+struct SlotEntry {
+    uint32_t lo;
+    uint32_t hi;
+};
+
+struct DevTensor {
+    uint32_t cols;
+    uint32_t kind;
+    uint32_t pad0, pad1;
+};
+
+struct DevChunk {
+    uint64_t byte_offset;   // region start in the blob
+    uint64_t out_elem;      // absolute output index of the chunk's first symbol
+    uint64_t scale_row;     // absolute scale index of the chunk's first symbol
+    uint32_t col0;          // column of the chunk's first symbol
+    uint32_t n_symbols;
+    uint32_t n_words;
+    uint32_t status_index;  // position in the caller's chunk index
+    uint32_t tensor;
+    uint32_t pad;
+};
+static_assert(sizeof(DevChunk) == 48, "DevChunk layout");
+
+struct DevTask {
+    uint32_t first_chunk;   // into the plan's DevChunk array
+    uint32_t n_chunks;      // 1 .. kWaves, all of the same tensor
+    uint32_t tensor;
+    uint32_t pad;
+};
+
+}  // namespace entq
+
+// The host-side plan object behind the opaque C handle.
+struct entq_plan_s {
+    int n_tensors;
+    int64_t n_chunks;
+    int64_t n_tasks;
+    uint64_t blob_bytes;
+    uint64_t out_elems;
+    uint64_t scale_rows;
+    uint32_t kinds_mask;        // bit k set if some non-empty tensor has kind k
+    const entq::SlotEntry *d_tables;
+    const entq::DevTensor *d_tensors;
+    const entq::DevChunk *d_chunks;
+    const entq::DevTask *d_tasks;
+    void *host_staging;         // kept alive until destroy (async copy source)
+};
+
+// Launchers implemented in entq_decode.hip.
+namespace entq {
+enum DecodeMode { kModeCodes = 0, kModeBf16 = 1, kModeSplit = 2 };
+int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
+                  const float *scales, const uint8_t *signmant, int32_t *status,
+                  void *stream);
+}  // namespace entq

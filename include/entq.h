@@ -1,0 +1,209 @@
+/*
+ * entq.h -- C ABI of the MI355X entropy-coded weight decoder (libentq.so).
+ *
+ * What is decoded. Weights are stored as 8-bit codes of a full-range base
+ * format (Int8 or Float8 e4m3) that have been flattened into a symbol stream
+ * and compressed without loss by an ANS entropy coder, next to per-channel
+ * (per-row) scales and metadata; the decoder runs on the GPU and fills a
+ * buffer just before a transformer block's forward pass uses it [EntQuant,
+ * "Float8@2bits: Entropy Coding Enables Data-Free Model Compression",
+ * technical summary §2 "Codificación de Pesos" and "Decodificación en Tiempo
+ * de Inferencia"]. The same decoder also serves BF16 weights whose 8-bit
+ * exponent is the coded symbol while the sign+mantissa byte is stored raw,
+ * rebuilt bit for bit [DFloat11 write-up, "Formato DFloat11"]. All matrices
+ * of one block are decoded in one batch [DFloat11 write-up, "Descompresión
+ * por bloque transformer"].
+ *
+ * Coder (range ANS, Duda 2013, with interleaved states, Giesen 2014; the
+ * pages give no coder parameters, these are the library's format):
+ *   - probability scale M = 2^12: a tensor's table freq[256] sums to 4096;
+ *   - 32-bit state in [2^16, 2^32), 16-bit renormalisation words;
+ *   - a tensor is cut into chunks of chunk_symbols symbols (the last one may
+ *     be shorter); symbol i of a chunk belongs to lane i mod 64 of 64
+ *     interleaved states; the lanes share one word stream, read front to back
+ *     and, within a step of 64 symbols, in ascending lane order.
+ *   Decoding symbol i (lane j): slot = x_j & 4095, s = owner of the slot
+ *   (cum[s] <= slot < cum[s] + f[s]), x_j = f[s] * (x_j >> 12) + slot -
+ *   cum[s]; then if x_j < 2^16, x_j = x_j << 16 | next word.
+ *
+ * Compressed layout (the "blob"), one region per chunk:
+ *   uint32 states[64]   initial decoder state of lane j at index j
+ *   uint16 words[n]     the chunk's word stream, in decoding order
+ *   zero padding to a multiple of 16 bytes
+ * all little-endian; every region starts at a multiple of 16 bytes.
+ *
+ * Outputs:
+ *   ENTQ_OUT_CODES  uint8  out[i] = the decoded code byte;
+ *   ENTQ_OUT_BF16   uint16 out[i] = RNE_bf16( fl32( value(code) * scale[row] ) )
+ *                   where value is the two's-complement integer (INT8) or
+ *                   the OCP e4m3 ("E4M3FN") value (E4M3), the product is
+ *                   one IEEE single multiply rounded to nearest even, and
+ *                   RNE_bf16 rounds to nearest even (a NaN stays a quiet NaN
+ *                   with its sign and top payload bits);
+ *   entq_decode_bf16_split: uint16 out[i] = (sm & 0x80) << 8 | exp << 7 |
+ *                   (sm & 0x7F), exp the decoded symbol, sm the raw byte.
+ *
+ * Ownership: every device buffer is allocated by the caller; the library
+ * never allocates device memory. A plan is host memory owned by the library
+ * until entq_plan_destroy; it points into the caller's device workspace,
+ * which must outlive the plan and every decode enqueued with it.
+ * Asynchrony: device work is enqueued on the given HIP stream (NULL = the
+ * default stream); no call synchronises. Errors: argument, table, index and
+ * alignment problems and launch failures return a negative entq_status;
+ * corrupt compressed data is reported per chunk through chunk_status (after
+ * the stream is synchronised). No exception crosses this interface.
+ */
+#ifndef ENTQ_H
+#define ENTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENTQ_PROB_BITS 12
+#define ENTQ_PROB_SCALE 4096u
+#define ENTQ_LANES 64u
+#define ENTQ_STATE_LOW 65536u
+#define ENTQ_REGION_ALIGN 16u
+
+typedef enum {
+    ENTQ_OK = 0,
+    ENTQ_EINVAL = -1,       /* a NULL pointer, a bad size or kind           */
+    ENTQ_EBADTABLE = -2,    /* a frequency table does not sum to 4096       */
+    ENTQ_EBADINDEX = -3,    /* chunk index does not tile the tensors        */
+    ENTQ_EALIGN = -4,       /* a region or buffer is misaligned             */
+    ENTQ_EWORKSPACE = -5,   /* workspace too small                          */
+    ENTQ_EHIP = -6,         /* a HIP call or kernel launch failed           */
+    ENTQ_ENOMEM = -7,       /* host allocation failed                       */
+    ENTQ_ESYMBOL = -8       /* encoder: a symbol has frequency 0            */
+} entq_status;
+
+typedef enum { ENTQ_SYM_INT8 = 0, ENTQ_SYM_E4M3 = 1, ENTQ_SYM_BF16EXP = 2 } entq_symkind;
+typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
+
+/* Per-chunk decode status written to chunk_status[k] (k = position in the
+ * chunk index given to entq_plan). */
+#define ENTQ_CHUNK_OK 0
+#define ENTQ_CHUNK_BAD_STATE 1  /* a lane did not end at 2^16              */
+#define ENTQ_CHUNK_BAD_WORDS 2  /* words ran out or were not all consumed  */
+
+/* One tensor of a batch (40 bytes). rows x cols row-major; n_symbols must be
+ * rows * cols. Output element i of the tensor goes to out[out_elem_offset +
+ * i]; its scale is scales[scale_row_offset + i / cols]. */
+typedef struct {
+    uint32_t kind;            /* entq_symkind                                */
+    uint32_t rows, cols;
+    uint32_t chunk_symbols;   /* C: a positive multiple of 64, <= 2^20       */
+    uint64_t n_symbols;
+    uint64_t out_elem_offset;
+    uint64_t scale_row_offset;
+} entq_tensor_desc;
+
+/* One chunk (32 bytes): symbols [elem_offset, elem_offset + n_symbols) of
+ * tensor `tensor`, its region at byte_offset in the blob. */
+typedef struct {
+    uint32_t tensor;
+    uint32_t n_symbols;       /* 1 .. chunk_symbols                          */
+    uint32_t n_words;         /* <= n_symbols                                */
+    uint32_t reserved;        /* 0                                           */
+    uint64_t byte_offset;     /* multiple of 16                              */
+    uint64_t elem_offset;     /* k * chunk_symbols for the tensor's chunk k  */
+} entq_chunk_desc;
+
+/* Opaque plan handle (host memory owned by the library). */
+typedef struct entq_plan_s entq_plan_t;
+
+/* Bytes of device workspace a plan over n_tensors tensors and n_chunks
+ * chunks needs. */
+size_t entq_plan_workspace_bytes(int n_tensors, int64_t n_chunks);
+
+/* Validates the batch and builds the decoder's device-side tables and chunk
+ * lists in d_workspace (copied on `stream`).
+ *   tensors      host [n_tensors]
+ *   freq_tables  host [n_tensors][256]; each table of a non-empty tensor must
+ *                sum to 4096 and give every coded symbol a nonzero entry
+ *   chunk_index  host [n_chunks]: the chunks of every tensor must tile
+ *                [0, n_symbols) exactly (any order); regions must lie inside
+ *                [0, blob_bytes)
+ *   blob_bytes   size of the compressed buffer later passed to decode
+ *   d_workspace  device, >= entq_plan_workspace_bytes(), 256-byte aligned
+ * Checks also that tensor outputs do not overlap. Returns ENTQ_OK and a new
+ * plan in *out, or an error and *out = NULL. Host inputs may be freed after
+ * return. */
+entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors,
+                      const uint16_t *freq_tables,
+                      const entq_chunk_desc *chunk_index, int64_t n_chunks,
+                      uint64_t blob_bytes,
+                      void *d_workspace, size_t workspace_bytes, void *stream,
+                      entq_plan_t **out);
+
+/* Decodes every chunk of the plan in one launch.
+ *   d_compressed  device blob (16-byte aligned, blob_bytes long)
+ *   d_out         device; uint8 [total] for ENTQ_OUT_CODES, uint16 (bf16
+ *                 bit patterns) [total] for ENTQ_OUT_BF16, where total =
+ *                 max(out_elem_offset + n_symbols) over tensors; 16-byte
+ *                 aligned
+ *   d_scales      device fp32, required for ENTQ_OUT_BF16 (INT8 and E4M3
+ *                 tensors only; BF16EXP tensors need entq_decode_bf16_split),
+ *                 ignored for ENTQ_OUT_CODES
+ *   d_chunk_status device int32 [n_chunks] or NULL */
+entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void *d_out,
+                        entq_outkind out_kind, const float *d_scales,
+                        int32_t *d_chunk_status, void *stream);
+
+/* Decodes a plan whose tensors are all ENTQ_SYM_BF16EXP into bf16 words:
+ * the coded exponent bytes come from d_exp_stream (the blob), the raw
+ * sign+mantissa byte of output element i is d_signmant[i] (same indexing as
+ * d_out). d_out is 16-byte aligned, d_signmant 8-byte aligned. */
+entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
+                                   const uint8_t *d_signmant, uint16_t *d_out,
+                                   int32_t *d_chunk_status, void *stream);
+
+void entq_plan_destroy(entq_plan_t *plan);
+
+const char *entq_status_str(entq_status status);
+
+/* Facts about a plan (for callers sizing buffers and for byte accounting):
+ * total output elements, scale rows, chunks, tensors and blob bytes. */
+entq_status entq_plan_info(const entq_plan_t *plan, uint64_t *out_elems, uint64_t *scale_rows,
+                           int64_t *n_chunks, int *n_tensors, uint64_t *blob_bytes);
+
+/* ---- Host-side encoder (offline compression; multi-threaded C++) ---- */
+
+/* Counts of each byte value in symbols[0..n). */
+entq_status entq_count_symbols(const uint8_t *symbols, uint64_t n, uint64_t counts[256],
+                               int n_threads);
+
+/* Quantises counts to a table summing to 4096: every present symbol gets at
+ * least 1; the sum is corrected by taking from the largest frequencies
+ * (smallest byte on ties) or giving to the most frequent symbol; a single
+ * present symbol gets 4096. An all-zero count vector gives an all-zero
+ * table (empty tensor). */
+entq_status entq_build_freq(const uint64_t counts[256], uint16_t freq[256]);
+
+/* Upper bound on the blob bytes one tensor can take. */
+uint64_t entq_encode_bound(uint64_t n_symbols, uint32_t chunk_symbols);
+
+/* Encodes n symbols of one tensor into consecutive chunk regions written to
+ * out[0 ..). chunks_out[k] (k < ceil(n / C)) receives the chunk descriptors
+ * with tensor = tensor_id and byte_offset = base_offset + the region's
+ * position in out. *bytes_written is the total. Multi-threaded over chunks. */
+entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chunk_symbols,
+                               const uint16_t freq[256], uint32_t tensor_id,
+                               uint64_t base_offset, uint8_t *out, uint64_t out_cap,
+                               entq_chunk_desc *chunks_out, uint64_t *bytes_written,
+                               int n_threads);
+
+/* Splits bf16 words into exponent bytes ((w >> 7) & 0xFF) and sign+mantissa
+ * bytes ((w >> 15) << 7 | (w & 0x7F)). */
+entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uint8_t *sm_out,
+                            int n_threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTQ_H */

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP decoder (through the C ABI) against the CPU oracle,
+element by element, on the same seeded inputs.
+
+Containers fed to the GPU are written by the oracle's encoder (for the
+largest workload, by the library's encoder, which the CPU suite proves
+byte-identical to the oracle's, and the expected values are then the
+oracle's dequantisation of the source codes). The bar is bit-exact for every
+output byte and bf16 word: all arithmetic is integer except the dequant,
+which is defined as one fp32 product rounded to nearest even, then rounded
+to bf16."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()  # loud failure if libentq.so is missing
+    return E
+
+
+def plan_from_container(E, c: oracle.Container, order=None):
+    import torch
+    tens = np.zeros(len(c.tensors), E.TENSOR_DESC)
+    freq = np.zeros((len(c.tensors), 256), np.uint16)
+    for t, td in enumerate(c.tensors):
+        tens[t] = (td["kind"], td["rows"], td["cols"], td["chunk_symbols"], td["n_symbols"],
+                   td["out_elem_offset"], td["scale_row_offset"])
+        freq[t] = td["freq"]
+    ch = np.zeros(c.n_chunks, E.CHUNK_DESC)
+    if c.n_chunks:
+        ch["tensor"] = c.chunks[:, 0]
+        ch["n_symbols"] = c.chunks[:, 1]
+        ch["n_words"] = c.chunks[:, 2]
+        ch["byte_offset"] = c.chunks[:, 3]
+        ch["elem_offset"] = c.chunks[:, 4]
+    if order is not None:
+        ch = ch[order]
+    blob = torch.from_numpy(c.blob if c.blob.size else np.zeros(16, np.uint8)).cuda()
+    p = E.plan(tens, freq, ch, c.blob.size)
+    return p, blob
+
+
+def gpu_decode(E, c, out_kind, scales=None, order=None, split_sm=None):
+    import torch
+    p, blob = plan_from_container(E, c, order)
+    total = max([t["out_elem_offset"] + t["n_symbols"] for t in c.tensors] + [1])
+    status = torch.full((max(c.n_chunks, 1),), -7, dtype=torch.int32, device="cuda")
+    if split_sm is not None:
+        out = torch.zeros(total, dtype=torch.int16, device="cuda")
+        sm = torch.from_numpy(split_sm).cuda()
+        E.decode_bf16_split(p, blob, sm, out, status)
+    elif out_kind == E.OUT_CODES:
+        out = torch.zeros(total, dtype=torch.uint8, device="cuda")
+        E.decode(p, blob, out, E.OUT_CODES, None, status)
+    else:
+        out = torch.zeros(total, dtype=torch.int16, device="cuda")
+        sc = torch.from_numpy(np.ascontiguousarray(scales, np.float32)).cuda()
+        E.decode(p, blob, out, E.OUT_BF16, sc, status)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    st = status.cpu().numpy()[:c.n_chunks]
+    if order is not None:
+        # status is indexed by position in the chunk index the plan was given
+        st_c = np.empty_like(st)
+        st_c[order] = st
+        st = st_c
+    p.close()
+    return (o.view(np.uint16) if o.dtype == np.int16 else o), st
+
+
+def expected_codes(c):
+    syms, st = oracle.decode_container_symbols(c)
+    total = max([t["out_elem_offset"] + t["n_symbols"] for t in c.tensors] + [1])
+    out = np.zeros(total, np.uint8)
+    for td, s in zip(c.tensors, syms):
+        out[td["out_elem_offset"]:td["out_elem_offset"] + td["n_symbols"]] = s
+    return out, st
+
+
+def all_scales(specs):
+    return np.concatenate([np.asarray(s["scales"], np.float32) for s in specs])
+
+
+def check_codes_and_bf16(E, specs, order=None):
+    c = oracle.encode_container(specs)
+    want_codes, st = expected_codes(c)
+    assert np.all(st == 0)
+    got, gst = gpu_decode(E, c, E.OUT_CODES, order=order)
+    np.testing.assert_array_equal(got, want_codes)
+    np.testing.assert_array_equal(gst, st)
+    scales = all_scales(specs)
+    want_bf16, _ = oracle.decode_container_bf16(c, scales)
+    got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales, order=order)
+    np.testing.assert_array_equal(got, want_bf16)
+    np.testing.assert_array_equal(gst, st)
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_tiny_int8_laplace_256x256(E):
+    _say("tiny int8 laplace 256x256, C=4096")
+    check_codes_and_bf16(E, synth.tiny_int8_laplace())
+
+
+def test_e4m3_4096x4096(E):
+    _say("e4m3 4096x4096, C=65536")
+    check_codes_and_bf16(E, synth.e4m3_matrix())
+
+
+def test_llama2_13b_block_bf16(E):
+    _say("llama2-13b block, 7 tensors, bf16")
+    specs = synth.llama2_13b_block()
+    c = oracle.encode_container(specs)
+    scales = all_scales(specs)
+    want, st = oracle.decode_container_bf16(c, scales)
+    assert np.all(st == 0)
+    got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales)
+    np.testing.assert_array_equal(gst, st)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_exponent_split_8192x8192(E):
+    _say("bf16 exponent split 8192x8192")
+    w = synth.bf16_weights()[0]
+    e, sm = oracle.bf16_split(w["bf16"])
+    spec = dict(kind=oracle.KIND_BF16EXP, rows=w["rows"], cols=w["cols"], symbols=e,
+                chunk_symbols=65536)
+    c = oracle.encode_container([spec])
+    got, gst = gpu_decode(E, c, None, split_sm=sm)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, w["bf16"])
+
+
+def test_llama2_70b_layer0_full(E):
+    """One full 70B-shaped layer (855.6 M symbols, 13,056 chunks) in the
+    launch configuration the benchmark times: one decode of the whole layer
+    into one bf16 buffer."""
+    _say("llama2-70b layer 0, full, oracle-encoded")
+    specs = synth.llama2_70b_layer(0)
+    c = oracle.encode_container(specs)
+    scales = all_scales(specs)
+    want, st = oracle.decode_container_bf16(c, scales)
+    assert np.all(st == 0)
+    got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_llama2_70b_last_layer_against_source(E):
+    """Layer 79, encoded by the library's encoder (byte-identical to the
+    oracle's on the CPU suite); expected = the oracle's dequantisation of the
+    generated source codes."""
+    import torch
+    _say("llama2-70b layer 79, library-encoded, vs oracle dequant of source")
+    specs = synth.llama2_70b_layer(79)
+    b = E.encode_batch(specs)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    sc = torch.from_numpy(all_scales(specs)).cuda()
+    out = torch.empty(b.out_elems, dtype=torch.int16, device="cuda")
+    st = torch.full((b.chunks.size,), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, blob, out, E.OUT_BF16, sc, st)
+    torch.cuda.synchronize()
+    assert int((st != 0).sum()) == 0
+    got = out.cpu().numpy().view(np.uint16)
+    for t, sp in enumerate(specs):
+        o = int(b.tensors[t]["out_elem_offset"])
+        n = sp["rows"] * sp["cols"]
+        want = oracle.dequant_tensor(sp["symbols"], sp["rows"], sp["cols"], sp["kind"], sp["scales"])
+        np.testing.assert_array_equal(got[o:o + n], want, err_msg=sp["name"])
+    p.close()
+
+
+# --------------------------------------------------------------- edge cases
+
+def test_ragged_shapes_and_odd_columns(E):
+    _say("ragged shapes")
+    specs = [
+        synth.random_int8_tensor(1, 1, 1.0, 1, 64),          # one symbol
+        synth.random_int8_tensor(1, 63, 1.0, 2, 64),         # one partial step
+        synth.random_int8_tensor(3, 65, 2.0, 3, 128),        # cols not a multiple of 64
+        synth.random_int8_tensor(7, 13, 0.7, 4, 64),         # cols < 64
+        synth.random_int8_tensor(17, 4099, 3.0, 5, 4096),    # ragged chunks and steps
+        synth.random_int8_tensor(2, 100003, 1.3, 6, 65536),  # long rows, ragged tail
+        synth.random_int8_tensor(40, 2048, 1.0, 7, 1 << 20), # chunk of 2^20 (one chunk)
+    ]
+    check_codes_and_bf16(E, specs)
+
+
+def test_shuffled_chunk_index_and_status_positions(E):
+    _say("shuffled chunk index")
+    specs = [synth.random_int8_tensor(64, 1000, 1.5, s, 1024) for s in range(3)]
+    c = oracle.encode_container(specs)
+    order = np.random.default_rng(0).permutation(c.n_chunks)
+    check_codes_and_bf16(E, specs, order=order)
+
+
+def test_one_symbol_and_all_symbol_tensors(E):
+    _say("one-symbol and 256-symbol tables")
+    const = dict(name="c", kind=oracle.KIND_INT8, rows=33, cols=64, chunk_symbols=256,
+                 symbols=np.full(33 * 64, 0xF3, np.uint8),
+                 scales=synth.uniform_f32(1e-3, 1e-2, 33, synth.key(97, 1, 0, 1)))
+    allb = dict(name="a", kind=oracle.KIND_INT8, rows=64, cols=1024, chunk_symbols=4096,
+                symbols=synth.random_bytes(64 * 1024, 3),
+                scales=synth.uniform_f32(-1.0, 1.0, 64, synth.key(97, 2, 0, 1)))
+    check_codes_and_bf16(E, [const, allb])
+
+
+def test_e4m3_every_code_including_nan(E):
+    _say("e4m3 all 256 codes incl. NaN")
+    sym = synth.random_bytes(128 * 512, 11)
+    sym[:256] = np.arange(256, dtype=np.uint8)
+    sc = synth.uniform_f32(1e-3, 4.0, 128, synth.key(97, 3, 0, 1))
+    sc[:3] = np.array([1.0, -1.0, 3.0e38], np.float32)
+    spec = dict(name="e", kind=oracle.KIND_E4M3, rows=128, cols=512, chunk_symbols=8192,
+                symbols=sym, scales=sc)
+    check_codes_and_bf16(E, [spec])
+
+
+def test_mixed_kinds_and_empty_tensor_in_one_batch(E):
+    _say("mixed kinds + empty tensor")
+    e4 = synth.e4m3_matrix(256, 320)[0]
+    specs = [synth.random_int8_tensor(30, 700, 2.0, 8, 2048), e4,
+             dict(name="z", kind=oracle.KIND_INT8, rows=0, cols=64, chunk_symbols=64,
+                  symbols=np.zeros(0, np.uint8), scales=np.zeros(0, np.float32)),
+             synth.random_int8_tensor(5, 64, 1.0, 9, 64)]
+    check_codes_and_bf16(E, specs)
+
+
+def test_gaps_in_output_and_scale_layout(E):
+    """Tensors placed at arbitrary output and scale offsets (with gaps) land
+    exactly there and nothing else is written."""
+    import torch
+    _say("output/scale gaps")
+    specs = [synth.random_int8_tensor(9, 320, 1.5, 12 + s, 1024) for s in range(2)]
+    b = E.encode_batch(specs, n_threads=2)
+    t = b.tensors.copy()
+    t[0]["out_elem_offset"], t[1]["out_elem_offset"] = 5000, 64
+    t[0]["scale_row_offset"], t[1]["scale_row_offset"] = 20, 3
+    p = E.plan(t, b.freq, b.chunks, b.blob.size)
+    scales = np.zeros(40, np.float32)
+    scales[20:29] = specs[0]["scales"]
+    scales[3:12] = specs[1]["scales"]
+    out = torch.full((5000 + 2880 + 64,), 0x5A5A, dtype=torch.int16, device="cuda")
+    E.decode(p, torch.from_numpy(b.blob).cuda(), out, E.OUT_BF16, torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    w0 = oracle.dequant_tensor(specs[0]["symbols"], 9, 320, 0, specs[0]["scales"])
+    w1 = oracle.dequant_tensor(specs[1]["symbols"], 9, 320, 0, specs[1]["scales"])
+    np.testing.assert_array_equal(got[5000:5000 + 2880], w0)
+    np.testing.assert_array_equal(got[64:64 + 2880], w1)
+    untouched = np.ones(got.size, bool)
+    untouched[5000:5000 + 2880] = False
+    untouched[64:64 + 2880] = False
+    assert np.all(got[untouched] == 0x5A5A)
+    p.close()
+
+
+def test_corrupt_streams_report_the_oracles_status(E):
+    _say("corruption statuses")
+    specs = [synth.random_int8_tensor(16, 4096, 2.0, 20, 4096)]
+    c = oracle.encode_container(specs)
+    rng = np.random.default_rng(5)
+    blob = c.blob.copy()
+    chunks = c.chunks.copy()
+    # chunk 0: flip a word bit; chunk 1: drop the last word from the count;
+    # chunk 2: flip a state bit; chunk 3: claim one word more than coded
+    # (the padding word); others intact
+    off0, nw0 = int(chunks[0, 3]), int(chunks[0, 2])
+    blob[off0 + 256 + 2 * int(rng.integers(0, nw0))] ^= 0x10
+    chunks[1, 2] -= 1
+    blob[int(chunks[2, 3]) + 4 * 7] ^= 0x01
+    if (256 + 2 * int(chunks[3, 2])) % 16:
+        chunks[3, 2] += 1
+    bad = oracle.Container(blob, c.tensors, chunks)
+    _, want_st = oracle.decode_container_symbols(bad)
+    assert want_st[0] != 0 and want_st[1] == 2 and want_st[4:].max() == 0
+    _, gst = gpu_decode(E, bad, E.OUT_CODES)
+    np.testing.assert_array_equal(gst, want_st)
+
+
+def test_repeat_runs_are_identical(E):
+    _say("determinism")
+    specs = synth.llama2_13b_block(shapes=[("k", 1024, 5120), ("d", 512, 13824)])
+    c = oracle.encode_container(specs)
+    scales = all_scales(specs)
+    a, _ = gpu_decode(E, c, E.OUT_BF16, scales=scales)
+    b, _ = gpu_decode(E, c, E.OUT_BF16, scales=scales)
+    np.testing.assert_array_equal(a, b)
