@@ -36,8 +36,11 @@
  *   ENTQ_OUT_CODES  uint8  out[i] = the decoded code byte;
  *   ENTQ_OUT_BF16   uint16 out[i] = RNE_bf16( fl32( value(code) * scale[row] ) )
  *                   where value is the two's-complement integer (INT8) or
- *                   the OCP e4m3 ("E4M3FN") value (E4M3), the product is
- *                   one IEEE single multiply rounded to nearest even, and
+ *                   the OCP e4m3 ("E4M3FN") value (E4M3; both NaN codes have
+ *                   the default NaN 0xFFC00000 as value), the product is one
+ *                   IEEE single multiply rounded to nearest even (a NaN
+ *                   operand comes out quieted with its payload, the code's
+ *                   before the scale's; 0 * inf gives 0xFFC00000), and
  *                   RNE_bf16 rounds to nearest even (a NaN stays a quiet NaN
  *                   with its sign and top payload bits);
  *   entq_decode_bf16_split: uint16 out[i] = (sm & 0x80) << 8 | exp << 7 |

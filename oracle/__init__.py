@@ -76,6 +76,7 @@ def lib():
             "orc_e4m3_to_f32_bits": (c.c_uint32, [c.c_uint8]),
             "orc_int8_to_f32_bits": (c.c_uint32, [c.c_uint8]),
             "orc_dequant_bf16": (c.c_uint16, [c.c_uint8, c.c_int, c.c_float]),
+            "orc_mul_f32_bits": (c.c_uint32, [c.c_uint32, c.c_uint32]),
             "orc_bf16_merge": (c.c_uint16, [c.c_uint8, c.c_uint8]),
             "orc_quantize_freqs": (c.c_int, [_u64p, _u16p]),
             "orc_table_valid": (c.c_int, [_u16p]),
@@ -116,6 +117,10 @@ def e4m3_table() -> np.ndarray:
     out = np.empty(256, np.uint32)
     lib().orc_e4m3_table(out)
     return out
+
+
+def mul_f32_bits(vb: int, sb: int) -> int:
+    return int(lib().orc_mul_f32_bits(vb & 0xFFFFFFFF, sb & 0xFFFFFFFF))
 
 
 def dequant_bf16(code: int, kind: int, scale: float) -> int:
@@ -322,3 +327,7 @@ def decode_container_bf16(c: Container, scales: np.ndarray):
         out[o:o + td["n_symbols"]] = dequant_tensor(sym, td["rows"], td["cols"], td["kind"],
                                                     scales[so:so + td["rows"]])
     return out, status
+
+
+def _isnan_bits(u: int) -> bool:
+    return (u & 0x7F800000) == 0x7F800000 and (u & 0x007FFFFF) != 0

@@ -66,6 +66,14 @@
 static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 
+/* The default NaN: the pattern an invalid operation (0 * inf) produces. */
+#define ORC_DEFAULT_NAN 0xFFC00000u
+
+static int is_nan_bits(uint32_t u)
+{
+    return ((u & 0x7F800000u) == 0x7F800000u) && ((u & 0x007FFFFFu) != 0);
+}
+
 /* fp32 -> bf16, round to nearest, ties to even.
  * bf16 keeps the upper 16 bits of the fp32 pattern. The dropped half r is
  * compared with the half-way point 0x8000: above rounds up, below truncates,
@@ -74,8 +82,7 @@ static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
  * A NaN stays a NaN: it is truncated and its quiet bit (bit 6) is set. */
 uint16_t orc_bf16_from_f32_bits(uint32_t u)
 {
-    int is_nan = ((u & 0x7F800000u) == 0x7F800000u) && ((u & 0x007FFFFFu) != 0);
-    if (is_nan)
+    if (is_nan_bits(u))
         return (uint16_t)((u >> 16) | 0x0040u);
     uint32_t hi = u >> 16;
     uint32_t r = u & 0xFFFFu;
@@ -88,14 +95,14 @@ uint16_t orc_bf16_from_f32_bits(uint32_t u)
  * 3 mantissa bits, no infinities, NaN only at S.1111.111.
  *   E = 0        : subnormal, value = m * 2^-9
  *   otherwise    : value = (1 + m/8) * 2^(E-7)
- * NaN codes give the quiet NaN pattern 0x7FC00000 with the code's sign. */
+ * A NaN code carries no payload; it decodes to the default NaN. */
 uint32_t orc_e4m3_to_f32_bits(uint8_t c)
 {
     uint32_t sign = c >> 7;
     uint32_t E = (c >> 3) & 15u;
     uint32_t m = c & 7u;
     if (E == 15u && m == 7u)
-        return (sign << 31) | 0x7FC00000u;
+        return ORC_DEFAULT_NAN;
     double v;
     if (E == 0u)
         v = ldexp((double)m, -9);
@@ -117,6 +124,21 @@ uint32_t orc_int8_to_f32_bits(uint8_t c)
 #define ORC_KIND_E4M3 1
 #define ORC_KIND_BF16EXP 2
 
+/* IEEE single-precision product v * s, rounded to nearest even, with the
+ * NaN rules of IEEE 754-2008 §6.2.3 made explicit: a NaN operand is
+ * returned quieted with its payload (the code's value is looked at first,
+ * then the scale), and an invalid product (0 * inf) is the default NaN. */
+uint32_t orc_mul_f32_bits(uint32_t vb, uint32_t sb)
+{
+    if (is_nan_bits(vb))
+        return vb | 0x00400000u;
+    if (is_nan_bits(sb))
+        return sb | 0x00400000u;
+    float p = bits_f32(vb) * bits_f32(sb);
+    uint32_t pb = f32_bits(p);
+    return is_nan_bits(pb) ? ORC_DEFAULT_NAN : pb;
+}
+
 /* Dequantisation of one code: bf16 = RNE16(fl32(value(code) * scale)).
  * One IEEE single-precision multiply, rounded to nearest even, then the
  * fp32 -> bf16 rounding above. */
@@ -124,9 +146,7 @@ uint16_t orc_dequant_bf16(uint8_t code, int kind, float scale)
 {
     uint32_t vb = (kind == ORC_KIND_E4M3) ? orc_e4m3_to_f32_bits(code)
                                           : orc_int8_to_f32_bits(code);
-    float v = bits_f32(vb);
-    float p = v * scale;
-    return orc_bf16_from_f32_bits(f32_bits(p));
+    return orc_bf16_from_f32_bits(orc_mul_f32_bits(vb, f32_bits(scale)));
 }
 
 /* BF16 = sign(1) | exponent(8) | mantissa(7). The exponent byte is the coded

@@ -73,9 +73,9 @@ def test_e4m3_decode_all_256_codes_match_torch():
     assert np.array_equal(np.isnan(mine), nan_ref)
     assert nan_ref.sum() == 2 and nan_ref[0x7F] and nan_ref[0xFF]
     np.testing.assert_array_equal(mine[~nan_ref].view(np.uint32), ref[~nan_ref].view(np.uint32))
-    # NaN codes keep their sign and are quiet
+    # NaN codes carry no payload: both decode to the default NaN
     bits = oracle.e4m3_table()
-    assert bits[0x7F] == 0x7FC00000 and bits[0xFF] == 0xFFC00000
+    assert bits[0x7F] == 0xFFC00000 and bits[0xFF] == 0xFFC00000
     # a few values by the format definition: 448 max, 2^-9 min subnormal, -0
     assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and bits[0x80] == 0x80000000
 
@@ -106,9 +106,42 @@ def test_dequant_matches_torch_fp32_product_then_bf16(kind):
     np.testing.assert_array_equal(got, want)
 
 
-def test_dequant_of_nan_code_is_quiet_nan_with_sign():
-    assert oracle.dequant_bf16(0x7F, oracle.KIND_E4M3, 0.5) == 0x7FC0
-    assert oracle.dequant_bf16(0xFF, oracle.KIND_E4M3, 0.5) == 0xFFC0
+def test_dequant_of_nan_code_is_the_default_nan():
+    assert oracle.dequant_bf16(0x7F, oracle.KIND_E4M3, 0.5) == 0xFFC0
+    assert oracle.dequant_bf16(0xFF, oracle.KIND_E4M3, -0.5) == 0xFFC0
+
+
+def _np_mul_bits(a_bits, b_bits):
+    a = np.array(a_bits, np.uint32).view(np.float32)
+    b = np.array(b_bits, np.uint32).view(np.float32)
+    with np.errstate(all="ignore"):
+        return (a * b).view(np.uint32)
+
+
+def test_product_nan_rules_match_ieee_hardware_multiply():
+    # numpy's float32 multiply runs the host's IEEE unit: with one NaN
+    # operand the result is that operand quieted (payload and sign kept),
+    # 0 * inf is the default NaN, everything else is the rounded product.
+    rng = np.random.default_rng(9)
+    specials = [0x7FC12345, 0xFFA00001, 0x7F800001, 0x7F800000, 0xFF800000, 0x00000000,
+                0x80000000, 0x00000001, 0x7F7FFFFF, 0x3F800000, 0xBF800000]
+    finite = rng.integers(0, 1 << 32, 2000, dtype=np.uint64).astype(np.uint32)
+    finite = finite[((finite >> 23) & 0xFF) != 0xFF]
+    pairs = [(a, b) for a in specials for b in specials
+             if not (oracle._isnan_bits(a) and oracle._isnan_bits(b))]
+    pairs += [(int(a), int(b)) for a, b in zip(finite[:1000], finite[1000:2000])]
+    pairs += [(int(a), s) for a in finite[:50] for s in specials]
+    a = [p[0] for p in pairs]
+    b = [p[1] for p in pairs]
+    want = _np_mul_bits(a, b)
+    got = np.array([oracle.mul_f32_bits(x, y) for x, y in pairs], np.uint32)
+    np.testing.assert_array_equal(got, want)
+    assert oracle.mul_f32_bits(0x00000000, 0x7F800000) == 0xFFC00000
+
+
+def test_product_with_two_nans_keeps_the_codes_nan():
+    assert oracle.mul_f32_bits(0xFFC00000, 0x7FC12345) == 0xFFC00000
+    assert oracle.mul_f32_bits(0x7FA00000, 0xFFC00001) == 0x7FE00000
 
 
 def test_bf16_split_merge_round_trip_all_patterns():
