@@ -131,9 +131,9 @@ def main():
     mean_launch_s = float(launch_ms.mean()) / 1e3
     achieved_gbs = alg_bytes_layer / mean_launch_s / 1e9
     log(f"{args.steps} steps x {args.layers} layers: {ms_per_step:.3f} ms/step "
-        f"(wall {1e3 * t_wall / args.steps:.3f}), launch mean {1e3 * mean_launch_s:.1f} us "
-        f"p10 {1e3 * np.percentile(launch_ms, 10) / 1e3:.1f} p90 "
-        f"{1e3 * np.percentile(launch_ms, 90) / 1e3:.1f} us, {achieved_gbs:.0f} GB/s")
+        f"(wall {1e3 * t_wall / args.steps:.3f}), launch mean {1e6 * mean_launch_s:.1f} us "
+        f"p10 {1e3 * np.percentile(launch_ms, 10):.1f} p90 "
+        f"{1e3 * np.percentile(launch_ms, 90):.1f} us, {achieved_gbs:.0f} GB/s")
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None

@@ -21,6 +21,12 @@ constexpr uint32_t kMaxChunkSymbols = 1u << 20;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
+// The streaming kernel works in blocks of kBlockSteps steps (512 symbols
+// per wave); a tensor can use it when its chunk size is a multiple of the
+// block, and, for bf16 output, when a block never crosses a row.
+constexpr uint32_t kBlockSteps = 8;
+constexpr uint32_t kBlockSyms = kBlockSteps * kLanes;
+
 // Slot table entry, one per slot (4096 per tensor), 8 bytes:
 //   lo = f | sym << 24   (f = frequency of the owning symbol, 1..4096, in
 //                         bits 0..12; bits 13..23 are zero so that a 24-bit
@@ -64,6 +70,11 @@ struct entq_plan_s {
     int n_tensors;
     int64_t n_chunks;
     int64_t n_tasks;
+    // Tasks are ordered in three groups: [0, n_tasks_rows) have chunk sizes
+    // and row lengths that are multiples of kBlockSyms; [n_tasks_rows,
+    // n_tasks_blocks) only chunk sizes; the rest neither.
+    int64_t n_tasks_rows;
+    int64_t n_tasks_blocks;
     uint64_t blob_bytes;
     uint64_t out_elems;
     uint64_t scale_rows;

@@ -168,8 +168,23 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         dten[t].cols = tensors[t].cols;
         dten[t].kind = tensors[t].kind;
     }
+    // task groups: block- and row-aligned tensors first, then block-aligned,
+    // then the rest (the launcher picks a kernel per group)
+    auto group_of = [&](int t) {
+        const entq_tensor_desc &td = tensors[t];
+        // the streaming kernel writes 8 outputs per lane with 16-byte
+        // accesses: chunk sizes must be whole blocks and outputs 16-aligned
+        if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return 2;
+        return (td.cols % entq::kBlockSyms) ? 1 : 0;
+    };
     int64_t c = 0, task = 0;
-    for (int t = 0; t < n_tensors; ++t) {
+    int64_t group_end[3] = {0, 0, 0};
+    std::vector<int> order;
+    for (int g = 0; g < 3; ++g)
+        for (int t = 0; t < n_tensors; ++t)
+            if (group_of(t) == g) order.push_back(t);
+    for (int oi = 0; oi < (int)order.size(); ++oi) {
+        const int t = order[oi];
         const entq_tensor_desc &td = tensors[t];
         const int64_t first = c;
         for (int64_t s : slot_of[t]) {
@@ -190,6 +205,7 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
             dtask[task].tensor = (uint32_t)t;
             ++task;
         }
+        for (int g = group_of(t); g < 3; ++g) group_end[g] = task;
     }
 
     if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
@@ -206,6 +222,8 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
     p->n_tensors = n_tensors;
     p->n_chunks = n_chunks;
     p->n_tasks = n_tasks;
+    p->n_tasks_rows = group_end[0];
+    p->n_tasks_blocks = group_end[1];
     p->blob_bytes = blob_bytes;
     p->out_elems = out_elems;
     p->scale_rows = scale_rows;
@@ -263,7 +281,7 @@ entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_st
     if (plan->n_chunks == 0) return ENTQ_OK;
     if (!d_exp_stream || !d_signmant || !d_out) return ENTQ_EINVAL;
     if ((uintptr_t)d_exp_stream % ENTQ_REGION_ALIGN || (uintptr_t)d_out % 16 ||
-        (uintptr_t)d_signmant % 8)
+        (uintptr_t)d_signmant % 16)
         return ENTQ_EALIGN;
     return (entq_status)entq::launch_decode(plan, entq::kModeSplit, d_exp_stream, d_out, nullptr,
                                             d_signmant, d_chunk_status, stream);

@@ -160,7 +160,7 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
 /* Decodes a plan whose tensors are all ENTQ_SYM_BF16EXP into bf16 words:
  * the coded exponent bytes come from d_exp_stream (the blob), the raw
  * sign+mantissa byte of output element i is d_signmant[i] (same indexing as
- * d_out). d_out is 16-byte aligned, d_signmant 8-byte aligned. */
+ * d_out). d_out and d_signmant are 16-byte aligned. */
 entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                    const uint8_t *d_signmant, uint16_t *d_out,
                                    int32_t *d_chunk_status, void *stream);

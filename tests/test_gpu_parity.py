@@ -302,3 +302,64 @@ def test_repeat_runs_are_identical(E):
     a, _ = gpu_decode(E, c, E.OUT_BF16, scales=scales)
     b, _ = gpu_decode(E, c, E.OUT_BF16, scales=scales)
     np.testing.assert_array_equal(a, b)
+
+
+def test_stream_kernel_high_entropy_ring_wraps(E):
+    """All 256 byte values, near-uniform: ~8 bits/symbol, so a wave's word
+    ring wraps every ~64 steps and the mirror tail is used constantly; chunk
+    sizes 512 .. 2^20 with ragged tails, output offsets 16-aligned so every
+    tensor takes the streaming kernel."""
+    _say("high-entropy streaming path")
+    specs = []
+    for i, (rows, cols, C) in enumerate([(4, 512, 512), (3, 1024, 1024), (7, 4096, 8192),
+                                         (2, 1 << 19, 1 << 20), (1, 700_000, 65536),
+                                         (5, 512 * 37, 4096)]):
+        sym = synth.random_bytes(rows * cols, 40 + i)
+        specs.append(dict(name=f"u{i}", kind=oracle.KIND_INT8, rows=rows, cols=cols,
+                          chunk_symbols=C, symbols=sym,
+                          scales=synth.uniform_f32(1e-3, 1e-2, rows, synth.key(97, 40 + i, 0, 1))))
+    c = oracle.encode_container(specs)
+    assert all(t["out_elem_offset"] % 16 == 0 for t in c.tensors)
+    want_codes, st = expected_codes(c)
+    got, gst = gpu_decode(E, c, E.OUT_CODES)
+    np.testing.assert_array_equal(gst, st)
+    np.testing.assert_array_equal(got, want_codes)
+    scales = all_scales(specs)
+    want, _ = oracle.decode_container_bf16(c, scales)
+    got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_split_stream_ragged_and_high_entropy(E):
+    """bf16 split on the streaming path with partial blocks and a random
+    (high-entropy) exponent stream."""
+    _say("split streaming ragged")
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 1 << 16, size=3 * 70_001 + 5, dtype=np.uint64).astype(np.uint16)
+    words[: words.size // 2] = synth.bf16_weights(1, words.size // 2)[0]["bf16"]
+    e, sm = oracle.bf16_split(words)
+    spec = dict(kind=oracle.KIND_BF16EXP, rows=1, cols=words.size, symbols=e,
+                chunk_symbols=65536)
+    c = oracle.encode_container([spec])
+    got, gst = gpu_decode(E, c, None, split_sm=sm)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, words)
+
+
+@pytest.mark.parametrize("cols", [320, 512])
+def test_nan_and_inf_scales_both_kernels(E, cols):
+    """Non-finite scales and e4m3 NaN codes: cols=320 runs the simple
+    kernel, cols=512 the streaming one; both must give the oracle's NaN
+    propagation."""
+    _say(f"nan/inf scales cols={cols}")
+    rows = 12
+    specs = []
+    for kind in (oracle.KIND_INT8, oracle.KIND_E4M3):
+        sym = synth.random_bytes(rows * cols, 60 + kind)
+        sym[:256] = np.arange(256, dtype=np.uint8)
+        sc = np.array([0x3F800000, 0xBF800000, 0x7FC00000, 0xFFC00000, 0x7FC12345, 0xFFA00001,
+                       0x7F800000, 0xFF800000, 0x7F7FFFFF, 0x00000001, 0x00000000, 0x80000000],
+                      np.uint32).view(np.float32)
+        specs.append(dict(name=f"k{kind}", kind=kind, rows=rows, cols=cols, chunk_symbols=512,
+                          symbols=sym, scales=sc))
+    check_codes_and_bf16(E, specs)
