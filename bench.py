@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-sample-tensors", type=int, default=5,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline")
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain fp32 negate (read N MiB, write N MiB) before timing, as a "
+                         "known-size reference for hardware byte counters")
     return ap.parse_args()
 
 
@@ -102,6 +105,16 @@ def main():
             E.decode(plans[layer], blobs[layer], out, E.OUT_BF16, scales[layer], None, stream)
             if events is not None:
                 events[layer][1].record(stream)
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibration_copy_mib} MiB read + written")
+        del src, dst
 
     # ---------------------------------------------------------------- timing
     for _ in range(args.warmup):

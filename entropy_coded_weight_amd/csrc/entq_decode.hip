@@ -77,22 +77,11 @@ __device__ __forceinline__ void load_table(uint2 *T, const SlotEntry *tables, ui
 // ---------------------------------------------------------------------------
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void decode_simple(
-    const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
-    const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
-    const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
-    const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
-    __shared__ uint2 T[kProbScale];
-
-    const DevTask task = tasks[task0 + blockIdx.x];
-    const DevTensor td = tensors[task.tensor];
-    load_table(T, tables, task.tensor);
-    __syncthreads();
-
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t lane = threadIdx.x & 63;
-    if (wave >= task.n_chunks) return;
-    const DevChunk ch = chunks[task.first_chunk + wave];
+__device__ __forceinline__ void simple_chunk(const uint2 *T, const DevTensor &td, const DevChunk &ch,
+                                             const uint8_t *__restrict__ blob, void *__restrict__ out,
+                                             const float *__restrict__ scales,
+                                             const uint8_t *__restrict__ signmant,
+                                             int32_t *__restrict__ status, uint32_t lane) {
     const uint8_t *region = blob + ch.byte_offset;
     const uint16_t *words = reinterpret_cast<const uint16_t *>(region + kStateBytes);
     uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
@@ -155,26 +144,50 @@ __global__ __launch_bounds__(kThreads) void decode_simple(
                                   : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
 }
 
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void decode_simple(
+    const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
+    const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
+    const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
+    const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
+    __shared__ uint2 T[kProbScale];
+
+    const DevTask task = tasks[task0 + blockIdx.x];
+    const DevTensor td = tensors[task.tensor];
+    load_table(T, tables, task.tensor);
+    __syncthreads();
+
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t lane = threadIdx.x & 63;
+    for (uint32_t c = wave; c < task.n_chunks; c += kWaves)
+        simple_chunk<MODE>(T, td, chunks[task.first_chunk + c], blob, out, scales, signmant,
+                           status, lane);
+}
+
 // ---------------------------------------------------------------------------
 // decode_stream
 // ---------------------------------------------------------------------------
 
-// Word ring of one wave: kRingWords 16-bit words in LDS plus a mirror of its
-// first kMirrorWords after the end, so that the up-to-64 words one step
-// reads are contiguous without a wrap-around mask. It is refilled in units
-// of kRingUnit words (64 lanes x 16 bytes, one direct global->LDS load) and
-// kept at most kRingLead words ahead of the read pointer, which leaves one
-// unit of room for the unit in flight.
-constexpr uint32_t kRingWords = 2048;
-constexpr uint32_t kMirrorWords = 64;
-constexpr uint32_t kRingUnit = 512;
+// Word ring of one wave: kRingWords 16-bit words in LDS at a 2 KB-aligned
+// base, so that "base | (index mod kRingWords) * 2" is one v_and_or. It is
+// refilled in units of kRingUnit words (32 lanes x 16 bytes, one direct
+// global->LDS load) and kept at most kRingLead words ahead of the read
+// pointer, which leaves one unit of room for the unit in flight. A block
+// reads at most kBlockSyms words, so a unit issued at one block's start is
+// not needed before the next block's start.
+constexpr uint32_t kRingWords = 1024;
+constexpr uint32_t kRingUnit = 256;
 constexpr uint32_t kRingLead = kRingWords - kRingUnit;
 static_assert(kRingLead >= 2 * kBlockSyms, "a block must find its words loaded a block early");
+static_assert(kRingUnit == 32 * 8, "one unit = 32 lanes x 8 words");
+static_assert((kRingWords & (kRingWords - 1)) == 0, "ring index wraps with a mask");
 
+// Per-wave staging and (split mode) sign+mantissa buffers. A decoded step
+// stores, per lane, the high half of its slot-table entry (symbol << 8), so
+// the symbol is byte 1 of a 16-bit slot.
 template <int MODE>
-struct alignas(16) WaveLds {
-    uint16_t ring[kRingWords + kMirrorWords];
-    uint8_t stage[kBlockSyms];                               // decoded bytes of a block
+struct alignas(16) WaveStage {
+    uint16_t stage[kBlockSyms];
     uint8_t sm[MODE == kModeSplit ? 2 : 1][MODE == kModeSplit ? kBlockSyms : 16];
 };
 
@@ -186,54 +199,114 @@ struct alignas(16) WaveLds {
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(lds_base), "v"(gptr)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-// All vector-memory operations but the most recent `n` are complete. The asm
+// All vector-memory operations but the most recent N are complete. The asm
 // form is invisible to the compiler's own wait insertion, which therefore
 // never relaxes it.
-__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vm1() { asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)p;
 }
 
-// Issues the load of words [first, first + kRingUnit) of the chunk into the
-// ring (only lanes whose 16 bytes lie inside the chunk's region), and of the
-// mirror when the unit starts the ring.
-__device__ __forceinline__ void ring_fill(uint16_t *ring, const uint8_t *words_g, uint32_t first,
-                                          uint32_t nw8, uint32_t lane) {
-    const uint32_t w = first + 8u * lane;
-    const uint32_t slot = first & (kRingWords - 1);
-    if (w < nw8) {
-        const uint8_t *g = words_g + 2u * w;
-        dma16(g, lds_addr(ring + slot));
-        if (slot == 0 && lane < kMirrorWords / 8) dma16(g, lds_addr(ring + kRingWords));
-    }
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+
+// Uniform bookkeeping of one chunk on the streaming path.
+struct Stream {
+    const uint8_t *words_g;     // the chunk's word stream in global memory
+    uint32_t ring;              // LDS byte address of the wave's ring
+    uint32_t nw, nw8;           // words, and words rounded up to 8 (16 bytes)
+    uint32_t p;                 // words consumed
+    uint32_t issued, landed;    // words loaded into the ring / known landed
+    uint32_t horizon;           // the ring needs attention once p passes this
+};
+
+// Loads words [issued, issued + kRingUnit) of the chunk into the ring (lanes
+// whose 16 bytes lie inside the chunk's region).
+__device__ __forceinline__ void ring_fill(const Stream &s, uint32_t lane) {
+    const uint32_t w = s.issued + 8u * lane;
+    if (lane < kRingUnit / 8 && w < s.nw8)
+        dma16(s.words_g + 2u * w, s.ring + 2u * (s.issued & (kRingWords - 1)));
 }
 
-// One decode step of a wave: lane j decodes its next symbol, writes the byte
-// to the block's stage at `row` and renormalises from the ring.
+// Block start, slow path: makes sure this block's words have landed, tops
+// the ring up to kRingLead words ahead and sets the next horizon.
+__device__ __forceinline__ void ring_service(Stream &s, uint32_t lane) {
+    const uint32_t need_to = (s.p + kBlockSyms < s.nw) ? s.p + kBlockSyms : s.nw;
+    if (s.landed < need_to) {
+        wait_vm<1>();  // everything but the previous block's store
+        s.landed = s.issued;
+    }
+    while (s.issued < s.nw && s.issued < s.p + kRingLead) {
+        ring_fill(s, lane);
+        s.issued += kRingUnit;
+    }
+    // next time: once a block could read past the landed words, or the ring
+    // could take another unit
+    const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
+    const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
+    s.horizon = a < b ? a : b;
+}
+
+// One decode step of a wave: lane j decodes its next symbol (stores the
+// high half of its table entry in the stage) and renormalises from the
+// ring. Every lane reads the ring (no branch on the mask); lanes that
+// renormalise shift the word in, the others keep x (v_perm with a per-lane
+// selector).
+// The ring's byte-index mask in a VGPR: v_and_or_b32 takes one scalar operand
+// (the ring base) and no literal, so the mask has to come in a register. The
+// asm keeps the compiler from folding it back into a literal.
+__device__ __forceinline__ uint32_t ring_mask_vgpr() {
+    uint32_t m;
+    asm("v_mov_b32 %0, %1" : "=v"(m) : "i"(2 * kRingWords - 1));
+    return m;
+}
+
 template <bool PARTIAL>
-__device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &p, const uint2 *T,
-                                            const uint16_t *ring, uint8_t *stage_row,
-                                            uint32_t lane, bool active) {
+__device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &p, uint32_t ring,
+                                            uint32_t ring_mask, const uint2 *T,
+                                            uint16_t *stage_row, uint32_t lane, bool active) {
     bool need = false;
     if (!PARTIAL || active) {
         const uint2 e = T[x & (kProbScale - 1)];
         x = __umul24(e.x, x >> kProbBits) + e.y;
-        stage_row[lane] = (uint8_t)(e.x >> 24);
+        stage_row[lane] = (uint16_t)(e.x >> 16);
         need = x < kStateLow;
     }
     const uint64_t mask = __ballot(need);
-    if (need) {
-        const uint16_t *r = ring + (p & (kRingWords - 1));
-        x = (x << 16) | r[lane_prefix(mask)];
-    }
+    const uint32_t a = (((p + lane_prefix(mask)) << 1) & ring_mask) | ring;
+    const uint32_t w = *reinterpret_cast<lds_u16 *>(a);
+    x = __builtin_amdgcn_perm(x, w, need ? 0x05040100u : 0x07060504u);
     p += (uint32_t)__popcll(mask);
+}
+
+// bf16 of (value of a code byte) * scale, two per dword; d holds two staged
+// 16-bit slots, the code bytes in bytes 1 and 3.
+template <bool E4M3>
+__device__ __forceinline__ uint32_t dequant2(uint32_t d, float scale) {
+    float v0, v1;
+    if (E4M3) {
+        v0 = __builtin_amdgcn_cvt_f32_fp8((int)d, 1);
+        v1 = __builtin_amdgcn_cvt_f32_fp8((int)d, 3);
+    } else {
+        v0 = (float)((int32_t)(d << 16) >> 24);
+        v1 = (float)((int32_t)d >> 24);
+    }
+    return bf16x2_bits(mul_value_scale(v0, scale), mul_value_scale(v1, scale));
+}
+
+// sign << 15 | exponent << 7 | mantissa for two elements: q holds, per
+// 16-bit half, exponent << 8 | sign+mantissa byte.
+__device__ __forceinline__ uint32_t merge2(uint32_t q) {
+    return ((q >> 1) & 0x7F807F80u) | ((q << 8) & 0x80008000u) | (q & 0x007F007Fu);
 }
 
 template <int MODE>
@@ -242,168 +315,136 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
     const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
+    __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
-    __shared__ WaveLds<MODE> W[kWaves];
+    __shared__ WaveStage<MODE> STG[kWaves];
 
     const DevTask task = tasks[task0 + blockIdx.x];
-    const uint32_t kind = tensors[task.tensor].kind;
+    const bool e4m3 = tensors[task.tensor].kind == ENTQ_SYM_E4M3;
     const uint32_t cols = tensors[task.tensor].cols;
     load_table(T, tables, task.tensor);
+    __syncthreads();
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
-    const bool has_chunk = wave < task.n_chunks;
-    const DevChunk ch = chunks[task.first_chunk + (has_chunk ? wave : 0)];
-    const uint8_t *region = blob + ch.byte_offset;
-    const uint8_t *words_g = region + kStateBytes;
-    WaveLds<MODE> &L = W[wave];
-    const uint32_t n = ch.n_symbols;
-    const uint32_t nw = ch.n_words;
-    const uint32_t nw8 = (nw + 7u) & ~7u;  // the region is padded to 16 bytes
-
-    uint32_t x = has_chunk ? reinterpret_cast<const uint32_t *>(region)[lane] : kStateLow;
-    // words issued to the ring / known to have landed
-    uint32_t issued = 0, landed = 0;
-    if (has_chunk) {
-        while (issued < nw && issued < kRingLead) {
-            ring_fill(L.ring, words_g, issued, nw8, lane);
-            issued += kRingUnit;
+    WaveStage<MODE> &G = STG[wave];
+    // the task's chunks in rounds of equal width: every round keeps the same
+    // number of waves busy
+    const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
+    const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
+        const DevChunk ch = chunks[task.first_chunk + c];
+        const uint8_t *region = blob + ch.byte_offset;
+        Stream s;
+        s.words_g = region + kStateBytes;
+        s.ring = lds_addr(RING[wave]);
+        s.nw = ch.n_words;
+        s.nw8 = (ch.n_words + 7u) & ~7u;  // the region is padded to 16 bytes
+        s.p = 0;
+        s.issued = 0;
+        const uint32_t n = ch.n_symbols;
+        uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
+        while (s.issued < s.nw && s.issued < kRingLead) {
+            ring_fill(s, lane);
+            s.issued += kRingUnit;
         }
-        // first block's sign+mantissa bytes (a partial block reads them
-        // straight from global memory instead)
+        // first block's sign+mantissa bytes (a partial block reads them from
+        // global memory instead)
         if (MODE == kModeSplit && n >= kBlockSyms && lane < kBlockSyms / 16)
-            dma16(signmant + ch.out_elem + 16u * lane, lds_addr(L.sm[0]));
-    }
-    // vmcnt(0) as a real instruction, so that the compiler also knows the
-    // state load has completed and places no wait of its own in the loop
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
-    landed = issued;
-    __syncthreads();  // table in LDS
-    if (!has_chunk) return;
-
-    uint32_t p = 0;
-    const uint32_t n_blocks = (n + kBlockSyms - 1) / kBlockSyms;
-    const float *scale_row = scales + ch.scale_row;  // the block's row (uniform)
-    uint32_t col = ch.col0;  // a multiple of kBlockSyms on this path
-
-    for (uint32_t b = 0; b < n_blocks; ++b) {
-        const uint32_t base = b * kBlockSyms;
-        const bool full = base + kBlockSyms <= n;
-        // ---- ring: the words of this block must have landed; top up ahead
-        const uint32_t need_to = (p + kBlockSyms < nw) ? p + kBlockSyms : nw;
-        if (landed < need_to) {
-            wait_vm1();  // all but the previous block's store
-            landed = issued;
+            dma16(signmant + ch.out_elem + 16u * lane, lds_addr(G.sm[0]));
+        // vmcnt(0) as a real instruction, so that the compiler also knows the
+        // state load has completed and places no wait of its own in the loop
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+        s.landed = s.issued;
+        {
+            const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
+            const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
+            s.horizon = a < b ? a : b;
         }
-        while (issued < nw && issued < p + kRingLead) {
-            ring_fill(L.ring, words_g, issued, nw8, lane);
-            issued += kRingUnit;
-        }
-        float scale = 0.f;
-        if (MODE == kModeBf16) scale = *scale_row;
-        // ---- decode
-        if (full) {
+        const float *scale_row = scales + ch.scale_row;
+        float scale = (MODE == kModeBf16) ? *scale_row : 0.f;
+        uint32_t col = ch.col0;  // a multiple of kBlockSyms on this path
+        uint16_t *o16 = static_cast<uint16_t *>(out) + ch.out_elem;
+        uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
+        const uint8_t *sm_g = signmant + ch.out_elem;
+
+        const uint32_t ring_mask = ring_mask_vgpr();
+        const uint32_t full_blocks = n / kBlockSyms;
+        for (uint32_t b = 0; b < full_blocks; ++b) {
+            if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
-                stream_step<false>(x, p, T, L.ring, L.stage + 64u * t, lane, true);
-        } else {
-            const uint32_t steps = (n - base + 63u) >> 6;
-            for (uint32_t t = 0; t < steps; ++t)
-                stream_step<true>(x, p, T, L.ring, L.stage + 64u * t, lane,
-                                  base + 64u * t + lane < n);
-        }
-        // ---- output: lane k converts and stores symbols 8k .. 8k+7 of the block
-        const uint2 sym8 = *reinterpret_cast<const uint2 *>(L.stage + 8u * lane);
-        const uint64_t o = ch.out_elem + base + 8u * lane;
-        if (MODE == kModeCodes) {
-            if (full) {
-                *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(out) + o) = sym8;
+                stream_step<false>(x, s.p, s.ring, ring_mask, T, G.stage + 64u * t, lane, true);
+            // lane k: symbols 4k .. 4k+3 of the block (bytes 1, 3, 5, 7)
+            const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
+            if (MODE == kModeCodes) {
+                reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
+                o8 += kBlockSyms;
+            } else if (MODE == kModeBf16) {
+                const uint2 w = e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
+                                     : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
+                reinterpret_cast<uint2 *>(o16)[lane] = w;
+                o16 += kBlockSyms;
+                col += kBlockSyms;
+                if (col == cols) {
+                    col = 0;
+                    ++scale_row;
+                    scale = *scale_row;
+                }
             } else {
-                const uint8_t *s = reinterpret_cast<const uint8_t *>(&sym8);
-                for (uint32_t m = 0; m < 8; ++m)
-                    if (base + 8u * lane + m < n) static_cast<uint8_t *>(out)[o + m] = s[m];
-            }
-        } else {
-            uint32_t w[4];
-            if (MODE == kModeBf16) {
-                float v[8];
-                if (kind == ENTQ_SYM_E4M3) {
-                    v[0] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.x, 0);
-                    v[1] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.x, 1);
-                    v[2] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.x, 2);
-                    v[3] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.x, 3);
-                    v[4] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.y, 0);
-                    v[5] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.y, 1);
-                    v[6] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.y, 2);
-                    v[7] = __builtin_amdgcn_cvt_f32_fp8((int)sym8.y, 3);
-                } else {
-                    v[0] = (float)((int32_t)(sym8.x << 24) >> 24);
-                    v[1] = (float)((int32_t)(sym8.x << 16) >> 24);
-                    v[2] = (float)((int32_t)(sym8.x << 8) >> 24);
-                    v[3] = (float)((int32_t)sym8.x >> 24);
-                    v[4] = (float)((int32_t)(sym8.y << 24) >> 24);
-                    v[5] = (float)((int32_t)(sym8.y << 16) >> 24);
-                    v[6] = (float)((int32_t)(sym8.y << 8) >> 24);
-                    v[7] = (float)((int32_t)sym8.y >> 24);
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    w[m] = bf16x2_bits(mul_value_scale(v[2 * m], scale),
-                                       mul_value_scale(v[2 * m + 1], scale));
-            } else {
-                // sign+mantissa bytes of the same 8 elements; rebuild bf16 as
-                // sign << 15 | exponent << 7 | mantissa, two per dword
-                uint2 sm8;
-                if (full) {
-                    wait_vm0();
-                    sm8 = *reinterpret_cast<const uint2 *>(L.sm[b & 1] + 8u * lane);
-                } else {
-                    uint8_t sb[8];
-                    for (uint32_t m = 0; m < 8; ++m)
-                        sb[m] = (base + 8u * lane + m < n) ? signmant[o + m] : 0;
-                    sm8 = make_uint2(sb[0] | sb[1] << 8 | sb[2] << 16 | (uint32_t)sb[3] << 24,
-                                     sb[4] | sb[5] << 8 | sb[6] << 16 | (uint32_t)sb[7] << 24);
-                }
-                const uint32_t e4[2] = {sym8.x, sym8.y};
-                const uint32_t s4[2] = {sm8.x, sm8.y};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    // bytes (e1 s1 e0 s0) and (e3 s3 e2 s2): each half = e << 8 | s
-                    const uint32_t lo = __builtin_amdgcn_perm(e4[h], s4[h], 0x05010400u);
-                    const uint32_t hi = __builtin_amdgcn_perm(e4[h], s4[h], 0x07030602u);
-                    const uint32_t pr[2] = {lo, hi};
-#pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const uint32_t q = pr[k];
-                        // e << 7 from (q >> 1); mantissa from q; sign from q << 8
-                        const uint32_t sh = (q >> 1) & 0x7F807F80u;
-                        const uint32_t sg = (q << 8) & 0x80008000u;
-                        w[2 * h + k] = sh | sg | (q & 0x007F007Fu);
-                    }
-                }
+                wait_vm<0>();  // this block's sign+mantissa bytes
+                const uint32_t sm4 = *reinterpret_cast<const uint32_t *>(G.sm[b & 1] + 4u * lane);
+                // per 16-bit half: exponent << 8 | sign+mantissa
+                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
+                                           merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
                 // next block's sign+mantissa bytes, if that block is full
-                const uint32_t nb = base + kBlockSyms;
-                if (nb + kBlockSyms <= n && lane < kBlockSyms / 16)
-                    dma16(signmant + ch.out_elem + nb + 16u * lane, lds_addr(L.sm[(b + 1) & 1]));
-            }
-            uint16_t *o16 = static_cast<uint16_t *>(out) + o;
-            if (full) {
-                *reinterpret_cast<uint4 *>(o16) = make_uint4(w[0], w[1], w[2], w[3]);
-            } else {
-                for (uint32_t m = 0; m < 8; ++m)
-                    if (base + 8u * lane + m < n) o16[m] = (uint16_t)(w[m >> 1] >> (16 * (m & 1)));
+                sm_g += kBlockSyms;
+                if (b + 1 < full_blocks && lane < kBlockSyms / 16)
+                    dma16(sm_g + 16u * lane, lds_addr(G.sm[(b + 1) & 1]));
+                reinterpret_cast<uint2 *>(o16)[lane] = w;
+                o16 += kBlockSyms;
             }
         }
-        if (MODE == kModeBf16) {
-            col += kBlockSyms;
-            if (col == cols) { col = 0; ++scale_row; }
+        // the last, partial block: one symbol per lane and step, element-wise output
+        const uint32_t rest = n - full_blocks * kBlockSyms;
+        if (rest) {
+            if (s.p > s.horizon) ring_service(s, lane);
+            for (uint32_t t = 0; 64u * t < rest; ++t)
+                stream_step<true>(x, s.p, s.ring, ring_mask, T, G.stage + 64u * t, lane,
+                                  64u * t + lane < rest);
+            const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
+            const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
+            for (uint32_t m = 0; m < 4; ++m) {
+                const uint32_t i = 4u * lane + m;
+                if (i >= rest) break;
+                const uint32_t sym = (sym4 >> (8 * m)) & 0xFFu;
+                if (MODE == kModeCodes) {
+                    o8[i] = (uint8_t)sym;
+                } else if (MODE == kModeBf16) {
+                    const float v = e4m3 ? __builtin_amdgcn_cvt_f32_fp8((int)sym, 0)
+                                         : (float)(int8_t)sym;
+                    o16[i] = bf16_bits(mul_value_scale(v, scale));
+                } else {
+                    const uint32_t sm = sm_g[i];
+                    o16[i] = (uint16_t)(((sm & 0x80u) << 8) | (sym << 7) | (sm & 0x7Fu));
+                }
+            }
         }
+        const uint64_t bad_state = __ballot(x != kStateLow);
+        if (status && lane == 0)
+            status[ch.status_index] = (s.p != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+                                      : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
+        wait_vm<0>();  // no global->LDS load may outlive the chunk (corrupt input stops early)
     }
-    const uint64_t bad_state = __ballot(x != kStateLow);
-    if (status && lane == 0)
-        status[ch.status_index] = (p != nw) ? ENTQ_CHUNK_BAD_WORDS
-                                  : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
-    wait_vm0();  // no global->LDS load may outlive the wave (corrupt input stops early)
+}
+
+template <int MODE>
+__host__ int64_t stream_occupancy() {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_stream<MODE>, kThreads, 0) !=
+        hipSuccess)
+        return 0;
+    return blocks;
 }
 
 template <int MODE>
@@ -425,6 +466,21 @@ int launch_mode(const entq_plan_t *plan, bool stream, int64_t first, int64_t cou
 }
 
 }  // namespace
+
+int64_t resident_workgroups() {
+    static int64_t cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        int64_t per_cu = stream_occupancy<kModeSplit>();  // the largest LDS footprint
+        if (per_cu <= 0) per_cu = 1;
+        cached[dev] = (int64_t)cus * per_cu;
+    }
+    return cached[dev];
+}
 
 int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
                   const float *scales, const uint8_t *signmant, int32_t *status, void *stream) {

@@ -16,15 +16,16 @@ constexpr uint32_t kStateBytes = 4 * kLanes;       // states at the start of a r
 constexpr uint32_t kMaxChunkSymbols = 1u << 20;
 
 // Workgroup shape of the decode kernels: kWaves waves, each decoding one
-// chunk; all chunks of a workgroup belong to one tensor so they share the
-// slot table held in LDS.
-constexpr int kWaves = 8;
+// chunk at a time; all chunks of a workgroup belong to one tensor so they
+// share the slot table held in LDS. A workgroup's task is a run of chunks of
+// one tensor, decoded in rounds of up to kWaves chunks.
+constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 
-// The streaming kernel works in blocks of kBlockSteps steps (512 symbols
-// per wave); a tensor can use it when its chunk size is a multiple of the
+// The streaming kernel works in blocks of kBlockSteps steps (256 symbols
+// per chunk); a tensor can use it when its chunk size is a multiple of the
 // block, and, for bf16 output, when a block never crosses a row.
-constexpr uint32_t kBlockSteps = 8;
+constexpr uint32_t kBlockSteps = 4;
 constexpr uint32_t kBlockSyms = kBlockSteps * kLanes;
 
 // Slot table entry, one per slot (4096 per tensor), 8 bytes:
@@ -58,7 +59,7 @@ static_assert(sizeof(DevChunk) == 48, "DevChunk layout");
 
 struct DevTask {
     uint32_t first_chunk;   // into the plan's DevChunk array
-    uint32_t n_chunks;      // 1 .. kWaves, all of the same tensor
+    uint32_t n_chunks;      // >= 1, consecutive chunks of one tensor
     uint32_t tensor;
     uint32_t pad;
 };
@@ -92,4 +93,7 @@ enum DecodeMode { kModeCodes = 0, kModeBf16 = 1, kModeSplit = 2 };
 int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
                   const float *scales, const uint8_t *signmant, int32_t *status,
                   void *stream);
+// Workgroups of the decode kernels that fit on the current device at once
+// (compute units x workgroups per compute unit); 0 if HIP cannot tell.
+int64_t resident_workgroups();
 }  // namespace entq

@@ -135,12 +135,76 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         if (slot >= 0) return ENTQ_EBADINDEX;  // two chunks for one place
         slot = c;
     }
-    int64_t n_tasks = 0;
-    for (int t = 0; t < n_tensors; ++t) {
+    for (int t = 0; t < n_tensors; ++t)
         for (int64_t s : slot_of[t])
             if (s < 0) return ENTQ_EBADINDEX;  // a hole
-        n_tasks += ((int64_t)slot_of[t].size() + entq::kWaves - 1) / entq::kWaves;
+
+    // ---- task groups: block- and row-aligned tensors first, then
+    // block-aligned, then the rest (the launcher picks a kernel per group)
+    auto group_of = [&](int t) {
+        const entq_tensor_desc &td = tensors[t];
+        // the streaming kernel writes 4 outputs per lane and streams the
+        // sign+mantissa bytes 16 at a time: chunk sizes must be whole blocks
+        // and outputs 16-aligned
+        if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return 2;
+        return (td.cols % entq::kBlockSyms) ? 1 : 0;
+    };
+    std::vector<int> order;
+    for (int g = 0; g < 3; ++g)
+        for (int t = 0; t < n_tensors; ++t)
+            if (group_of(t) == g && !slot_of[t].empty()) order.push_back(t);
+    std::vector<int64_t> chunk_base(n_tensors, 0);  // first DevChunk of each tensor
+    {
+        int64_t c = 0;
+        for (int t : order) { chunk_base[t] = c; c += (int64_t)slot_of[t].size(); }
     }
+    // Tasks. Chunks cost about the same, so a launch finishes when its
+    // busiest workgroup does. When a group holds more chunks than one round
+    // of all resident workgroups can take, every resident workgroup gets one
+    // task: the tensors share the workgroups in proportion to their chunks
+    // and each splits its chunks into near-equal runs.
+    const int64_t slots = std::max<int64_t>(1, entq::resident_workgroups());
+    std::vector<entq::DevTask> task_list;
+    int64_t group_end[3] = {0, 0, 0};
+    for (int g = 0; g < 3; ++g) {
+        std::vector<int> tens;
+        int64_t K = 0;
+        for (int t : order)
+            if (group_of(t) == g) { tens.push_back(t); K += (int64_t)slot_of[t].size(); }
+        std::vector<int64_t> share(tens.size());
+        if (K <= slots * entq::kWaves) {
+            for (size_t i = 0; i < tens.size(); ++i)
+                share[i] = ((int64_t)slot_of[tens[i]].size() + entq::kWaves - 1) / entq::kWaves;
+        } else {
+            // largest-remainder apportionment of the slots, at least one each
+            std::vector<std::pair<double, size_t>> frac;
+            int64_t given = 0;
+            for (size_t i = 0; i < tens.size(); ++i) {
+                const double q = (double)slots * (double)slot_of[tens[i]].size() / (double)K;
+                share[i] = std::max<int64_t>(1, (int64_t)q);
+                given += share[i];
+                frac.emplace_back(q - (double)(int64_t)q, i);
+            }
+            std::sort(frac.begin(), frac.end(), [](auto &a, auto &b) { return a.first > b.first; });
+            for (size_t j = 0; given < slots && j < frac.size(); ++j, ++given) share[frac[j].second]++;
+        }
+        for (size_t i = 0; i < tens.size(); ++i) {
+            const int t = tens[i];
+            const int64_t k = (int64_t)slot_of[t].size();
+            const int64_t parts = std::min(share[i], k);
+            for (int64_t j = 0; j < parts; ++j) {
+                const int64_t lo = k * j / parts, hi = k * (j + 1) / parts;
+                entq::DevTask d;
+                d.first_chunk = (uint32_t)(chunk_base[t] + lo);
+                d.n_chunks = (uint32_t)(hi - lo);
+                d.tensor = (uint32_t)t;
+                d.pad = 0;
+                task_list.push_back(d);
+            }
+        }
+        group_end[g] = (int64_t)task_list.size();
+    }
+    const int64_t n_tasks = (int64_t)task_list.size();
 
     const Layout lay = layout_for(n_tensors, n_chunks, n_tasks);
     if (workspace_bytes < lay.total) return ENTQ_EWORKSPACE;
@@ -168,25 +232,9 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         dten[t].cols = tensors[t].cols;
         dten[t].kind = tensors[t].kind;
     }
-    // task groups: block- and row-aligned tensors first, then block-aligned,
-    // then the rest (the launcher picks a kernel per group)
-    auto group_of = [&](int t) {
+    for (int t : order) {
         const entq_tensor_desc &td = tensors[t];
-        // the streaming kernel writes 8 outputs per lane with 16-byte
-        // accesses: chunk sizes must be whole blocks and outputs 16-aligned
-        if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return 2;
-        return (td.cols % entq::kBlockSyms) ? 1 : 0;
-    };
-    int64_t c = 0, task = 0;
-    int64_t group_end[3] = {0, 0, 0};
-    std::vector<int> order;
-    for (int g = 0; g < 3; ++g)
-        for (int t = 0; t < n_tensors; ++t)
-            if (group_of(t) == g) order.push_back(t);
-    for (int oi = 0; oi < (int)order.size(); ++oi) {
-        const int t = order[oi];
-        const entq_tensor_desc &td = tensors[t];
-        const int64_t first = c;
+        int64_t c = chunk_base[t];
         for (int64_t s : slot_of[t]) {
             const entq_chunk_desc &cd = chunk_index[s];
             entq::DevChunk &d = dch[c++];
@@ -199,14 +247,8 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
             d.status_index = (uint32_t)s;
             d.tensor = (uint32_t)t;
         }
-        for (int64_t b = first; b < c; b += entq::kWaves) {
-            dtask[task].first_chunk = (uint32_t)b;
-            dtask[task].n_chunks = (uint32_t)std::min<int64_t>(entq::kWaves, c - b);
-            dtask[task].tensor = (uint32_t)t;
-            ++task;
-        }
-        for (int g = group_of(t); g < 3; ++g) group_end[g] = task;
     }
+    std::copy(task_list.begin(), task_list.end(), dtask);
 
     if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
         hipSuccess) {
