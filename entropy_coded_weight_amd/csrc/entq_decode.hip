@@ -21,15 +21,15 @@
 //  * decode_stream (the hot path): the word stream reaches LDS through a
 //    per-wave ring fed by direct global->LDS loads issued far ahead of use,
 //    so a renormalisation read is an LDS read; decoded bytes are staged in
-//    LDS for a block of 8 steps and leave as 8 consecutive outputs per lane
-//    (one 16-byte store for bf16), the fp32 row-scale multiply and the bf16
+//    LDS for a block of 4 steps and leave as 4 consecutive outputs per lane
+//    (one 8-byte store for bf16), the fp32 row-scale multiply and the bf16
 //    rounding fused into that store. Like DFloat11's kernel it stages output
 //    on chip and writes it coalesced [DFloat11 write-up, "Kernels GPU de 2
 //    etapas y metadatos auxiliares"], but rANS needs no counting pass: a
 //    chunk's output position is known up front.
 //  * decode_simple: one symbol per lane per step straight from global
 //    memory; used for tensors whose chunk size or row length is not a
-//    multiple of the 512-symbol block.
+//    multiple of the 256-symbol block.
 #include <hip/hip_runtime.h>
 
 #include "entq.h"
@@ -54,6 +54,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) {
 __device__ __forceinline__ float mul_value_scale(float v, float s) {
     float r;
     asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(s));
+    return r;
+}
+
+// The same with a wave-uniform scale taken straight from a scalar register
+// (the VOP3 form reads an SGPR as its second operand; no copy to a VGPR).
+__device__ __forceinline__ float mul_value_uscale(float v, float s) {
+    float r;
+    asm("v_mul_f32_e64 %0, %1, %2" : "=v"(r) : "v"(v), "s"(s));
     return r;
 }
 
@@ -300,7 +308,7 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t d, float scale) {
         v0 = (float)((int32_t)(d << 16) >> 24);
         v1 = (float)((int32_t)d >> 24);
     }
-    return bf16x2_bits(mul_value_scale(v0, scale), mul_value_scale(v1, scale));
+    return bf16x2_bits(mul_value_uscale(v0, scale), mul_value_uscale(v1, scale));
 }
 
 // sign << 15 | exponent << 7 | mantissa for two elements: q holds, per
@@ -332,6 +340,17 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     // number of waves busy
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
     const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    // Wave priority by progress: a wave drops one level each time it has
+    // done a quarter of its blocks, so waves that are behind win issue
+    // arbitration. (The default favours the oldest waves: the younger
+    // workgroup on a CU, and the younger waves of a workgroup, then finish
+    // long after the rest, with the CU half idle.)
+    uint32_t my_blocks = 0;
+    for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
+        my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
+    const uint32_t quarter = my_blocks / 4 ? my_blocks / 4 : 1;
+    uint32_t done = 0, prio_at = quarter, prio = 3;
+    __builtin_amdgcn_s_setprio(3);
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         const uint8_t *region = blob + ch.byte_offset;
@@ -371,6 +390,13 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         const uint32_t ring_mask = ring_mask_vgpr();
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
+            if (++done == prio_at) {
+                prio_at += quarter;
+                --prio;
+                if (prio == 2) __builtin_amdgcn_s_setprio(2);
+                else if (prio == 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
             if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
@@ -381,16 +407,18 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
                 o8 += kBlockSyms;
             } else if (MODE == kModeBf16) {
-                const uint2 w = e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
-                                     : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
-                reinterpret_cast<uint2 *>(o16)[lane] = w;
-                o16 += kBlockSyms;
-                col += kBlockSyms;
+                // the previous block ended a row: this one starts the next
+                // (only rows that get outputs have their scale read)
                 if (col == cols) {
                     col = 0;
                     ++scale_row;
                     scale = *scale_row;
                 }
+                const uint2 w = e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
+                                     : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
+                reinterpret_cast<uint2 *>(o16)[lane] = w;
+                o16 += kBlockSyms;
+                col += kBlockSyms;
             } else {
                 wait_vm<0>();  // this block's sign+mantissa bytes
                 const uint32_t sm4 = *reinterpret_cast<const uint32_t *>(G.sm[b & 1] + 4u * lane);
@@ -409,6 +437,10 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         const uint32_t rest = n - full_blocks * kBlockSyms;
         if (rest) {
             if (s.p > s.horizon) ring_service(s, lane);
+            if (MODE == kModeBf16 && col == cols) {
+                ++scale_row;
+                scale = *scale_row;
+            }
             for (uint32_t t = 0; 64u * t < rest; ++t)
                 stream_step<true>(x, s.p, s.ring, ring_mask, T, G.stage + 64u * t, lane,
                                   64u * t + lane < rest);

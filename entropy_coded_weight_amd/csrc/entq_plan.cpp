@@ -159,10 +159,11 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         for (int t : order) { chunk_base[t] = c; c += (int64_t)slot_of[t].size(); }
     }
     // Tasks. Chunks cost about the same, so a launch finishes when its
-    // busiest workgroup does. When a group holds more chunks than one round
-    // of all resident workgroups can take, every resident workgroup gets one
-    // task: the tensors share the workgroups in proportion to their chunks
-    // and each splits its chunks into near-equal runs.
+    // busiest workgroup does: when a group holds more chunks than there are
+    // resident workgroups, every resident workgroup gets one task, the
+    // tensors sharing the workgroups in proportion to their chunks and each
+    // splitting its chunks into near-equal runs; otherwise every chunk is a
+    // task of its own (latency-bound, so spread over as many CUs as possible).
     const int64_t slots = std::max<int64_t>(1, entq::resident_workgroups());
     std::vector<entq::DevTask> task_list;
     int64_t group_end[3] = {0, 0, 0};
@@ -172,9 +173,8 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         for (int t : order)
             if (group_of(t) == g) { tens.push_back(t); K += (int64_t)slot_of[t].size(); }
         std::vector<int64_t> share(tens.size());
-        if (K <= slots * entq::kWaves) {
-            for (size_t i = 0; i < tens.size(); ++i)
-                share[i] = ((int64_t)slot_of[tens[i]].size() + entq::kWaves - 1) / entq::kWaves;
+        if (K <= slots) {
+            for (size_t i = 0; i < tens.size(); ++i) share[i] = (int64_t)slot_of[tens[i]].size();
         } else {
             // largest-remainder apportionment of the slots, at least one each
             std::vector<std::pair<double, size_t>> frac;
