@@ -30,6 +30,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Hardware byte counts of the decode kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, calibrated against a plain copy), valid only for the kernel source
+# they were taken with (its SHA-256 is stored beside them).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_bf16_llama2_70b_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "entropy_coded_weight_amd", "csrc", "entq_decode.hip")
 METRIC = "decoded params/s and achieved HBM GB/s (% of peak) for 70B-shaped layer decode"
 
 
@@ -58,7 +63,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "the decode has no cross-GPU step -- see DESIGN.md for how it shards", file=sys.stderr)
+              "the decode has no cross-GPU step: each GPU decodes the chunks of its own shard", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -183,11 +188,25 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter record, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
 
 
 def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
