@@ -45,8 +45,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=80,
                     help="layers in the model (80 is the workload; fewer only for quick checks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,6 +139,7 @@ def main():
     total_ms = start.elapsed_time(stop)
     launch_ms = np.array([[e[0].elapsed_time(e[1]) for e in ev[s]] for s in range(args.steps)])
     ms_per_step = total_ms / args.steps
+    step_ms = launch_ms.sum(axis=1)  # per step: sum of its launches (HIP events)
     params_total = params_per_layer * args.layers
     value = params_total / (ms_per_step / 1e3)
 
@@ -152,6 +153,9 @@ def main():
         f"(wall {1e3 * t_wall / args.steps:.3f}), launch mean {1e6 * mean_launch_s:.1f} us "
         f"p10 {1e3 * np.percentile(launch_ms, 10):.1f} p90 "
         f"{1e3 * np.percentile(launch_ms, 90):.1f} us, {achieved_gbs:.0f} GB/s")
+
+    # ------------------------------------------- context: device-to-device copy
+    copy_gbs = d2d_copy_gbs(out)
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None
@@ -181,6 +185,9 @@ def main():
             "bits_per_param": 8.0 * blob_mean / params_per_layer,
             "algorithmic_bytes_per_layer": alg_bytes_layer,
             "hbm_gbs_whole_step": alg_bytes_layer * args.layers / (ms_per_step / 1e3) / 1e9,
+            "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+            "launch_us_p10_p50_p90": [float(1e3 * np.percentile(launch_ms, q)) for q in (10, 50, 90)],
+            "d2d_copy_gbs_context": copy_gbs,
         },
         "roofline": {
             "bound": "hbm",
@@ -193,6 +200,23 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def d2d_copy_gbs(buf):
+    """Bandwidth of a plain device-to-device copy of the layer buffer (read +
+    write bytes / time, median of 5), as context for the decode's GB/s."""
+    import torch
+    other = torch.empty_like(buf)
+    times = []
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        other.copy_(buf)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    del other
+    return 2.0 * buf.numel() * buf.element_size() / float(np.median(times[1:])) / 1e9
 
 
 def measured_traffic():
