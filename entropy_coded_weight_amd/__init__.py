@@ -15,6 +15,9 @@ Entry points (the C ABI in include/entq.h, same names):
   count_symbols, build_freq, encode_tensor, bf16_split   host encoder
   encode_batch(...)       -> Batch    convenience: a list of tensors -> blob,
                                       tables, chunk index
+  count_symbols_device, encode_device, pack_device, region_bytes
+                                      on-device encoder (same regions)
+  encode_batch_device(...) -> DeviceBatch  the device path of encode_batch
 """
 from __future__ import annotations
 
@@ -74,6 +77,11 @@ def lib():
             "entq_encode_tensor": (c.c_int, [vp, u64, c.c_uint32, vp, c.c_uint32, u64, vp, u64,
                                              vp, vp, c.c_int]),
             "entq_bf16_split": (c.c_int, [vp, u64, vp, vp, c.c_int]),
+            "entq_count_symbols_device": (c.c_int, [vp, u64, vp, vp]),
+            "entq_encode_device_scratch_bytes": (u64, [u64, c.c_uint32]),
+            "entq_region_bytes": (u64, [c.c_uint32]),
+            "entq_encode_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, u64, vp, vp]),
+            "entq_pack_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -85,7 +93,9 @@ def lib():
 
 EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decode_bf16_split",
             "entq_plan_destroy", "entq_status_str", "entq_plan_info", "entq_count_symbols",
-            "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split"]
+            "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split",
+            "entq_count_symbols_device", "entq_encode_device_scratch_bytes", "entq_region_bytes",
+            "entq_encode_device", "entq_pack_device"]
 
 
 def _str(status: int) -> str:
@@ -293,3 +303,110 @@ def encode_batch(specs, n_threads: int | None = None) -> Batch:
     blob = np.concatenate(regions) if regions else np.zeros(0, np.uint8)
     chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
     return Batch(blob, tens, freqs, chunks)
+
+
+# --------------------------------------------------------------------------
+# on-device encoder
+# --------------------------------------------------------------------------
+
+def count_symbols_device(symbols, counts=None, stream=None):
+    """Byte counts of a device uint8 tensor (16-byte aligned) into a device
+    uint64 tensor [256] (zeroed here unless given)."""
+    import torch
+    if counts is None:
+        counts = torch.zeros(256, dtype=torch.int64, device=symbols.device)
+    _check(lib().entq_count_symbols_device(_ptr(symbols) or None, symbols.numel(), _ptr(counts),
+                                           _stream(stream)), "entq_count_symbols_device")
+    return counts
+
+
+def region_bytes(n_words: int) -> int:
+    return int(lib().entq_region_bytes(int(n_words)))
+
+
+def encode_device(symbols, chunk_symbols: int, freq: np.ndarray, scratch, n_words, stream=None):
+    """Encode one tensor's device symbols into ``scratch`` (device uint8,
+    entq_encode_device_scratch_bytes long); word counts to ``n_words``
+    (device int32 [n_chunks], 0xFFFFFFFF marks a chunk with a frequency-0
+    symbol)."""
+    freq = np.ascontiguousarray(freq, dtype=np.uint16)
+    _check(lib().entq_encode_device(_ptr(symbols) or None, symbols.numel(), int(chunk_symbols),
+                                    _ptr(freq), _ptr(scratch) or None,
+                                    scratch.numel() if scratch is not None else 0,
+                                    _ptr(n_words) or None, _stream(stream)), "entq_encode_device")
+
+
+def pack_device(scratch, n: int, chunk_symbols: int, n_words, offsets, blob, stream=None):
+    _check(lib().entq_pack_device(_ptr(scratch) or None, int(n), int(chunk_symbols),
+                                  _ptr(n_words) or None, _ptr(offsets) or None,
+                                  _ptr(blob) or None, _stream(stream)), "entq_pack_device")
+
+
+@dataclass
+class DeviceBatch:
+    """Like Batch, with the blob left in device memory (a torch uint8 view)."""
+    blob: object                # torch uint8 on the device
+    tensors: np.ndarray
+    freq: np.ndarray
+    chunks: np.ndarray
+
+    @property
+    def out_elems(self) -> int:
+        t = self.tensors
+        return int((t["out_elem_offset"] + t["n_symbols"]).max()) if t.size else 0
+
+
+def encode_batch_device(specs, stream=None) -> DeviceBatch:
+    """The device path of encode_batch: specs' ``symbols`` are device uint8
+    tensors (contiguous, 16-byte aligned). Counts, encoding and packing run
+    on the GPU; the frequency tables and the region offsets are settled on
+    the host between the steps (the word counts come back once per
+    tensor)."""
+    import torch
+    dev = specs[0]["symbols"].device if specs else torch.device("cuda")
+    s = torch.cuda.current_stream() if stream is None else stream
+    tens = np.zeros(len(specs), TENSOR_DESC)
+    freqs = np.zeros((len(specs), 256), np.uint16)
+    bound = sum(int(lib().entq_encode_bound(sp["symbols"].numel(), int(sp["chunk_symbols"])))
+                for sp in specs)
+    scratch_need = max([int(lib().entq_encode_device_scratch_bytes(sp["symbols"].numel(),
+                                                                    int(sp["chunk_symbols"])))
+                        for sp in specs] + [16])
+    blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(scratch_need, dtype=torch.uint8, device=dev)
+    descs = []
+    off = out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        sym = sp["symbols"]
+        rows, cols, C = int(sp["rows"]), int(sp["cols"]), int(sp["chunk_symbols"])
+        n = sym.numel()
+        assert n == rows * cols and sym.dtype == torch.uint8 and sym.is_contiguous()
+        k = -(-n // C)
+        f = build_freq(count_symbols_device(sym, stream=s).cpu().numpy().view(np.uint64))
+        if n == 0:
+            f[0] = PROB_SCALE
+        ch = np.zeros(k, CHUNK_DESC)
+        if k:
+            nw_d = torch.empty(k, dtype=torch.int32, device=dev)
+            encode_device(sym, C, f, scratch, nw_d, s)
+            nw = nw_d.cpu().numpy().view(np.uint32)
+            if (nw == 0xFFFFFFFF).any():
+                raise EntqError(-2, "entq_encode_device: a symbol has frequency 0")
+            sizes = np.array([region_bytes(w) for w in nw], np.uint64)
+            offs = off + np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+            ch["tensor"] = t
+            ch["n_symbols"] = np.minimum(C, n - np.arange(k, dtype=np.int64) * C)
+            ch["n_words"] = nw
+            ch["byte_offset"] = offs
+            ch["elem_offset"] = np.arange(k, dtype=np.uint64) * C
+            offs_d = torch.from_numpy(offs.view(np.int64)).to(dev)
+            pack_device(scratch, n, C, nw_d, offs_d, blob, s)
+            off += int(sizes.sum())
+        descs.append(ch)
+        tens[t] = (int(sp["kind"]), rows, cols, C, n, out_off, scale_off)
+        freqs[t] = f
+        out_off += n
+        scale_off += rows
+    torch.cuda.current_stream().synchronize() if stream is None else s.synchronize()
+    chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
+    return DeviceBatch(blob[:off], tens, freqs, chunks)

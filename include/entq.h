@@ -205,6 +205,56 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
 entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uint8_t *sm_out,
                             int n_threads);
 
+/* ---- On-device encoder (one wavefront per chunk; same regions as the
+ * host encoder, byte for byte) ----
+ *
+ * The pages compress with a GPU ANS library before deployment [EntQuant,
+ * "Float8@2bits: Entropy Coding Enables Data-Free Model Compression",
+ * technical summary §2 "Codificación de Pesos"]; these calls encode the
+ * library's own format on the GPU. A tensor is encoded in three enqueued
+ * steps, with the frequency table and the region offsets settled on the
+ * host between them:
+ *   1. entq_count_symbols_device -> counts (copy to host) -> entq_build_freq
+ *   2. entq_encode_device -> per-chunk word counts (copy to host); region k
+ *      takes entq_region_bytes(n_words[k]) bytes at a 16-byte-aligned offset
+ *   3. entq_pack_device -> the regions in the caller's blob
+ * All buffers are caller-owned device memory; all work is enqueued on
+ * `stream` and nothing synchronises. */
+
+/* Adds the counts of each byte value in d_symbols[0..n) to d_counts[256]
+ * (device u64, 8-byte aligned; the caller zeroes it first). d_symbols is
+ * 16-byte aligned. */
+entq_status entq_count_symbols_device(const uint8_t *d_symbols, uint64_t n, uint64_t *d_counts,
+                                      void *stream);
+
+/* Bytes of scratch entq_encode_device needs for n symbols in chunks of
+ * chunk_symbols: per chunk 64 states and room for one word per symbol. */
+uint64_t entq_encode_device_scratch_bytes(uint64_t n_symbols, uint32_t chunk_symbols);
+
+/* Bytes of the region of a chunk with n_words words: 256 + 2 n_words,
+ * rounded up to 16. */
+uint64_t entq_region_bytes(uint32_t n_words);
+
+/* Encodes the n symbols of one tensor (d_symbols, device, 16-byte aligned)
+ * in chunks of chunk_symbols (a multiple of 64, at most 2^20) with the host
+ * table freq[256] (sum 4096). Chunk k's final states and words go to
+ * d_scratch (device, 16-byte aligned, at least
+ * entq_encode_device_scratch_bytes; layout private to the library) and its
+ * word count to d_n_words[k] (device u32), or 0xFFFFFFFF if the chunk holds
+ * a symbol whose frequency is 0 (such a chunk cannot be coded; pack skips
+ * it). Returns ENTQ_EBADTABLE for a table not summing to 4096. */
+entq_status entq_encode_device(const uint8_t *d_symbols, uint64_t n, uint32_t chunk_symbols,
+                               const uint16_t freq[256], void *d_scratch, uint64_t scratch_bytes,
+                               uint32_t *d_n_words, void *stream);
+
+/* Writes the regions of an encoded tensor into d_blob (device, 16-byte
+ * aligned): region k (64 states, the chunk's words in decoding order, zero
+ * padding) at byte d_byte_offsets[k] (device u64, multiples of 16, regions
+ * not overlapping; the caller lays them out with entq_region_bytes). */
+entq_status entq_pack_device(const void *d_scratch, uint64_t n, uint32_t chunk_symbols,
+                             const uint32_t *d_n_words, const uint64_t *d_byte_offsets,
+                             void *d_blob, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,137 @@
+"""GPU parity of the on-device encoder (through the C ABI): its containers
+must be byte-identical to the oracle's encoder (small tensors) and to the
+library's host encoder, which the CPU suite proves byte-identical to the
+oracle's (the full 70B-shaped layer). Also: device byte counts against
+numpy, decode of a device-encoded container back to the source codes, and
+the frequency-0 rejection."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-encoder] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()
+    return E
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).ravel().copy()).cuda()
+
+
+def _dev_specs(specs):
+    return [dict(sp, symbols=_dev(sp["symbols"])) for sp in specs]
+
+
+def _oracle_chunks(c):
+    return np.array([(int(r[0]), int(r[1]), int(r[2]), int(r[3]), int(r[4])) for r in c.chunks],
+                    dtype=np.uint64).reshape(-1, 5)
+
+
+def _device_chunks(b):
+    ch = b.chunks
+    return np.stack([ch["tensor"], ch["n_symbols"], ch["n_words"], ch["byte_offset"],
+                     ch["elem_offset"]], axis=1).astype(np.uint64)
+
+
+def _check_against_oracle(E, specs):
+    c = oracle.encode_container(specs)
+    b = E.encode_batch_device(_dev_specs(specs))
+    blob = b.blob.cpu().numpy()
+    assert blob.size == c.blob.size
+    assert np.array_equal(blob, c.blob)
+    assert np.array_equal(_device_chunks(b), _oracle_chunks(c))
+    for t, td in enumerate(c.tensors):
+        assert np.array_equal(b.freq[t], td["freq"])
+    return b
+
+
+def test_count_symbols_device(E):
+    import torch
+    rng = np.random.default_rng(5)
+    for n in (0, 1, 15, 16, 17, 4095, 1 << 20, (1 << 20) + 7):
+        a = rng.integers(0, 256, n, dtype=np.uint8)
+        a[: n // 3] = 7  # a heavy symbol
+        got = E.count_symbols_device(_dev(a) if n else torch.zeros(16, dtype=torch.uint8,
+                                                                   device="cuda")[:0])
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().view(np.uint64),
+                              np.bincount(a, minlength=256).astype(np.uint64)), n
+
+
+def test_tiny_laplace_and_e4m3_match_oracle(E):
+    _say("tiny laplace 256x256, 4096-symbol chunks")
+    _check_against_oracle(E, synth.tiny_int8_laplace())
+    _say("e4m3 4096x4096")
+    _check_against_oracle(E, synth.e4m3_matrix())
+
+
+def test_ragged_and_degenerate_tensors_match_oracle(E):
+    specs = []
+    for seed, (r, c, C) in enumerate([(3, 7, 64), (1, 65, 64), (17, 129, 4096), (5, 4097, 4096),
+                                      (33, 1000, 65536), (2, 65536 + 64, 65536)]):
+        specs.append(synth.random_int8_tensor(r, c, 1.5 + seed, seed, C))
+    one = synth.random_int8_tensor(16, 64, 1.0, 40, 64)
+    one["symbols"] = np.full(one["symbols"].shape, 9, np.uint8)  # single symbol: f = 4096
+    specs.append(one)
+    allb = synth.random_int8_tensor(64, 512, 1.0, 41, 4096)
+    allb["symbols"] = synth.random_bytes(64 * 512, 41).view(np.uint8)  # all 256 byte values
+    specs.append(allb)
+    _say(f"{len(specs)} ragged / degenerate tensors")
+    _check_against_oracle(E, specs)
+
+
+def test_device_container_decodes_to_source(E):
+    import torch
+    specs = synth.llama2_13b_block(shapes=[("q", 5120, 5120), ("down", 5120, 13824)])
+    b = E.encode_batch_device(_dev_specs(specs))
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
+    out = torch.zeros(b.out_elems, dtype=torch.uint8, device="cuda")
+    status = torch.full((len(b.chunks),), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, b.blob, out, E.OUT_CODES, None, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    src = np.concatenate([np.ascontiguousarray(s["symbols"]).view(np.uint8).ravel()
+                          for s in specs])
+    assert np.array_equal(out.cpu().numpy(), src)
+
+
+def test_frequency_zero_symbol_is_rejected(E):
+    import torch
+    sym = np.zeros(64 * 70, np.uint8)
+    sym[64 * 65 + 3] = 5          # in chunk 1 (chunks of 4096)
+    freq = np.zeros(256, np.uint16)
+    freq[0] = 4096                # byte 5 has frequency 0
+    d = _dev(sym)
+    scratch = torch.empty(int(E.lib().entq_encode_device_scratch_bytes(sym.size, 4096)),
+                          dtype=torch.uint8, device="cuda")
+    nw = torch.zeros(2, dtype=torch.int32, device="cuda")
+    E.encode_device(d, 4096, freq, scratch, nw)
+    torch.cuda.synchronize()
+    got = nw.cpu().numpy().view(np.uint32)
+    assert got[0] == 0 and got[1] == 0xFFFFFFFF
+    with pytest.raises(E.EntqError):
+        E.encode_device(d, 4096, np.zeros(256, np.uint16), scratch, nw)  # sum != 4096
+
+
+def test_llama2_70b_layer_matches_host_encoder(E):
+    _say("70B-shaped layer 0: device encoder vs host encoder (855.6 M symbols)")
+    specs = synth.llama2_70b_layer(0)
+    host = E.encode_batch(specs)
+    dev = E.encode_batch_device(_dev_specs(specs))
+    assert dev.blob.numel() == host.blob.size
+    assert np.array_equal(dev.blob.cpu().numpy(), host.blob)
+    assert np.array_equal(dev.chunks, host.chunks)
+    assert np.array_equal(dev.freq, host.freq)
