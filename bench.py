@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--cpu-sample-tensors", type=int, default=5,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline")
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--path", choices=("decode", "encode"), default="decode",
+                    help="decode: the layer-by-layer decode (the headline line); encode: the "
+                         "on-device encoder over 70B-shaped layers")
+    ap.add_argument("--encode-layers", type=int, default=4,
+                    help="resident layers of source codes the encode steps cycle through")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain fp32 negate (read N MiB, write N MiB) before timing, as a "
                          "known-size reference for hardware byte counters")
@@ -65,6 +70,8 @@ def main():
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the decode has no cross-GPU step: each GPU decodes the chunks of its own shard", file=sys.stderr)
         sys.exit(2)
+    if args.path == "encode":
+        return bench_encode(args)
     import torch
 
     import entropy_coded_weight_amd as E
@@ -266,6 +273,130 @@ def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
     return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0, first {len(specs)} tensors ({n_sample} params): single-threaded "
                       "C oracle rANS decode + fp32 dequant + RNE bf16 from the same compressed bytes"}
+
+
+ENCODE_METRIC = "encoded symbols/s for 70B-shaped layer encode on the GPU (counts, rANS encode, layout, pack)"
+
+
+def bench_encode(args):
+    """One step = the on-device encoder over one 70B-shaped layer (855.6 M
+    int8 codes, 7 tensors, 65,536-symbol chunks), resident in HBM: byte
+    counts, frequency tables (host), 64-lane rANS encode, region layout and
+    packing, ending with the chunk index on the host. The steps cycle over
+    --encode-layers layers. The roofline entry is the encode kernel's:
+    algorithmic bytes = symbols read + final states and words written."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    nthreads = args.threads or synth.default_threads()
+    layers, host_layer0 = [], None
+    t0 = time.time()
+    for layer in range(args.encode_layers):
+        specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
+        if layer == 0:
+            host_layer0 = specs
+        layers.append([dict(sp, symbols=torch.from_numpy(
+            np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()).to(dev)) for sp in specs])
+        log(f"encode: layer {layer} resident ({time.time() - t0:.1f}s)")
+    n_layer = sum(sp["symbols"].numel() for sp in layers[0])
+    stream = torch.cuda.current_stream()
+    for w in range(args.warmup):
+        E.encode_batch_device(layers[w % len(layers)], stream)
+    torch.cuda.synchronize()
+    events, wall, comp = [], [], []
+    for st in range(args.steps):
+        ev = []
+        t = time.perf_counter()
+        b = E.encode_batch_device(layers[st % len(layers)], stream, events=ev)
+        wall.append(time.perf_counter() - t)
+        comp.append(int(b.blob.numel()))
+        events.append(ev)
+        del b
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * float(np.mean(wall))
+    value = n_layer / (ms_per_step / 1e3)
+    per_kind = {}
+    for ev in events:
+        for name, a, z in ev:
+            per_kind.setdefault(name, []).append(a.elapsed_time(z) * 1e3)
+    # per step, kernel microseconds by kind; encode launches per tensor
+    kind_us = {k: float(np.sum(v)) / args.steps for k, v in per_kind.items()}
+    enc_us = np.array(per_kind["encode"])
+    n_t = len(layers[0])
+    comp_mean = float(np.mean(comp))
+    # encode kernel: reads every symbol once, writes 64 states + the words of
+    # each chunk (the compressed bytes minus the regions' zero padding ~ the
+    # blob); counted per step over its n_t launches.
+    enc_bytes_step = n_layer + comp_mean
+    enc_gbs = enc_bytes_step / (kind_us["encode"] / 1e6) / 1e9
+    log(f"encode: {ms_per_step:.2f} ms/step wall, kernels per step (us): "
+        + ", ".join(f"{k} {v:.0f}" for k, v in kind_us.items())
+        + f"; encode {n_layer / kind_us['encode'] / 1e6:.3f} T sym/s, {enc_gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = encode_cpu_baseline(host_layer0[1:3], layers[0][1:3], stream)
+    rec = {
+        "metric": ENCODE_METRIC,
+        "value": value,
+        "unit": "symbols/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8->u16 words+u32 states",
+        "data": "synthetic (seeded int8 codes of the stated distribution; no trained weights)",
+        "config": {
+            "workload": "llama2-70b-shaped layer encode, int8 codes -> rANS container, 65,536-symbol chunks",
+            "layers_cycled": len(layers),
+            "symbols_per_layer": n_layer,
+            "compressed_bytes_per_layer": comp_mean,
+            "kernel_us_per_step": kind_us,
+            "encode_launch_us_p10_p50_p90": [float(np.percentile(enc_us, q)) for q in (10, 50, 90)],
+            "step_ms_wall_p10_p50_p90": [1e3 * float(np.percentile(wall, q)) for q in (10, 50, 90)],
+            "note": "value is wall time per layer including the two host reads (counts; word "
+                    "counts and offsets) and the host frequency tables",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": enc_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": enc_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def encode_cpu_baseline(specs, dspecs, stream):
+    """The oracle encoder (single-threaded C: counts, table, 64-lane rANS,
+    layout) over the given tensors, timed on this host; its blob must equal
+    the device encoder's for the same tensors."""
+    import entropy_coded_weight_amd as E
+    import oracle
+
+    t = time.perf_counter()
+    c = oracle.encode_container(specs)
+    dt = time.perf_counter() - t
+    n = sum(int(np.asarray(sp["symbols"]).size) for sp in specs)
+    d = E.encode_batch_device(dspecs, stream)
+    ok = bool(d.blob.numel() == c.blob.size and np.array_equal(d.blob.cpu().numpy(), c.blob))
+    log(f"cpu oracle encode: {n} symbols in {dt:.2f}s ({n / dt / 1e6:.1f} M sym/s); "
+        f"matches GPU: {ok}")
+    if not ok:
+        raise SystemExit("device encoder differs from the oracle on the CPU-baseline sample")
+    return {"value": n / dt, "unit": "symbols/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, tensors k and v ({n} symbols): single-threaded C oracle "
+                      "counts + frequency table + 64-lane rANS encode + container layout"}
 
 
 if __name__ == "__main__":

@@ -41,6 +41,10 @@ TENSOR_DESC = np.dtype([("kind", "<u4"), ("rows", "<u4"), ("cols", "<u4"),
 CHUNK_DESC = np.dtype([("tensor", "<u4"), ("n_symbols", "<u4"), ("n_words", "<u4"),
                        ("reserved", "<u4"), ("byte_offset", "<u8"), ("elem_offset", "<u8")])
 assert TENSOR_DESC.itemsize == 40 and CHUNK_DESC.itemsize == 32
+# entq_encode_job (include/entq.h): device pointers as integers
+ENCODE_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
+                       ("reserved", "<u4"), ("freq", "<u8"), ("scratch", "<u8"),
+                       ("scratch_bytes", "<u8"), ("n_words", "<u8")])
 
 
 class EntqError(RuntimeError):
@@ -82,6 +86,8 @@ def lib():
             "entq_region_bytes": (u64, [c.c_uint32]),
             "entq_encode_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, u64, vp, vp]),
             "entq_pack_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, vp, vp]),
+            "entq_region_offsets_device": (c.c_int, [vp, u64, u64, vp, vp, vp]),
+            "entq_encode_device_batch": (c.c_int, [vp, c.c_int, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -95,7 +101,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_plan_destroy", "entq_status_str", "entq_plan_info", "entq_count_symbols",
             "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split",
             "entq_count_symbols_device", "entq_encode_device_scratch_bytes", "entq_region_bytes",
-            "entq_encode_device", "entq_pack_device"]
+            "entq_encode_device", "entq_pack_device", "entq_region_offsets_device",
+            "entq_encode_device_batch"]
 
 
 def _str(status: int) -> str:
@@ -342,6 +349,28 @@ def pack_device(scratch, n: int, chunk_symbols: int, n_words, offsets, blob, str
                                   _ptr(blob) or None, _stream(stream)), "entq_pack_device")
 
 
+def encode_device_batch(jobs, stream=None):
+    """jobs: list of (symbols, chunk_symbols, freq, scratch, n_words) with
+    device tensors (freq: device uint16/int16 [256]); one launch per 16
+    tensors. A chunk of a tensor whose table is invalid or holds a
+    frequency-0 symbol gets word count 0xFFFFFFFF."""
+    arr = np.zeros(len(jobs), ENCODE_JOB)
+    for i, (sym, C, freq, scratch, nw) in enumerate(jobs):
+        arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(freq), _ptr(scratch),
+                  scratch.numel(), _ptr(nw))
+    _check(lib().entq_encode_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                          _stream(stream)), "entq_encode_device_batch")
+
+
+def region_offsets_device(n_words, offsets, end, base_offset: int = 0, stream=None):
+    """Region byte offsets of consecutive chunks from their device word
+    counts (int32 [k]) into ``offsets`` (device int64 [k]); ``end`` (device
+    int64 [1]) gets base_offset + all their bytes."""
+    _check(lib().entq_region_offsets_device(_ptr(n_words) or None, n_words.numel(),
+                                            int(base_offset), _ptr(offsets) or None, _ptr(end),
+                                            _stream(stream)), "entq_region_offsets_device")
+
+
 @dataclass
 class DeviceBatch:
     """Like Batch, with the blob left in device memory (a torch uint8 view)."""
@@ -356,57 +385,96 @@ class DeviceBatch:
         return int((t["out_elem_offset"] + t["n_symbols"]).max()) if t.size else 0
 
 
-def encode_batch_device(specs, stream=None) -> DeviceBatch:
+def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
     """The device path of encode_batch: specs' ``symbols`` are device uint8
-    tensors (contiguous, 16-byte aligned). Counts, encoding and packing run
-    on the GPU; the frequency tables and the region offsets are settled on
-    the host between the steps (the word counts come back once per
-    tensor)."""
+    tensors (contiguous, 16-byte aligned). Counts, encoding, the region
+    layout and packing run on the GPU, each step over all tensors; the
+    host reads the counts once (to build the frequency tables) and the word
+    counts and offsets once at the end (for the chunk index). With
+    ``events`` (a list), each kernel launch appends (name, start, end) HIP
+    events recorded on the stream around it."""
     import torch
     dev = specs[0]["symbols"].device if specs else torch.device("cuda")
-    s = torch.cuda.current_stream() if stream is None else stream
-    tens = np.zeros(len(specs), TENSOR_DESC)
-    freqs = np.zeros((len(specs), 256), np.uint16)
-    bound = sum(int(lib().entq_encode_bound(sp["symbols"].numel(), int(sp["chunk_symbols"])))
-                for sp in specs)
-    scratch_need = max([int(lib().entq_encode_device_scratch_bytes(sp["symbols"].numel(),
-                                                                    int(sp["chunk_symbols"])))
-                        for sp in specs] + [16])
-    blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
-    scratch = torch.empty(scratch_need, dtype=torch.uint8, device=dev)
-    descs = []
-    off = out_off = scale_off = 0
-    for t, sp in enumerate(specs):
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    T = len(specs)
+    shapes = []
+    for sp in specs:
         sym = sp["symbols"]
         rows, cols, C = int(sp["rows"]), int(sp["cols"]), int(sp["chunk_symbols"])
         n = sym.numel()
         assert n == rows * cols and sym.dtype == torch.uint8 and sym.is_contiguous()
-        k = -(-n // C)
-        f = build_freq(count_symbols_device(sym, stream=s).cpu().numpy().view(np.uint64))
-        if n == 0:
-            f[0] = PROB_SCALE
-        ch = np.zeros(k, CHUNK_DESC)
-        if k:
-            nw_d = torch.empty(k, dtype=torch.int32, device=dev)
-            encode_device(sym, C, f, scratch, nw_d, s)
-            nw = nw_d.cpu().numpy().view(np.uint32)
-            if (nw == 0xFFFFFFFF).any():
-                raise EntqError(-2, "entq_encode_device: a symbol has frequency 0")
-            sizes = np.array([region_bytes(w) for w in nw], np.uint64)
-            offs = off + np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
-            ch["tensor"] = t
-            ch["n_symbols"] = np.minimum(C, n - np.arange(k, dtype=np.int64) * C)
-            ch["n_words"] = nw
-            ch["byte_offset"] = offs
-            ch["elem_offset"] = np.arange(k, dtype=np.uint64) * C
-            offs_d = torch.from_numpy(offs.view(np.int64)).to(dev)
-            pack_device(scratch, n, C, nw_d, offs_d, blob, s)
-            off += int(sizes.sum())
-        descs.append(ch)
+        shapes.append((rows, cols, C, n, -(-n // C)))
+    k_all = sum(sh[4] for sh in shapes)
+    bound = sum(int(lib().entq_encode_bound(sh[3], sh[2])) for sh in shapes)
+    scr = [int(lib().entq_encode_device_scratch_bytes(sh[3], sh[2])) for sh in shapes]
+    scr_off = np.concatenate([[0], np.cumsum(scr)]).astype(np.int64)
+    blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(max(int(scr_off[-1]), 16), dtype=torch.uint8, device=dev)
+    counts = torch.zeros((max(T, 1), 256), dtype=torch.int64, device=dev)
+    nw_d = torch.empty(max(k_all, 1), dtype=torch.int32, device=dev)
+    offs_d = torch.empty(max(k_all, 1), dtype=torch.int64, device=dev)
+    end_d = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def timed(name, fn):
+        if events is None:
+            return fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        events.append((name, a, b))
+
+    with torch.cuda.stream(s):
+        for t, sp in enumerate(specs):
+            timed("count", lambda: count_symbols_device(sp["symbols"], counts[t], s))
+        s.synchronize()
+        host_counts = counts.cpu().numpy().view(np.uint64)
+        freqs = np.zeros((max(T, 1), 256), np.uint16)
+        for t in range(T):
+            freqs[t] = build_freq(host_counts[t])
+            if shapes[t][3] == 0:
+                freqs[t, 0] = PROB_SCALE
+        freq_d = torch.from_numpy(freqs.view(np.int16)).to(dev, non_blocking=False)
+        jobs, k0 = [], 0
+        for t, sp in enumerate(specs):
+            rows, cols, C, n, k = shapes[t]
+            if k:
+                jobs.append((sp["symbols"], C, freq_d[t], scratch[scr_off[t]:scr_off[t + 1]],
+                             nw_d[k0:k0 + k]))
+            k0 += k
+        if jobs:
+            timed("encode", lambda: encode_device_batch(jobs, s))
+        freqs = freqs[:T]
+        if k_all:
+            timed("offsets", lambda: region_offsets_device(nw_d[:k_all], offs_d[:k_all], end_d,
+                                                           0, s))
+        k0 = 0
+        for t, sp in enumerate(specs):
+            rows, cols, C, n, k = shapes[t]
+            if k:
+                timed("pack", lambda: pack_device(scratch[scr_off[t]:scr_off[t + 1]], n, C,
+                                                  nw_d[k0:k0 + k], offs_d[k0:k0 + k], blob, s))
+            k0 += k
+        s.synchronize()
+        nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
+        offs = offs_d[:k_all].cpu().numpy().view(np.uint64)
+        end = int(end_d.cpu().numpy()[0])
+    if (nw == 0xFFFFFFFF).any():
+        raise EntqError(-2, "entq_encode_device: a symbol has frequency 0")
+    tens = np.zeros(T, TENSOR_DESC)
+    chunks = np.zeros(k_all, CHUNK_DESC)
+    k0 = out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        rows, cols, C, n, k = shapes[t]
+        ch = chunks[k0:k0 + k]
+        ch["tensor"] = t
+        ch["n_symbols"] = np.minimum(C, n - np.arange(k, dtype=np.int64) * C)
+        ch["n_words"] = nw[k0:k0 + k]
+        ch["byte_offset"] = offs[k0:k0 + k]
+        ch["elem_offset"] = np.arange(k, dtype=np.uint64) * C
         tens[t] = (int(sp["kind"]), rows, cols, C, n, out_off, scale_off)
-        freqs[t] = f
         out_off += n
         scale_off += rows
-    torch.cuda.current_stream().synchronize() if stream is None else s.synchronize()
-    chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
-    return DeviceBatch(blob[:off], tens, freqs, chunks)
+        k0 += k
+    return DeviceBatch(blob[:end], tens, freqs, chunks)

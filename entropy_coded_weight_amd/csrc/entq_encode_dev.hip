@@ -27,27 +27,73 @@ namespace {
 
 constexpr int kEncWaves = 8;                 // chunks per workgroup
 constexpr int kEncThreads = kEncWaves * 64;
-constexpr uint32_t kEncStageSteps = 16;      // steps per symbol stage (1 KB)
+constexpr uint32_t kEncGroup = 16;           // steps whose symbols are loaded together
+constexpr int kMaxEncJobs = 16;              // tensors per launch
 
-// The table by value: freq and start of each byte (start = sum of the
-// frequencies of the smaller bytes).
-struct EncTable {
-    uint16_t freq[256];
-    uint16_t start[256];
+// One encoding job (a tensor) as the kernel sees it. Its workgroups are
+// first_block .. first_block + ceil(n_chunks / kEncWaves) - 1.
+struct EncJob {
+    const uint8_t *symbols;
+    uint8_t *scratch;
+    uint32_t *n_words;
+    const uint16_t *freq;    // device table (batched calls)
+    uint64_t n;
+    uint32_t chunk_symbols;
+    uint32_t n_chunks;
+    uint32_t first_block;
+    uint32_t pad;
 };
+
+struct EncJobs {
+    EncJob job[kMaxEncJobs];
+    uint32_t n_jobs;
+};
+
+// The host table of a single-tensor call, by value.
+struct EncFreq {
+    uint16_t f[256];
+};
+
+// Everything one encoding step needs about a symbol s with frequency f and
+// cumulative start c, in one 16-byte LDS entry:
+//   xmax_m1 = 2^20 f - 1: the state sheds a word when x > xmax_m1 (never
+//             for f = 4096, whose bound 2^32 is out of range);
+//   rlo, rhi = floor(2^44 / f) + 1 split at bit 32 (rhi <= 4096);
+//   g_c     = (4096 - f) | c << 16, bit 31 set when f = 0 (not codable).
+// The coding step x' = floor(x / f) 2^12 + (x mod f) + c is computed as
+// x + q (4096 - f) + c with q = floor(x / f).
+struct alignas(16) EncEntry {
+    uint32_t xmax_m1, rlo, rhi, g_c;
+};
+
+__device__ __forceinline__ EncEntry make_entry(uint32_t f, uint32_t c) {
+    EncEntry e;
+    if (f == 0) {
+        e.xmax_m1 = 0xFFFFFFFFu;
+        e.rlo = e.rhi = 0;
+        e.g_c = 0x80000000u;
+        return e;
+    }
+    const uint64_t r = ((1ull << 44) / f) + 1;
+    e.xmax_m1 = f >= kProbScale ? 0xFFFFFFFFu : (f << 20) - 1u;
+    e.rlo = (uint32_t)r;
+    e.rhi = (uint32_t)(r >> 32);
+    e.g_c = (kProbScale - f) | (c << 16);
+    return e;
+}
 
 __device__ __forceinline__ uint32_t lane_prefix_enc(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// floor(x / f) for x < 2^32, 1 <= f <= 4096, with recip = floor(2^44 / f) + 1:
-// x * recip / 2^44 exceeds x / f by less than 2^-12 <= 1/f, and x / f is at
-// most (f - 1) / f above its floor. The 96-bit product's bits 44.. are
-// (x * (recip >> 32) + ((x * (recip & 0xFFFFFFFF)) >> 32)) >> 12.
-__device__ __forceinline__ uint32_t div_by_freq(uint32_t x, uint64_t recip) {
-    const uint64_t lo = (uint64_t)x * (uint32_t)recip;
-    const uint64_t hi = (uint64_t)x * (uint32_t)(recip >> 32) + (lo >> 32);
+// floor(x / f) for x < 2^32, 1 <= f <= 4096, with r = floor(2^44 / f) + 1:
+// x r / 2^44 exceeds x / f by less than 2^-12 <= 1/f, and x / f is at most
+// (f - 1) / f above its floor. Bits 44.. of the 96-bit product x r are
+// (x rhi + ((x rlo) >> 32)) >> 12.
+__device__ __forceinline__ uint32_t div_by_freq(uint32_t x, uint32_t rlo, uint32_t rhi) {
+    const uint64_t lo = (uint64_t)x * rlo;
+    const uint64_t hi = (uint64_t)x * rhi + (lo >> 32);
     return (uint32_t)(hi >> 12);
 }
 
@@ -57,89 +103,143 @@ __host__ __device__ inline uint64_t scratch_stride(uint32_t chunk_symbols) {
     return ((uint64_t)kStateBytes + 2ull * chunk_symbols + 15u) & ~(uint64_t)15u;
 }
 
-__global__ __launch_bounds__(kEncThreads) void encode_chunks(
-    EncTable table, const uint8_t *__restrict__ symbols, uint64_t n, uint32_t chunk_symbols,
-    uint64_t n_chunks, uint8_t *__restrict__ scratch, uint32_t *__restrict__ n_words_out) {
-    __shared__ uint32_t F[256];       // f
-    __shared__ uint32_t S[256];       // start
-    __shared__ uint64_t R[256];       // floor(2^44 / f) + 1 (0 if f = 0)
-    __shared__ __attribute__((aligned(16))) uint8_t STAGE[kEncWaves][64 * kEncStageSteps];
-
-    for (uint32_t s = threadIdx.x; s < 256; s += kEncThreads) {
-        const uint32_t f = table.freq[s];
-        F[s] = f;
-        S[s] = table.start[s];
-        R[s] = f ? ((1ull << 44) / f) + 1 : 0;
+// The symbols of steps 16 g .. 16 g + 15 for this lane. kGuard: the group
+// may reach past the chunk's cn symbols (0 there); below the top group
+// every step is full.
+template <bool kGuard>
+__device__ __forceinline__ void load_group(const uint8_t *__restrict__ sym, uint32_t cn,
+                                           uint32_t g, uint32_t lane, uint32_t (&a)[kEncGroup]) {
+#pragma unroll
+    for (uint32_t k = 0; k < kEncGroup; ++k) {
+        const uint32_t i = 64u * (kEncGroup * g + k) + lane;
+        a[k] = (!kGuard || i < cn) ? sym[i] : 0u;
     }
+}
+
+// Waits until every vector memory operation of the wave has completed
+// (s_waitcnt vmcnt(0); the other counters left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Codes the steps of group g, last first. The entry of the next step's
+// symbol is read from LDS before the current step is coded, so the read
+// overlaps the arithmetic. kTop: the group holding the chunk's last step,
+// which may be partial (steps at or past `steps` skipped, lanes past cn
+// inactive); every other group is full.
+template <bool kTop>
+__device__ __forceinline__ void code_group(const EncEntry *__restrict__ T,
+                                           const uint32_t (&cur)[kEncGroup], uint32_t g,
+                                           uint32_t steps, uint32_t cn, uint32_t lane,
+                                           uint32_t &x, uint32_t &w, uint32_t &bad,
+                                           uint16_t *__restrict__ words) {
+    int k = kEncGroup - 1;
+    if (kTop)
+        while (k > 0 && kEncGroup * g + (uint32_t)k >= steps) --k;  // uniform
+    EncEntry e = T[cur[k]];
+#pragma unroll
+    for (int kk = kEncGroup - 1; kk >= 0; --kk) {
+        if (kTop && kk > k) continue;
+        const uint32_t t = kEncGroup * g + (uint32_t)kk;
+        const bool active = !kTop || 64u * t + lane < cn;
+        const EncEntry en = T[cur[kk > 0 ? kk - 1 : 0]];  // next step's entry
+        // renormalise first: a state above 2^20 f - 1 sheds its low word
+        const bool emit = active && x > e.xmax_m1;
+        const uint64_t mask = __ballot(emit);
+        const uint32_t cnt = (uint32_t)__popcll(mask);
+        // emission order within a step is descending lane: the higher
+        // emitting lanes' words come first (at higher indices)
+        if (emit) words[w - cnt + lane_prefix_enc(mask)] = (uint16_t)x;
+        const uint32_t xr = emit ? x >> 16 : x;
+        w -= cnt;
+        const uint32_t q = div_by_freq(xr, e.rlo, e.rhi);
+        const uint32_t xn = xr + q * (e.g_c & 0xFFFFu) + ((e.g_c >> 16) & 0xFFFu);
+        x = active ? xn : xr;
+        bad |= active ? e.g_c : 0u;
+        e = en;
+    }
+}
+
+// One wave encodes one chunk: cn symbols at sym, final states and words
+// into area. Returns the word count, or 0xFFFFFFFF if a symbol has
+// frequency 0. Steps run from last to first in groups of kEncGroup; the
+// symbols of the next group are loaded while the current group is coded.
+__device__ __forceinline__ uint32_t encode_chunk(const EncEntry *__restrict__ T,
+                                                 const uint8_t *__restrict__ sym, uint32_t cn,
+                                                 uint32_t chunk_symbols, uint8_t *__restrict__ area,
+                                                 uint32_t lane) {
+    uint16_t *words = reinterpret_cast<uint16_t *>(area + kStateBytes);
+    uint32_t x = kStateLow;
+    uint32_t w = chunk_symbols;  // next word goes to words[w - 1]
+    uint32_t bad = 0;
+    const uint32_t steps = (cn + 63) / 64;
+    uint32_t cur[kEncGroup], nxt[kEncGroup];
+    uint32_t g = (steps - 1) / kEncGroup;
+    load_group<true>(sym, cn, g, lane, cur);
+    wait_vmem();
+    if (g > 0) load_group<false>(sym, cn, g - 1, lane, nxt);
+    code_group<true>(T, cur, g, steps, cn, lane, x, w, bad, words);
+    while (g > 0) {
+        --g;
+        wait_vmem();  // this group's symbols (and earlier word stores)
+#pragma unroll
+        for (uint32_t k = 0; k < kEncGroup; ++k) cur[k] = nxt[k];
+        if (g > 0) load_group<false>(sym, cn, g - 1, lane, nxt);
+        code_group<false>(T, cur, g, steps, cn, lane, x, w, bad, words);
+    }
+    reinterpret_cast<uint32_t *>(area)[lane] = x;
+    const uint64_t any_bad = __ballot(bad >> 31);
+    return any_bad ? 0xFFFFFFFFu : chunk_symbols - w;
+}
+
+// Builds the 256 entries from a frequency table (read by threads 0..255;
+// cumulative starts by a Hillis-Steele scan). Returns whether the table
+// sums to 4096 with every f <= 4096.
+__device__ bool build_entries(EncEntry *T, uint32_t *P, const uint16_t *freq) {
+    const uint32_t s = threadIdx.x;
+    const uint32_t f = s < 256 ? freq[s] : 0u;
+    if (s < 256) P[s] = f;
+    __syncthreads();
+    for (uint32_t d = 1; d < 256; d <<= 1) {
+        const uint32_t v = (s < 256 && s >= d) ? P[s - d] : 0u;
+        __syncthreads();
+        if (s < 256) P[s] += v;
+        __syncthreads();
+    }
+    const uint32_t total = P[255];
+    if (s < 256) T[s] = make_entry(f > kProbScale ? 0u : f, P[s] - f);
+    const bool over = __syncthreads_or(s < 256 && f > kProbScale);
+    return total == kProbScale && !over;
+}
+
+template <bool kInlineTable>
+__global__ __launch_bounds__(kEncThreads) void encode_chunks(EncJobs jobs, EncFreq inline_freq) {
+    __shared__ EncEntry T[256];
+    __shared__ uint32_t P[256];
+    uint32_t j = 0;
+    while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
+    const EncJob &job = jobs.job[j];
+    const bool ok = build_entries(T, P, kInlineTable ? inline_freq.f : job.freq);
     __syncthreads();
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
-    const uint64_t k = (uint64_t)blockIdx.x * kEncWaves + wave;
-    if (k >= n_chunks) return;
-    const uint64_t e0 = k * chunk_symbols;
-    const uint32_t cn = (uint32_t)((n - e0 < chunk_symbols) ? n - e0 : chunk_symbols);
-    const uint8_t *sym = symbols + e0;
-    uint8_t *area = scratch + k * scratch_stride(chunk_symbols);
-    uint16_t *words = reinterpret_cast<uint16_t *>(area + kStateBytes);
-    uint8_t *stage = STAGE[wave];
-
-    uint32_t x = kStateLow;
-    uint32_t w = chunk_symbols;  // next word goes to words[w - 1]
-    bool bad = false;            // a symbol with frequency 0
-    const uint32_t steps = (cn + 63) / 64;
-    // stages of kEncStageSteps steps, last stage first
-    const uint32_t stages = (steps + kEncStageSteps - 1) / kEncStageSteps;
-    for (uint32_t g = stages; g-- > 0;) {
-        // lane l copies bytes [16 l, 16 l + 16) of the stage (inside the chunk)
-        const uint32_t b0 = g * 64 * kEncStageSteps;
-        const uint32_t b = b0 + 16u * lane;
-        if (b + 16 <= cn) {
-            *reinterpret_cast<uint4 *>(stage + 16u * lane) =
-                *reinterpret_cast<const uint4 *>(sym + b);
-        } else {
-            for (uint32_t q = 0; q < 16; ++q)
-                stage[16u * lane + q] = (b + q < cn) ? sym[b + q] : 0;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint32_t t1 = (g + 1) * kEncStageSteps < steps ? (g + 1) * kEncStageSteps : steps;
-        for (uint32_t t = t1; t-- > g * kEncStageSteps;) {
-            const uint32_t i = 64u * t + lane;
-            const bool active = i < cn;
-            const uint32_t s = stage[i - b0];
-            const uint32_t f = F[s];
-            // renormalise first: a state at or above 2^20 f sheds its low word
-            // (f = 4096 never does: the bound is 2^32)
-            const bool emit = active && f < kProbScale && x >= (f << 20);
-            const uint64_t mask = __ballot(emit);
-            const uint32_t cnt = (uint32_t)__popcll(mask);
-            if (emit) {
-                // emission order within a step is descending lane: the
-                // higher emitting lanes' words come first (at higher indices)
-                words[w - cnt + lane_prefix_enc(mask)] = (uint16_t)x;
-                x >>= 16;
-            }
-            w -= cnt;
-            if (active) {
-                if (f == 0) {
-                    bad = true;
-                } else {
-                    const uint32_t q = div_by_freq(x, R[s]);
-                    x = (q << kProbBits) + (x - q * f) + S[s];
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();  // the stage is rewritten next
+    const uint64_t k = (uint64_t)(blockIdx.x - job.first_block) * kEncWaves + wave;
+    if (k >= job.n_chunks) return;
+    if (!ok) {
+        if (lane == 0) job.n_words[k] = 0xFFFFFFFFu;
+        return;
     }
-    reinterpret_cast<uint32_t *>(area)[lane] = x;
-    const uint64_t any_bad = __ballot(bad);
-    if (lane == 0) n_words_out[k] = any_bad ? 0xFFFFFFFFu : chunk_symbols - w;
+    const uint64_t e0 = k * job.chunk_symbols;
+    const uint32_t cn =
+        (uint32_t)((job.n - e0 < job.chunk_symbols) ? job.n - e0 : job.chunk_symbols);
+    const uint32_t nw = encode_chunk(T, job.symbols + e0, cn, job.chunk_symbols,
+                                     job.scratch + k * scratch_stride(job.chunk_symbols), lane);
+    if (lane == 0) job.n_words[k] = nw;
 }
 
 // One workgroup per chunk: region = 64 states, the words (the last n_words
-// of the chunk's word area), zeros up to the next 16-byte boundary.
+// of the chunk's word area), zeros up to the next 16-byte boundary. The
+// region is written one dword per thread and pass; when the words start at
+// an odd word index, each dword is funnelled from two source dwords.
 __global__ __launch_bounds__(256) void pack_chunks(const uint8_t *__restrict__ scratch,
                                                    uint32_t chunk_symbols,
                                                    const uint32_t *__restrict__ n_words,
@@ -149,33 +249,125 @@ __global__ __launch_bounds__(256) void pack_chunks(const uint8_t *__restrict__ s
     const uint32_t nw = n_words[k];
     if (nw > chunk_symbols) return;  // a chunk the encoder rejected (frequency-0 symbol)
     const uint8_t *area = scratch + k * scratch_stride(chunk_symbols);
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(area + kStateBytes) + (chunk_symbols - nw);
-    uint8_t *dst = blob + offsets[k];
-    if (threadIdx.x < 64)
-        reinterpret_cast<uint32_t *>(dst)[threadIdx.x] = reinterpret_cast<const uint32_t *>(area)[threadIdx.x];
-    uint16_t *dw = reinterpret_cast<uint16_t *>(dst + kStateBytes);
-    const uint32_t padded = (uint32_t)(((kStateBytes + 2ull * nw + 15u) & ~15ull) - kStateBytes) / 2;
-    for (uint32_t i = threadIdx.x; i < padded; i += blockDim.x) dw[i] = (i < nw) ? src[i] : 0;
-}
-
-__global__ __launch_bounds__(256) void count_bytes(const uint8_t *__restrict__ symbols, uint64_t n,
-                                                   unsigned long long *__restrict__ counts) {
-    __shared__ uint32_t H[256];
-    H[threadIdx.x] = 0;
-    __syncthreads();
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * 16;
-    for (uint64_t b = ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; b < n; b += stride) {
-        if (b + 16 <= n) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(symbols + b);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-            for (int q = 0; q < 4; ++q)
-                for (int c = 0; c < 4; ++c) atomicAdd(&H[(u[q] >> (8 * c)) & 0xFFu], 1u);
-        } else {
-            for (uint64_t q = b; q < n; ++q) atomicAdd(&H[symbols[q]], 1u);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(blob + offsets[k]);
+    if (threadIdx.x < 64) dst[threadIdx.x] = reinterpret_cast<const uint32_t *>(area)[threadIdx.x];
+    const uint32_t *A = reinterpret_cast<const uint32_t *>(area + kStateBytes);  // word pairs
+    uint32_t *D = dst + kStateBytes / 4;
+    const uint32_t sb = chunk_symbols - nw;  // first word
+    const uint32_t n_dw = (uint32_t)((((uint64_t)kStateBytes + 2ull * nw + 15u) & ~15ull) -
+                                     kStateBytes) / 4;  // dwords after the states
+    const uint32_t full = nw / 2;                       // dwords holding two words
+    if ((sb & 1u) == 0) {
+        const uint32_t a0 = sb / 2;
+        for (uint32_t d = threadIdx.x; d < n_dw; d += 256) {
+            uint32_t v = 0;
+            if (d < full) v = A[a0 + d];
+            else if (d == full && (nw & 1u)) v = A[a0 + d] & 0xFFFFu;
+            D[d] = v;
+        }
+    } else {
+        // word sb + 2d sits in the high half of dword (sb - 1) / 2 + d
+        const uint32_t a0 = (sb - 1) / 2;
+        for (uint32_t d = threadIdx.x; d < n_dw; d += 256) {
+            uint32_t v = 0;
+            if (d < full) {
+                v = __builtin_amdgcn_alignbit(A[a0 + d + 1], A[a0 + d], 16);
+            } else if (d == full && (nw & 1u)) {
+                v = A[a0 + d] >> 16;
+            }
+            D[d] = v;
         }
     }
+}
+
+// Region offsets: offsets[k] = base + the region bytes of chunks 0..k-1
+// (256 + 2 n_words rounded up to 16; a chunk marked rejected, n_words above
+// any chunk size, takes none), *end = base + all of them. One workgroup:
+// each thread sums a run of consecutive chunks, a Hillis-Steele scan over
+// the 1024 run sums gives each run its start, the run is then written out.
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ uint64_t region_size(uint32_t nw) {
+    return nw > (uint32_t)kMaxChunkSymbols ? 0 : (((uint64_t)kStateBytes + 2ull * nw + 15u) & ~15ull);
+}
+
+__global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *__restrict__ n_words,
+                                                               uint64_t n_chunks, uint64_t base,
+                                                               uint64_t *__restrict__ offsets,
+                                                               uint64_t *__restrict__ end) {
+    __shared__ uint64_t part[kScanThreads];
+    const uint32_t t = threadIdx.x;
+    const uint64_t per = (n_chunks + kScanThreads - 1) / kScanThreads;
+    const uint64_t lo = t * per < n_chunks ? t * per : n_chunks;
+    const uint64_t hi = lo + per < n_chunks ? lo + per : n_chunks;
+    uint64_t sum = 0;
+    for (uint64_t i = lo; i < hi; ++i) sum += region_size(n_words[i]);
+    part[t] = sum;
     __syncthreads();
-    if (H[threadIdx.x]) atomicAdd(&counts[threadIdx.x], (unsigned long long)H[threadIdx.x]);
+    for (uint32_t d = 1; d < kScanThreads; d <<= 1) {
+        const uint64_t v = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint64_t run = base + part[t] - sum;  // exclusive prefix of this run
+    for (uint64_t i = lo; i < hi; ++i) {
+        offsets[i] = run;
+        run += region_size(n_words[i]);
+    }
+    if (t == kScanThreads - 1) *end = base + part[t];
+}
+
+// Byte histogram. Each workgroup keeps one LDS table of 256 bins x 64 lane
+// columns (64 KB): lane j adds into column j, so the 64 atomic adds of one
+// wave instruction always fall into 64 different banks, however skewed the
+// bytes are (a shared 256-bin table serialises the many lanes that hold the
+// same common byte). The waves of the workgroup share the columns through the
+// LDS atomics. Each lane reads 64 bytes per round as four 16-byte loads.
+constexpr int kCountThreads = 512;
+constexpr int kCountBytesPerLane = 64;
+
+__global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__restrict__ symbols,
+                                                             uint64_t n,
+                                                             unsigned long long *__restrict__ counts) {
+    __shared__ uint32_t H[256 * 64];
+    const uint32_t lane_off = (threadIdx.x & 63u) * 4u;  // byte offset of the lane's column
+    for (uint32_t i = threadIdx.x; i < 256u * 64u / 4u; i += kCountThreads)
+        reinterpret_cast<uint4 *>(H)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    char *const Hb = reinterpret_cast<char *>(H);
+    auto add_byte = [&](uint32_t b) {  // b < 256
+        __hip_atomic_fetch_add(reinterpret_cast<uint32_t *>(Hb + ((b << 8) | lane_off)), 1u,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto add4 = [&](uint32_t u) {
+        for (int c = 0; c < 4; ++c) add_byte((u >> (8 * c)) & 0xFFu);
+    };
+    const uint64_t n_full = n / kCountBytesPerLane;  // whole 64-byte lane rounds
+    const uint64_t stride = (uint64_t)gridDim.x * kCountThreads;
+    for (uint64_t r = (uint64_t)blockIdx.x * kCountThreads + threadIdx.x; r < n_full; r += stride) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(symbols + r * kCountBytesPerLane);
+        uint4 v[4];
+        for (int q = 0; q < 4; ++q) v[q] = src[q];
+        for (int q = 0; q < 4; ++q) {
+            add4(v[q].x);
+            add4(v[q].y);
+            add4(v[q].z);
+            add4(v[q].w);
+        }
+    }
+    // the last n % 64 bytes, one per thread of workgroup 0
+    if (blockIdx.x == 0) {
+        const uint64_t tail = n_full * kCountBytesPerLane + threadIdx.x;
+        if (tail < n) add_byte(symbols[tail]);
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        uint64_t sum = 0;
+        for (uint32_t j = 0; j < 64; ++j)  // column order rotated by bin: no bank conflicts
+            sum += H[threadIdx.x * 64u + ((j + threadIdx.x) & 63u)];
+        if (sum) atomicAdd(&counts[threadIdx.x], (unsigned long long)sum);
+    }
 }
 
 }  // namespace
@@ -189,9 +381,16 @@ entq_status entq_count_symbols_device(const uint8_t *d_symbols, uint64_t n, uint
     if (n && (uintptr_t)d_symbols % 16) return ENTQ_EALIGN;
     if ((uintptr_t)d_counts % 8) return ENTQ_EALIGN;
     if (n == 0) return ENTQ_OK;
-    uint64_t blocks = (n + 256 * 16 * 64 - 1) / (256 * 16 * 64);  // >= 64 bytes-per-thread rounds
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(entq::count_bytes, dim3((unsigned)blocks), dim3(256), 0,
+    // Two workgroups per CU on 256 CUs, fewer for small inputs (at least 16
+    // lane rounds per thread). A lane column counts at most n / (64 blocks)
+    // bytes; more blocks keep that below 2^32.
+    const uint64_t rounds = n / entq::kCountBytesPerLane;
+    uint64_t blocks = (rounds + 16ull * entq::kCountThreads - 1) / (16ull * entq::kCountThreads);
+    if (blocks > 512) blocks = 512;
+    const uint64_t min_blocks = (n >> 37) + 1;
+    if (blocks < min_blocks) blocks = min_blocks;
+    if (blocks > 0x7FFFFFFF) return ENTQ_EINVAL;
+    hipLaunchKernelGGL(entq::count_bytes, dim3((unsigned)blocks), dim3(entq::kCountThreads), 0,
                        (hipStream_t)stream, d_symbols, n,
                        reinterpret_cast<unsigned long long *>(d_counts));
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
@@ -215,26 +414,70 @@ entq_status entq_encode_device(const uint8_t *d_symbols, uint64_t n, uint32_t ch
     if (chunk_symbols == 0 || chunk_symbols % entq::kLanes ||
         chunk_symbols > entq::kMaxChunkSymbols)
         return ENTQ_EINVAL;
+    uint32_t total = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (freq[s] > entq::kProbScale) return ENTQ_EBADTABLE;
+        total += freq[s];
+    }
+    if (total != entq::kProbScale) return ENTQ_EBADTABLE;
     if (n == 0) return ENTQ_OK;
     if ((uintptr_t)d_symbols % 16 || (uintptr_t)d_scratch % 16 || (uintptr_t)d_n_words % 4)
         return ENTQ_EALIGN;
     if (scratch_bytes < entq_encode_device_scratch_bytes(n, chunk_symbols)) return ENTQ_EWORKSPACE;
-    entq::EncTable table;
-    uint32_t total = 0;
-    for (int s = 0; s < 256; ++s) {
-        table.freq[s] = freq[s];
-        table.start[s] = (uint16_t)total;
-        total += freq[s];
-        if (freq[s] > entq::kProbScale) return ENTQ_EBADTABLE;
-    }
-    if (total != entq::kProbScale) return ENTQ_EBADTABLE;
     const uint64_t n_chunks = (n + chunk_symbols - 1) / chunk_symbols;
     const uint64_t blocks = (n_chunks + entq::kEncWaves - 1) / entq::kEncWaves;
     if (blocks > 0x7FFFFFFF) return ENTQ_EINVAL;
-    hipLaunchKernelGGL(entq::encode_chunks, dim3((unsigned)blocks), dim3(entq::kEncThreads), 0,
-                       (hipStream_t)stream, table, d_symbols, n, chunk_symbols, n_chunks,
-                       static_cast<uint8_t *>(d_scratch), d_n_words);
+    entq::EncJobs jobs = {};
+    jobs.n_jobs = 1;
+    jobs.job[0] = {d_symbols, static_cast<uint8_t *>(d_scratch), d_n_words, nullptr, n,
+                   chunk_symbols, (uint32_t)n_chunks, 0, 0};
+    entq::EncFreq table;
+    for (int s = 0; s < 256; ++s) table.f[s] = freq[s];
+    hipLaunchKernelGGL(entq::encode_chunks<true>, dim3((unsigned)blocks),
+                       dim3(entq::kEncThreads), 0, (hipStream_t)stream, jobs, table);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_encode_device_batch(const entq_encode_job *jobs, int n_jobs, void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_encode_job &jb = jobs[j];
+        const uint32_t C = jb.chunk_symbols;
+        if (C == 0 || C % entq::kLanes || C > entq::kMaxChunkSymbols) return ENTQ_EINVAL;
+        if (jb.n_symbols == 0) continue;
+        if (!jb.d_symbols || !jb.d_freq || !jb.d_scratch || !jb.d_n_words) return ENTQ_EINVAL;
+        if ((uintptr_t)jb.d_symbols % 16 || (uintptr_t)jb.d_scratch % 16 ||
+            (uintptr_t)jb.d_n_words % 4 || (uintptr_t)jb.d_freq % 2)
+            return ENTQ_EALIGN;
+        if (jb.scratch_bytes < entq_encode_device_scratch_bytes(jb.n_symbols, C))
+            return ENTQ_EWORKSPACE;
+        if ((jb.n_symbols + C - 1) / C > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    }
+    // up to kMaxEncJobs non-empty jobs per launch, their workgroups back to back
+    entq::EncJobs batch = {};
+    uint64_t blocks = 0;
+    const entq::EncFreq no_table = {};
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::encode_chunks<false>, dim3((unsigned)blocks),
+                           dim3(entq::kEncThreads), 0, (hipStream_t)stream, batch, no_table);
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_encode_job &jb = jobs[j];
+        if (jb.n_symbols == 0) continue;
+        const uint64_t k = (jb.n_symbols + jb.chunk_symbols - 1) / jb.chunk_symbols;
+        const uint64_t b = (k + entq::kEncWaves - 1) / entq::kEncWaves;
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + b > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {jb.d_symbols, static_cast<uint8_t *>(jb.d_scratch),
+                                     jb.d_n_words, jb.d_freq, jb.n_symbols, jb.chunk_symbols,
+                                     (uint32_t)k, (uint32_t)blocks, 0};
+        blocks += b;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
 }
 
 entq_status entq_pack_device(const void *d_scratch, uint64_t n, uint32_t chunk_symbols,
@@ -251,6 +494,19 @@ entq_status entq_pack_device(const void *d_scratch, uint64_t n, uint32_t chunk_s
     hipLaunchKernelGGL(entq::pack_chunks, dim3((unsigned)n_chunks), dim3(256), 0,
                        (hipStream_t)stream, static_cast<const uint8_t *>(d_scratch),
                        chunk_symbols, d_n_words, d_byte_offsets, static_cast<uint8_t *>(d_blob));
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_region_offsets_device(const uint32_t *d_n_words, uint64_t n_chunks,
+                                      uint64_t base_offset, uint64_t *d_byte_offsets,
+                                      uint64_t *d_end_offset, void *stream) {
+    if (!d_end_offset || (n_chunks && (!d_n_words || !d_byte_offsets))) return ENTQ_EINVAL;
+    if ((uintptr_t)d_n_words % 4 || (uintptr_t)d_byte_offsets % 8 || (uintptr_t)d_end_offset % 8)
+        return ENTQ_EALIGN;
+    if (base_offset % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
+    hipLaunchKernelGGL(entq::region_offsets, dim3(1), dim3(entq::kScanThreads), 0,
+                       (hipStream_t)stream, d_n_words, n_chunks, base_offset, d_byte_offsets,
+                       d_end_offset);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
 }
 

@@ -215,9 +215,12 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * steps, with the frequency table and the region offsets settled on the
  * host between them:
  *   1. entq_count_symbols_device -> counts (copy to host) -> entq_build_freq
- *   2. entq_encode_device -> per-chunk word counts (copy to host); region k
- *      takes entq_region_bytes(n_words[k]) bytes at a 16-byte-aligned offset
+ *   2. entq_encode_device -> per-chunk word counts; region k takes
+ *      entq_region_bytes(n_words[k]) bytes at a 16-byte-aligned offset, laid
+ *      out on the device by entq_region_offsets_device (or on the host)
  *   3. entq_pack_device -> the regions in the caller's blob
+ * Only the counts of step 1 need to reach the host before step 2; the word
+ * counts and offsets are read back once, after step 3, for the chunk index.
  * All buffers are caller-owned device memory; all work is enqueued on
  * `stream` and nothing synchronises. */
 
@@ -247,6 +250,25 @@ entq_status entq_encode_device(const uint8_t *d_symbols, uint64_t n, uint32_t ch
                                const uint16_t freq[256], void *d_scratch, uint64_t scratch_bytes,
                                uint32_t *d_n_words, void *stream);
 
+/* One tensor of a batched device encode (all pointers device memory). */
+typedef struct {
+    const uint8_t *d_symbols;  /* n_symbols codes, 16-byte aligned */
+    uint64_t n_symbols;
+    uint32_t chunk_symbols;    /* multiple of 64, at most 2^20 */
+    uint32_t reserved;
+    const uint16_t *d_freq;    /* the tensor's table [256], sum 4096 */
+    void *d_scratch;           /* entq_encode_device_scratch_bytes(n_symbols, chunk_symbols) */
+    uint64_t scratch_bytes;
+    uint32_t *d_n_words;       /* [ceil(n_symbols / chunk_symbols)] */
+} entq_encode_job;
+
+/* entq_encode_device for several tensors in as few launches as possible
+ * (one per 16 tensors), so that small tensors' chunks run beside the large
+ * ones'. The tables are read on the device: a table that does not sum to
+ * 4096 (or has an entry above 4096) marks every chunk of its tensor with
+ * 0xFFFFFFFF instead of an error code. Empty tensors are skipped. */
+entq_status entq_encode_device_batch(const entq_encode_job *jobs, int n_jobs, void *stream);
+
 /* Writes the regions of an encoded tensor into d_blob (device, 16-byte
  * aligned): region k (64 states, the chunk's words in decoding order, zero
  * padding) at byte d_byte_offsets[k] (device u64, multiples of 16, regions
@@ -254,6 +276,17 @@ entq_status entq_encode_device(const uint8_t *d_symbols, uint64_t n, uint32_t ch
 entq_status entq_pack_device(const void *d_scratch, uint64_t n, uint32_t chunk_symbols,
                              const uint32_t *d_n_words, const uint64_t *d_byte_offsets,
                              void *d_blob, void *stream);
+
+/* Lays out consecutive regions: d_byte_offsets[k] = base_offset + the sum of
+ * entq_region_bytes(d_n_words[i]) over i < k, and *d_end_offset = base_offset
+ * + the sum over all n_chunks (device u32 / u64 / u64). A chunk marked
+ * rejected (n_words above 2^20, as entq_encode_device's 0xFFFFFFFF) takes 0
+ * bytes, so later regions stay inside the blob's bound. The word counts of
+ * several tensors can be scanned in one call when their chunks are
+ * consecutive in d_n_words. base_offset is a multiple of 16. */
+entq_status entq_region_offsets_device(const uint32_t *d_n_words, uint64_t n_chunks,
+                                      uint64_t base_offset, uint64_t *d_byte_offsets,
+                                      uint64_t *d_end_offset, void *stream);
 
 #ifdef __cplusplus
 }

@@ -135,3 +135,49 @@ def test_llama2_70b_layer_matches_host_encoder(E):
     assert np.array_equal(dev.blob.cpu().numpy(), host.blob)
     assert np.array_equal(dev.chunks, host.chunks)
     assert np.array_equal(dev.freq, host.freq)
+
+
+def test_region_offsets_device(E):
+    import torch
+    rng = np.random.default_rng(9)
+    for k, base in ((1, 0), (1023, 16), (1024, 0), (5001, 4096), (40000, 32)):
+        nw = rng.integers(0, 65537, k).astype(np.uint32)
+        if k > 3:
+            nw[3] = 0xFFFFFFFF  # a rejected chunk takes no bytes
+        size = np.where(nw > (1 << 20), 0, (256 + 2 * nw.astype(np.uint64) + 15) // 16 * 16)
+        want = base + np.concatenate([[0], np.cumsum(size)[:-1]]).astype(np.uint64)
+        nw_d = torch.from_numpy(nw.view(np.int32)).cuda()
+        offs = torch.empty(k, dtype=torch.int64, device="cuda")
+        end = torch.zeros(1, dtype=torch.int64, device="cuda")
+        E.region_offsets_device(nw_d, offs, end, base)
+        torch.cuda.synchronize()
+        assert np.array_equal(offs.cpu().numpy().view(np.uint64), want), k
+        assert int(end.cpu()[0]) == base + int(size.sum()), k
+
+
+def test_batched_encode_over_sixteen_tensors_matches_oracle(E):
+    # 21 tensors: the batched call splits them over two launches
+    specs = [synth.random_int8_tensor(3 + t, 64 * (1 + t % 5), 0.8 + 0.2 * t, 100 + t,
+                                      (64, 4096, 256)[t % 3]) for t in range(21)]
+    _say("21 tensors through the batched encode")
+    _check_against_oracle(E, specs)
+
+
+def test_batched_encode_marks_invalid_device_table(E):
+    import torch
+    rng = np.random.default_rng(3)
+    sym = rng.integers(0, 4, 64 * 300, dtype=np.uint8)
+    good = np.zeros(256, np.uint16)
+    good[:4] = 1024
+    bad = good.copy()
+    bad[0] = 1023                           # sums to 4095
+    d = _dev(sym)
+    scr = [torch.empty(int(E.lib().entq_encode_device_scratch_bytes(sym.size, 4096)),
+                       dtype=torch.uint8, device="cuda") for _ in range(2)]
+    nws = [torch.zeros(5, dtype=torch.int32, device="cuda") for _ in range(2)]
+    fd = torch.from_numpy(np.stack([good, bad]).view(np.int16)).cuda()
+    E.encode_device_batch([(d, 4096, fd[0], scr[0], nws[0]), (d, 4096, fd[1], scr[1], nws[1])])
+    torch.cuda.synchronize()
+    ok = nws[0].cpu().numpy().view(np.uint32)
+    assert (ok != 0xFFFFFFFF).all() and (ok > 0).all()
+    assert (nws[1].cpu().numpy().view(np.uint32) == 0xFFFFFFFF).all()
