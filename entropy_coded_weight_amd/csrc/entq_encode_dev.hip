@@ -25,9 +25,9 @@
 namespace entq {
 namespace {
 
-constexpr int kEncWaves = 8;                 // chunks per workgroup
+constexpr int kEncWaves = 4;                 // chunks per workgroup
 constexpr int kEncThreads = kEncWaves * 64;
-constexpr uint32_t kEncGroup = 16;           // steps whose symbols are loaded together
+constexpr uint32_t kEncGroup = 8;            // steps whose symbols are loaded together
 constexpr int kMaxEncJobs = 16;              // tensors per launch
 
 // One encoding job (a tensor) as the kernel sees it. Its workgroups are
@@ -55,30 +55,31 @@ struct EncFreq {
 };
 
 // Everything one encoding step needs about a symbol s with frequency f and
-// cumulative start c, in one 16-byte LDS entry:
+// cumulative start c, in one 32-byte LDS entry:
 //   xmax_m1 = 2^20 f - 1: the state sheds a word when x > xmax_m1 (never
 //             for f = 4096, whose bound 2^32 is out of range);
-//   rlo, rhi = floor(2^44 / f) + 1 split at bit 32 (rhi <= 4096);
-//   g_c     = (4096 - f) | c << 16, bit 31 set when f = 0 (not codable).
-// The coding step x' = floor(x / f) 2^12 + (x mod f) + c is computed as
-// x + q (4096 - f) + c with q = floor(x / f).
-struct alignas(16) EncEntry {
-    uint32_t xmax_m1, rlo, rhi, g_c;
+//   rcp     = 1/f rounded to the nearest fp32;
+//   nf, f, g = -f, f, 4096 - f;
+//   c       = c, with bit 31 set when f = 0 (such a symbol cannot be coded).
+struct alignas(32) EncEntry {
+    uint32_t xmax_m1;
+    float rcp;
+    int32_t nf;
+    uint32_t f;
+    uint32_t g;
+    uint32_t c;
+    uint32_t pad[2];
 };
 
 __device__ __forceinline__ EncEntry make_entry(uint32_t f, uint32_t c) {
     EncEntry e;
-    if (f == 0) {
-        e.xmax_m1 = 0xFFFFFFFFu;
-        e.rlo = e.rhi = 0;
-        e.g_c = 0x80000000u;
-        return e;
-    }
-    const uint64_t r = ((1ull << 44) / f) + 1;
-    e.xmax_m1 = f >= kProbScale ? 0xFFFFFFFFu : (f << 20) - 1u;
-    e.rlo = (uint32_t)r;
-    e.rhi = (uint32_t)(r >> 32);
-    e.g_c = (kProbScale - f) | (c << 16);
+    e.xmax_m1 = (f == 0 || f >= kProbScale) ? 0xFFFFFFFFu : (f << 20) - 1u;
+    e.rcp = f ? (float)(1.0 / (double)f) : 0.0f;
+    e.nf = -(int32_t)f;
+    e.f = f;
+    e.g = kProbScale - f;
+    e.c = f ? c : 0x80000000u;
+    e.pad[0] = e.pad[1] = 0;
     return e;
 }
 
@@ -87,14 +88,22 @@ __device__ __forceinline__ uint32_t lane_prefix_enc(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// floor(x / f) for x < 2^32, 1 <= f <= 4096, with r = floor(2^44 / f) + 1:
-// x r / 2^44 exceeds x / f by less than 2^-12 <= 1/f, and x / f is at most
-// (f - 1) / f above its floor. Bits 44.. of the 96-bit product x r are
-// (x rhi + ((x rlo) >> 32)) >> 12.
-__device__ __forceinline__ uint32_t div_by_freq(uint32_t x, uint32_t rlo, uint32_t rhi) {
-    const uint64_t lo = (uint64_t)x * rlo;
-    const uint64_t hi = (uint64_t)x * rhi + (lo >> 32);
-    return (uint32_t)(hi >> 12);
+// The coding step x' = floor(x / f) 2^12 + (x mod f) + c = x + q (4096 - f)
+// + c, q = floor(x / f), for a renormalised state (x < 2^20 f, so
+// y = x / f < 2^20), with full-rate fp32 and 24-bit integer operations only.
+// The estimate z = fl(fl(x) * fl(1/f) - 1/4) is within 2^-23 y + 2^-5 < 0.16
+// of y - 1/4: each of the three roundings is relative 2^-24 or, for the
+// last, half an ulp below 2^20. With y = q + r/f, 0 <= r <= f - 1, z lies in
+// (q - 1, q + 1) and truncates to q - 1 or q (to 0 for q = 0); the remainder
+// x - q_est f, in [0, 2f), tells which, and a short estimate adds one more
+// 4096 - f. For f = 4096 (a single-symbol tensor) the step keeps x whatever
+// q_est is, as 4096 - f = 0 and c = 0.
+__device__ __forceinline__ uint32_t code_step(uint32_t x, const EncEntry &e) {
+    const float z = __builtin_fmaf((float)x, e.rcp, -0.25f);
+    const uint32_t q = (uint32_t)(int32_t)z;                     // z > -1
+    const uint32_t r = x + (uint32_t)__mul24((int32_t)q, e.nf);  // x - q f, exact mod 2^32
+    const uint32_t fix = r >= e.f ? e.g : 0u;
+    return __umul24(q, e.g) + x + e.c + fix;
 }
 
 // Scratch layout of one tensor: per chunk k, 64 u32 final states at
@@ -147,13 +156,13 @@ __device__ __forceinline__ void code_group(const EncEntry *__restrict__ T,
         const uint32_t cnt = (uint32_t)__popcll(mask);
         // emission order within a step is descending lane: the higher
         // emitting lanes' words come first (at higher indices)
-        if (emit) words[w - cnt + lane_prefix_enc(mask)] = (uint16_t)x;
-        const uint32_t xr = emit ? x >> 16 : x;
         w -= cnt;
-        const uint32_t q = div_by_freq(xr, e.rlo, e.rhi);
-        const uint32_t xn = xr + q * (e.g_c & 0xFFFFu) + ((e.g_c >> 16) & 0xFFFu);
+        uint16_t *const wb = words + w;  // uniform base: the store takes a lane offset only
+        if (emit) wb[lane_prefix_enc(mask)] = (uint16_t)x;
+        const uint32_t xr = emit ? x >> 16 : x;
+        const uint32_t xn = code_step(xr, e);
         x = active ? xn : xr;
-        bad |= active ? e.g_c : 0u;
+        bad |= active ? e.c : 0u;
         e = en;
     }
 }
@@ -171,19 +180,23 @@ __device__ __forceinline__ uint32_t encode_chunk(const EncEntry *__restrict__ T,
     uint32_t w = chunk_symbols;  // next word goes to words[w - 1]
     uint32_t bad = 0;
     const uint32_t steps = (cn + 63) / 64;
-    uint32_t cur[kEncGroup], nxt[kEncGroup];
+    // two symbol buffers used in turn: one being coded, one being loaded
+    uint32_t sa[kEncGroup], sb[kEncGroup];
     uint32_t g = (steps - 1) / kEncGroup;
-    load_group<true>(sym, cn, g, lane, cur);
+    load_group<true>(sym, cn, g, lane, sa);
     wait_vmem();
-    if (g > 0) load_group<false>(sym, cn, g - 1, lane, nxt);
-    code_group<true>(T, cur, g, steps, cn, lane, x, w, bad, words);
+    if (g > 0) load_group<false>(sym, cn, g - 1, lane, sb);
+    code_group<true>(T, sa, g, steps, cn, lane, x, w, bad, words);
     while (g > 0) {
         --g;
         wait_vmem();  // this group's symbols (and earlier word stores)
-#pragma unroll
-        for (uint32_t k = 0; k < kEncGroup; ++k) cur[k] = nxt[k];
-        if (g > 0) load_group<false>(sym, cn, g - 1, lane, nxt);
-        code_group<false>(T, cur, g, steps, cn, lane, x, w, bad, words);
+        if (g > 0) load_group<false>(sym, cn, g - 1, lane, sa);
+        code_group<false>(T, sb, g, steps, cn, lane, x, w, bad, words);
+        if (g == 0) break;
+        --g;
+        wait_vmem();
+        if (g > 0) load_group<false>(sym, cn, g - 1, lane, sb);
+        code_group<false>(T, sa, g, steps, cn, lane, x, w, bad, words);
     }
     reinterpret_cast<uint32_t *>(area)[lane] = x;
     const uint64_t any_bad = __ballot(bad >> 31);
