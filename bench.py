@@ -53,14 +53,18 @@ def parse():
     ap.add_argument("--cpu-sample-tensors", type=int, default=5,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline")
     ap.add_argument("--threads", type=int, default=0)
-    ap.add_argument("--path", choices=("decode", "encode", "overlap"), default="decode",
+    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused"), default="decode",
                     help="decode: the layer-by-layer decode (the headline line); encode: the "
                          "on-device encoder over 70B-shaped layers; overlap: decode of layer "
-                         "l+1 overlapped with layer l's projection GEMMs")
-    ap.add_argument("--tokens", type=str, default="2048,256,16",
-                    help="overlap: activation rows per GEMM; the first value is the line's")
+                         "l+1 overlapped with layer l's projection GEMMs; fused: decode and "
+                         "product with m activation rows in one kernel vs decode + GEMM")
+    ap.add_argument("--tokens", type=str, default="",
+                    help="activation rows per GEMM, comma-separated; the first value is the "
+                         "line's (overlap default 2048,256,16; fused default 16,4,1)")
     ap.add_argument("--encode-layers", type=int, default=4,
                     help="resident layers of source codes the encode steps cycle through")
+    ap.add_argument("--row-chunk-max", type=int, default=32768,
+                    help="fused: a chunk holds as many whole rows as fit in this many symbols")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain fp32 negate (read N MiB, write N MiB) before timing, as a "
                          "known-size reference for hardware byte counters")
@@ -77,6 +81,8 @@ def main():
         return bench_encode(args)
     if args.path == "overlap":
         return bench_overlap(args)
+    if args.path == "fused":
+        return bench_fused(args)
     import torch
 
     import entropy_coded_weight_amd as E
@@ -449,7 +455,7 @@ def bench_overlap(args):
              for t in range(len(tens))]
     gen = torch.Generator().manual_seed(0)
     results = []
-    for T in [int(v) for v in args.tokens.split(",") if v]:
+    for T in [int(v) for v in (args.tokens or "2048,256,16").split(",") if v]:
         X = (torch.randn(T, 8192, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         H = (torch.randn(T, 28672, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         Y = {n: torch.empty(T, r, dtype=torch.bfloat16, device=dev) for n, r, c, o in views}
@@ -525,6 +531,154 @@ def bench_overlap(args):
             "frac": r0["gemm_tflops"] / 2500.0,
             "traffic": None,
             "kernel": "the library bf16 GEMMs (torch.mm) of the GEMM-only schedule",
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+FUSED_METRIC = ("tokens/s through the 80-layer 70B-shaped projection stack with each layer's "
+                "weights decoded inside the GEMM (entq_decode_gemm)")
+
+
+def compressed_layers_row_aligned(args, E, synth, dev, torch):
+    """The 80 layers encoded on the device with chunks of whole rows (8 rows
+    of 8192 columns, 2 rows of 28672), as the fused kernel needs."""
+    nthreads = args.threads or synth.default_threads()
+    t0 = time.time()
+    layers, out_elems, tens = [], 0, None
+    for layer in range(args.layers):
+        specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
+        for sp in specs:
+            sp["chunk_symbols"] = sp["cols"] * max(1, args.row_chunk_max // sp["cols"])
+        ds = [dict(sp, symbols=torch.from_numpy(
+            np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()).to(dev)) for sp in specs]
+        b = E.encode_batch_device(ds)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
+        sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)
+        layers.append((p, b.blob.clone(), sc))
+        out_elems, tens = b.out_elems, b.tensors
+        del ds, b
+        if layer % 10 == 0 or layer == args.layers - 1:
+            log(f"layer {layer} encoded on the device, row-aligned chunks ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return layers, out_elems, tens
+
+
+def bench_fused(args):
+    """One step = one pass over the 80 layers computing every projection
+    Y = X . W^T (q,k,v,gate,up from X [m, 8192], o from an [m, 8192] and down
+    from an [m, 28672] activation, synthetic bf16) for m activation rows.
+    Fused: one entq_decode_gemm launch per layer (fp32 Y, the bf16 weights
+    never written). Unfused: entq_decode into a bf16 layer buffer, then seven
+    torch.mm (bf16 Y). HIP events around every launch on the one stream."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    layers, out_elems, tens = compressed_layers_row_aligned(args, E, synth, dev, torch)
+    names = [n for n, _, _ in synth.LLAMA2_70B_LAYER]
+    views = [(names[t], int(tens["rows"][t]), int(tens["cols"][t]), int(tens["out_elem_offset"][t]))
+             for t in range(len(tens))]
+    blob_mean = float(np.mean([l[1].numel() for l in layers]))
+    scale_bytes = 4.0 * int(layers[0][2].numel())
+    buf = torch.empty(out_elems, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator().manual_seed(0)
+    results = []
+    for m in [int(v) for v in (args.tokens or "16,4,1").split(",") if v]:
+        X = (torch.randn(m, 8192, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+        H = (torch.randn(m, 28672, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+        xs = [H if n == "down" else X for n, r, c, o in views]
+        ys = [torch.empty(m, r, dtype=torch.float32, device=dev) for n, r, c, o in views]
+        yb = [torch.empty(m, r, dtype=torch.bfloat16, device=dev) for n, r, c, o in views]
+
+        def fused(ev=None):
+            for li, (p_, blob, sc_) in enumerate(layers):
+                if ev is not None:
+                    ev[li][0].record(stream)
+                E.decode_gemm(p_, blob, sc_, xs, ys, None, stream)
+                if ev is not None:
+                    ev[li][1].record(stream)
+
+        def unfused(ev=None):
+            W = buf.view(torch.bfloat16)
+            for li, (p_, blob, sc_) in enumerate(layers):
+                if ev is not None:
+                    ev[li][0].record(stream)
+                E.decode(p_, blob, buf, E.OUT_BF16, sc_, None, stream)
+                for (n, r, c, o), x, y in zip(views, xs, yb):
+                    torch.mm(x, W[o:o + r * c].view(r, c).t(), out=y)
+                if ev is not None:
+                    ev[li][1].record(stream)
+
+        def decode_only(ev=None):
+            for li, (p_, blob, sc_) in enumerate(layers):
+                if ev is not None:
+                    ev[li][0].record(stream)
+                E.decode(p_, blob, buf, E.OUT_BF16, sc_, None, stream)
+                if ev is not None:
+                    ev[li][1].record(stream)
+
+        row = {"m": m}
+        for name, fn in (("fused", fused), ("unfused", unfused), ("decode_only", decode_only)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                   for _ in layers] for _ in range(args.steps)]
+            t = time.perf_counter()
+            for st in range(args.steps):
+                fn(ev[st])
+            torch.cuda.synchronize()
+            row[name + "_ms_per_step"] = 1e3 * (time.perf_counter() - t) / args.steps
+            lay = np.array([[e[0].elapsed_time(e[1]) for e in ev[st]] for st in range(args.steps)])
+            row[name + "_us_per_layer"] = float(1e3 * lay.mean())
+        row["speedup"] = row["unfused_ms_per_step"] / row["fused_ms_per_step"]
+        log(f"fused m={m}: " + ", ".join(f"{k} {v:.3f}" for k, v in row.items() if k != "m"))
+        results.append(row)
+        del X, H, xs, ys, yb
+    r0 = results[0]
+    # algorithmic bytes of one fused launch: compressed layer + scales + the
+    # activations read + the fp32 results written
+    m0 = r0["m"]
+    act_bytes = 2.0 * m0 * (8192 * 6 + 28672)
+    y_bytes = 4.0 * m0 * sum(r for n, r, c, o in views)
+    alg = blob_mean + scale_bytes + act_bytes + y_bytes
+    gbs = alg / (r0["fused_us_per_layer"] / 1e6) / 1e9
+    rec = {
+        "metric": FUSED_METRIC,
+        "value": m0 / (r0["fused_ms_per_step"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r0["fused_ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 codes -> bf16 weights x bf16 activations, fp32 accumulation",
+        "data": "synthetic (seeded int8 codes of the stated distribution and random bf16 activations; no trained weights)",
+        "config": {
+            "workload": "llama2-70b-shaped 80-layer projection stack, m activation rows, fused decode+GEMM vs decode then torch.mm",
+            "layers": args.layers,
+            "params_per_layer": out_elems,
+            "compressed_bytes_per_layer": blob_mean,
+            "chunking": f"whole rows, at most {args.row_chunk_max} symbols per chunk",
+            "results": results,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
         },
         "cpu_baseline": None,
     }

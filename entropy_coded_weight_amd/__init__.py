@@ -41,6 +41,8 @@ TENSOR_DESC = np.dtype([("kind", "<u4"), ("rows", "<u4"), ("cols", "<u4"),
 CHUNK_DESC = np.dtype([("tensor", "<u4"), ("n_symbols", "<u4"), ("n_words", "<u4"),
                        ("reserved", "<u4"), ("byte_offset", "<u8"), ("elem_offset", "<u8")])
 assert TENSOR_DESC.itemsize == 40 and CHUNK_DESC.itemsize == 32
+# entq_gemm_io (include/entq.h): device pointers as integers
+GEMM_IO = np.dtype([("x", "<u8"), ("ldx", "<u8"), ("y", "<u8"), ("ldy", "<u8")])
 # entq_encode_job (include/entq.h): device pointers as integers
 ENCODE_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
                        ("reserved", "<u4"), ("freq", "<u8"), ("scratch", "<u8"),
@@ -88,6 +90,7 @@ def lib():
             "entq_pack_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, vp, vp]),
             "entq_region_offsets_device": (c.c_int, [vp, u64, u64, vp, vp, vp]),
             "entq_encode_device_batch": (c.c_int, [vp, c.c_int, vp]),
+            "entq_decode_gemm": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -102,7 +105,7 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split",
             "entq_count_symbols_device", "entq_encode_device_scratch_bytes", "entq_region_bytes",
             "entq_encode_device", "entq_pack_device", "entq_region_offsets_device",
-            "entq_encode_device_batch"]
+            "entq_encode_device_batch", "entq_decode_gemm"]
 
 
 def _str(status: int) -> str:
@@ -208,6 +211,26 @@ def decode(p: Plan, compressed, out, out_kind: int, scales=None, chunk_status=No
     st = lib().entq_decode(p.handle, _ptr(compressed), _ptr(out), int(out_kind),
                            _ptr(scales) or None, _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode")
+
+
+def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
+    """Y_t = X_t . W_t^T for every tensor t of the plan, W_t the bf16 weights
+    the bf16 decode would write, without writing them: xs[t] is a device
+    bfloat16 tensor [m, ldx >= cols] (m <= 16, the same m for all), ys[t] a
+    device float32 tensor [m, ldy >= rows]."""
+    import torch
+    assert len(xs) == len(ys) == p.n_tensors
+    m = xs[0].shape[0] if xs else 0
+    io = np.zeros(len(xs), GEMM_IO)
+    for t, (x, y) in enumerate(zip(xs, ys)):
+        assert x.dtype == torch.bfloat16 and y.dtype == torch.float32
+        assert x.dim() == 2 and y.dim() == 2 and x.shape[0] == m and y.shape[0] == m
+        assert x.stride(1) == 1 and y.stride(1) == 1
+        io[t] = (_ptr(x), x.stride(0), _ptr(y), y.stride(0))
+    st = lib().entq_decode_gemm(p.handle, _ptr(compressed), _ptr(scales) or None,
+                                _ptr(io) if len(xs) else None, int(m),
+                                _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_gemm")
 
 
 def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):

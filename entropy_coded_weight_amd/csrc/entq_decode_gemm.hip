@@ -1,0 +1,247 @@
+// entq_decode_gemm.hip -- gfx950 kernel that decodes compressed weight
+// tensors and multiplies them with a few rows of activations in one pass,
+// without writing the decoded bf16 weights anywhere.
+//
+// The pages expect dedicated fused kernels to make entropy-coded weights
+// cheaper at inference [EntQuant, "Float8@2bits: Entropy Coding Enables
+// Data-Free Model Compression", technical summary §5], and the discussion of
+// the DFloat11 write-up suggests a matrix multiply that decompresses each
+// tile as it goes. For each tensor W [rows x cols] of a plan this computes
+//     Y [m x rows] = X [m x cols] . bf16(W)^T      (fp32 accumulation)
+// where bf16(W) are exactly the values the bf16 decode would write.
+//
+// Mapping onto CDNA4. A chunk holds whole rows (chunk size a multiple of
+// cols), so the chunks of a tensor start at row boundaries and, after the
+// same number of steps, every chunk is at the same column of one of its
+// rows. A workgroup of 16 waves decodes 16 consecutive chunks of one tensor
+// in lockstep, 4 steps (256 columns) per block, each wave into its own LDS
+// row: after a block the workgroup holds a 16-row x 256-column weight tile.
+// Each wave then multiplies a 16-column slice of it (its wave index picks
+// the slice) with the matching activation columns on the matrix cores,
+// v_mfma_f32_16x16x16_bf16 (A = activations, m <= 16 rows padded with
+// zeros; B = the slice, one column per weight row), accumulating in fp32.
+// At the end of each weight row the 16 waves' partial sums are added in LDS
+// (fixed order) and written out.
+#include <hip/hip_runtime.h>
+
+#include "entq.h"
+#include "entq_internal.h"
+#include "entq_stream.h"
+
+namespace entq {
+namespace {
+
+constexpr int kGemmMaxTensors = 16;  // tensors per launch
+constexpr uint32_t kGemmM = 16;      // activation rows of one MFMA tile
+
+struct GemmTensor {
+    const uint16_t *x;   // bf16 activations
+    float *y;
+    uint64_t ldx, ldy;   // row strides in elements
+    uint32_t chunk_base; // first DevChunk of the tensor
+    uint32_t n_chunks;
+    uint32_t group0;     // first workgroup of the tensor in this launch
+    uint32_t table;      // the tensor's index in the plan (its slot table)
+    uint32_t cols;
+    uint32_t rows_per_chunk;
+    uint32_t e4m3;
+    uint32_t rows;       // weight rows of the tensor
+};
+
+struct GemmArgs {
+    GemmTensor t[kGemmMaxTensors];
+    uint32_t n_tensors;
+    uint32_t m;
+};
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restrict__ tables,
+                                                        const DevChunk *__restrict__ chunks,
+                                                        const uint8_t *__restrict__ blob,
+                                                        const float *__restrict__ scales,
+                                                        int32_t *__restrict__ status,
+                                                        GemmArgs args) {
+    __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kWaves][kRingWords];
+    __shared__ uint2 T[kProbScale];
+    // two tiles of 16 weight rows x 256 columns (bf16), used in turn; at the
+    // end of a weight row the same bytes hold the 16 waves' partial sums
+    __shared__ __attribute__((aligned(16))) uint16_t TILE[2][kWaves][kBlockSyms];
+    static_assert(sizeof(TILE) >= kWaves * 256 * sizeof(float), "partial sums fit the tiles");
+
+    uint32_t ti = 0;
+    while (ti + 1 < args.n_tensors && args.t[ti + 1].group0 <= blockIdx.x) ++ti;
+    const GemmTensor &gt = args.t[ti];
+    load_table(T, tables, gt.table);
+
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t first = (blockIdx.x - gt.group0) * kWaves;  // this group's first chunk
+    const bool has_chunk = first + wave < gt.n_chunks;
+    const uint32_t cols = gt.cols;
+    const uint32_t blocks_per_row = cols / kBlockSyms;
+
+    DevChunk ch = {};
+    uint32_t my_rows = 0;  // weight rows in this wave's chunk
+    Stream s = {};
+    uint32_t x = 0;
+    if (has_chunk) {
+        ch = chunks[gt.chunk_base + first + wave];
+        my_rows = ch.n_symbols / cols;
+        const uint8_t *region = blob + ch.byte_offset;
+        s.words_g = region + kStateBytes;
+        s.ring = lds_addr(RING[wave]);
+        s.nw = ch.n_words;
+        s.nw8 = (ch.n_words + 7u) & ~7u;
+        x = reinterpret_cast<const uint32_t *>(region)[lane];
+        while (s.issued < s.nw && s.issued < kRingLead) {
+            ring_fill(s, lane);
+            s.issued += kRingUnit;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states and the first ring units
+    s.landed = s.issued;
+    {
+        const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
+        const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
+        s.horizon = a < b ? a : b;
+    }
+    __syncthreads();  // the slot table
+
+    const uint32_t ring_mask = ring_mask_vgpr();
+    // A operand: activation row (lane mod 16), columns 4 (lane / 16) .. +3 of
+    // this wave's 16-column slice of each block
+    const uint32_t a_row = lane & 15;
+    const bool a_live = a_row < args.m;
+    const uint16_t *xa = gt.x + (uint64_t)a_row * gt.ldx + 16u * wave + 4u * (lane >> 4);
+    // B operand: weight row (lane mod 16) of the tile, same columns
+    const uint32_t b_off = (lane & 15) * kBlockSyms + 16u * wave + 4u * (lane >> 4);
+    const uint32_t rows_per_chunk = gt.rows_per_chunk;
+
+    for (uint32_t r = 0; r < rows_per_chunk; ++r) {
+        const bool live = r < my_rows;  // uniform per wave
+        const float scale = live ? scales[ch.scale_row + r] : 0.f;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (uint32_t kb = 0; kb < blocks_per_row; ++kb) {
+            const uint32_t buf = kb & 1;
+            uint16_t *row_tile = TILE[buf][wave];
+            if (live) {
+                if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
+            }
+            // this block's activation slice (in flight while the block decodes)
+            uint2 a = make_uint2(0, 0);
+            if (a_live) a = *reinterpret_cast<const uint2 *>(xa + (uint64_t)kb * kBlockSyms);
+            if (live) {
+#pragma unroll
+                for (uint32_t t = 0; t < kBlockSteps; ++t)
+                    stream_step<false>(x, s.p, s.ring, ring_mask, T, row_tile + 64u * t, lane, true);
+                // lane k: columns 4k .. 4k+3 of the block, dequantised in place
+                const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
+                const uint2 w = gt.e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
+                                        : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
+                *reinterpret_cast<uint2 *>(row_tile + 4u * lane) = w;
+            } else {
+                *reinterpret_cast<uint2 *>(row_tile + 4u * lane) = make_uint2(0, 0);
+            }
+            __syncthreads();  // the tile of this block is complete
+            const uint2 bw = *reinterpret_cast<const uint2 *>(&TILE[buf][0][0] + b_off);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                            __builtin_bit_cast(short4_t, bw), acc,
+                                                            0, 0, 0);
+        }
+        // end of a weight row: add the 16 waves' partial sums, fixed order
+        __syncthreads();  // every wave's last product has read its tile
+        float *part = reinterpret_cast<float *>(&TILE[0][0][0]);
+        *reinterpret_cast<float4_t *>(part + 256u * wave + 4u * lane) = acc;
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            const uint32_t e = threadIdx.x;  // element of the 16x16 result
+            float sum = 0.f;
+            for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) sum += part[256u * w + e];
+            // lane l of a wave held rows 4 (l / 16) + i, column l mod 16
+            const uint32_t l = e >> 2, i = e & 3;
+            const uint32_t mrow = 4u * (l >> 4) + i;  // activation row
+            const uint32_t c = l & 15;                // chunk of the group
+            const uint64_t wrow = (uint64_t)(first + c) * rows_per_chunk + r;  // weight row
+            if (mrow < args.m && first + c < gt.n_chunks && wrow < gt.rows)
+                gt.y[(uint64_t)mrow * gt.ldy + wrow] = sum;
+        }
+        __syncthreads();  // the partial sums are read before the next tile
+    }
+    if (has_chunk) {
+        const uint64_t bad_state = __ballot(x != kStateLow);
+        if (status && lane == 0)
+            status[ch.status_index] = (s.p != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+                                      : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
+    }
+    wait_vm<0>();  // no global->LDS load may outlive the workgroup
+}
+
+}  // namespace
+
+int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
+                       const entq_gemm_io *io, int m, int32_t *status, void *stream) {
+    GemmArgs args = {};
+    args.m = (uint32_t)m;
+    uint64_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (args.n_tensors == 0) return ENTQ_OK;
+        hipLaunchKernelGGL(decode_gemm, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           (hipStream_t)stream, plan->d_tables, plan->d_chunks,
+                           static_cast<const uint8_t *>(blob), scales, status, args);
+        args.n_tensors = 0;
+        blocks = 0;
+        return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+    };
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[t];
+        if (h.n_symbols == 0) continue;
+        const uint64_t groups = ((uint64_t)h.n_chunks + kWaves - 1) / kWaves;
+        if (args.n_tensors == (uint32_t)kGemmMaxTensors || blocks + groups > 0x7FFFFFFFull) {
+            const int st = flush();
+            if (st != ENTQ_OK) return st;
+        }
+        GemmTensor &g = args.t[args.n_tensors++];
+        g.x = static_cast<const uint16_t *>(io[t].d_x);
+        g.y = io[t].d_y;
+        g.ldx = io[t].ldx;
+        g.ldy = io[t].ldy;
+        g.chunk_base = (uint32_t)h.chunk_base;
+        g.n_chunks = (uint32_t)h.n_chunks;
+        g.group0 = (uint32_t)blocks;
+        g.table = (uint32_t)t;
+        g.cols = h.cols;
+        g.rows_per_chunk = h.chunk_symbols / h.cols;
+        g.e4m3 = h.kind == ENTQ_SYM_E4M3;
+        g.rows = h.rows;
+        blocks += groups;
+    }
+    return flush();
+}
+
+}  // namespace entq
+
+extern "C" {
+
+entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
+                             const float *d_scales, const entq_gemm_io *io, int m,
+                             int32_t *d_chunk_status, void *stream) {
+    if (!plan || !io || m < 1 || m > (int)entq::kGemmM) return ENTQ_EINVAL;
+    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const entq::HostTensor &h = plan->host_tensors[t];
+        if (h.n_symbols == 0) continue;
+        if (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3) return ENTQ_EINVAL;
+        if (h.cols == 0 || h.cols % entq::kBlockSyms || h.chunk_symbols % h.cols) return ENTQ_EINVAL;
+        if (h.chunk_base > 0xFFFFFFFFll || h.n_chunks > 0xFFFFFFFFll) return ENTQ_EINVAL;
+        const entq_gemm_io &g = io[t];
+        if (!g.d_x || !g.d_y || g.ldx < h.cols || g.ldy < h.rows) return ENTQ_EINVAL;
+        if ((uintptr_t)g.d_x % 8 || g.ldx % 4 || (uintptr_t)g.d_y % 4) return ENTQ_EALIGN;
+    }
+    return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, io, m,
+                                                 d_chunk_status, stream);
+}
+
+}  // extern "C"

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <vector>
+
 #include "entq.h"
 
 namespace entq {
@@ -64,6 +66,14 @@ struct DevTask {
     uint32_t pad;
 };
 
+// What the host keeps of each tensor of a plan (for launches that need it).
+struct HostTensor {
+    uint32_t kind, rows, cols, chunk_symbols;
+    uint64_t n_symbols;
+    int64_t chunk_base;     // its first DevChunk (chunks in element order)
+    int64_t n_chunks;
+};
+
 }  // namespace entq
 
 // The host-side plan object behind the opaque C handle.
@@ -85,6 +95,7 @@ struct entq_plan_s {
     const entq::DevChunk *d_chunks;
     const entq::DevTask *d_tasks;
     void *host_staging;         // kept alive until destroy (async copy source)
+    std::vector<entq::HostTensor> host_tensors;
 };
 
 // Launchers implemented in entq_decode.hip.
@@ -93,6 +104,9 @@ enum DecodeMode { kModeCodes = 0, kModeBf16 = 1, kModeSplit = 2 };
 int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
                   const float *scales, const uint8_t *signmant, int32_t *status,
                   void *stream);
+// Fused decode + product with activations (entq_decode_gemm.hip).
+int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
+                       const entq_gemm_io *io, int n_rows, int32_t *status, void *stream);
 // Workgroups of the decode kernels that fit on the current device at once
 // (compute units x workgroups per compute unit); 0 if HIP cannot tell.
 int64_t resident_workgroups();

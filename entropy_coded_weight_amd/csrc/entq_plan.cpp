@@ -250,15 +250,30 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
     }
     std::copy(task_list.begin(), task_list.end(), dtask);
 
-    if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
-        hipSuccess) {
+    std::vector<entq::HostTensor> host_tensors;
+    try {
+        host_tensors.resize(n_tensors);
+    } catch (...) {
         std::free(img);
-        return ENTQ_EHIP;
+        return ENTQ_ENOMEM;
     }
+    for (int t = 0; t < n_tensors; ++t) {
+        const entq_tensor_desc &td = tensors[t];
+        host_tensors[t] = {td.kind, td.rows, td.cols, td.chunk_symbols, td.n_symbols,
+                           chunk_base[t], (int64_t)slot_of[t].size()};
+    }
+    // the plan object exists before the copy is enqueued, so that no failure
+    // after it has to free the copy's source
     entq_plan_t *p = new (std::nothrow) entq_plan_t;
     if (!p) {
         std::free(img);
         return ENTQ_ENOMEM;
+    }
+    if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
+        hipSuccess) {
+        delete p;
+        std::free(img);
+        return ENTQ_EHIP;
     }
     uint8_t *ws = (uint8_t *)d_workspace;
     p->n_tensors = n_tensors;
@@ -275,6 +290,7 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
     p->d_chunks = reinterpret_cast<const entq::DevChunk *>(ws + lay.chunks);
     p->d_tasks = reinterpret_cast<const entq::DevTask *>(ws + lay.tasks);
     p->host_staging = img;
+    p->host_tensors = std::move(host_tensors);
     *out = p;
     return ENTQ_OK;
 }

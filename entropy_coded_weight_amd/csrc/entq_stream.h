@@ -1,0 +1,195 @@
+// entq_stream.h -- device pieces of the streaming rANS decoder shared by the
+// decode kernels and the fused decode-GEMM kernel: the per-wave word ring in
+// LDS fed by direct global->LDS loads, the decode step, and the fp32 scale /
+// bf16 rounding of decoded Int8 or Float8 codes. Included by .hip sources
+// only (one private copy per translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "entq.h"
+#include "entq_internal.h"
+
+namespace entq {
+namespace {
+
+__device__ __forceinline__ uint32_t lane_prefix(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) {
+    __bf16 b = (__bf16)v;  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// fl32(v * s) with v as the first operand: when both operands are NaN the
+// hardware returns the first one (quieted), and the format defines the
+// code's NaN to win. The compiler would otherwise put a uniform scale first.
+__device__ __forceinline__ float mul_value_scale(float v, float s) {
+    float r;
+    asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(s));
+    return r;
+}
+
+// The same with a wave-uniform scale taken straight from a scalar register
+// (the VOP3 form reads an SGPR as its second operand; no copy to a VGPR).
+__device__ __forceinline__ float mul_value_uscale(float v, float s) {
+    float r;
+    asm("v_mul_f32_e64 %0, %1, %2" : "=v"(r) : "v"(v), "s"(s));
+    return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to two bf16 (RNE) in one v_cvt_pk_bf16_f32, lo in bits 0..15.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    const float2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ void load_table(uint2 *T, const SlotEntry *tables, uint32_t tensor) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(tables + (size_t)tensor * kProbScale);
+    uint4 *dst = reinterpret_cast<uint4 *>(T);
+    for (uint32_t i = threadIdx.x; i < kProbScale / 2; i += kThreads) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// the word ring and the decode step
+// ---------------------------------------------------------------------------
+
+// Word ring of one wave: kRingWords 16-bit words in LDS at a 2 KB-aligned
+// base, so that "base | (index mod kRingWords) * 2" is one v_and_or. It is
+// refilled in units of kRingUnit words (32 lanes x 16 bytes, one direct
+// global->LDS load) and kept at most kRingLead words ahead of the read
+// pointer, which leaves one unit of room for the unit in flight. A block
+// reads at most kBlockSyms words, so a unit issued at one block's start is
+// not needed before the next block's start.
+constexpr uint32_t kRingWords = 1024;
+constexpr uint32_t kRingUnit = 256;
+constexpr uint32_t kRingLead = kRingWords - kRingUnit;
+static_assert(kRingLead >= 2 * kBlockSyms, "a block must find its words loaded a block early");
+static_assert(kRingUnit == 32 * 8, "one unit = 32 lanes x 8 words");
+static_assert((kRingWords & (kRingWords - 1)) == 0, "ring index wraps with a mask");
+
+// One 16-byte global->LDS load per active lane: lane l's bytes land at LDS
+// address lds_base + 16 l. The compiler does not see this load, so it inserts
+// no wait for it; the kernel waits with explicit vmcnt counts instead.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// All vector-memory operations but the most recent N are complete. The asm
+// form is invisible to the compiler's own wait insertion, which therefore
+// never relaxes it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+
+// Uniform bookkeeping of one chunk on the streaming path.
+struct Stream {
+    const uint8_t *words_g;     // the chunk's word stream in global memory
+    uint32_t ring;              // LDS byte address of the wave's ring
+    uint32_t nw, nw8;           // words, and words rounded up to 8 (16 bytes)
+    uint32_t p;                 // words consumed
+    uint32_t issued, landed;    // words loaded into the ring / known landed
+    uint32_t horizon;           // the ring needs attention once p passes this
+};
+
+// Loads words [issued, issued + kRingUnit) of the chunk into the ring (lanes
+// whose 16 bytes lie inside the chunk's region).
+__device__ __forceinline__ void ring_fill(const Stream &s, uint32_t lane) {
+    const uint32_t w = s.issued + 8u * lane;
+    if (lane < kRingUnit / 8 && w < s.nw8)
+        dma16(s.words_g + 2u * w, s.ring + 2u * (s.issued & (kRingWords - 1)));
+}
+
+// Block start, slow path: makes sure this block's words have landed, tops
+// the ring up to kRingLead words ahead and sets the next horizon.
+__device__ __forceinline__ void ring_service(Stream &s, uint32_t lane) {
+    const uint32_t need_to = (s.p + kBlockSyms < s.nw) ? s.p + kBlockSyms : s.nw;
+    if (s.landed < need_to) {
+        wait_vm<1>();  // everything but the previous block's store
+        s.landed = s.issued;
+    }
+    while (s.issued < s.nw && s.issued < s.p + kRingLead) {
+        ring_fill(s, lane);
+        s.issued += kRingUnit;
+    }
+    // next time: once a block could read past the landed words, or the ring
+    // could take another unit
+    const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
+    const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
+    s.horizon = a < b ? a : b;
+}
+
+// One decode step of a wave: lane j decodes its next symbol (stores the
+// high half of its table entry in the stage) and renormalises from the
+// ring. Every lane reads the ring (no branch on the mask); lanes that
+// renormalise shift the word in, the others keep x (v_perm with a per-lane
+// selector).
+// The ring's byte-index mask in a VGPR: v_and_or_b32 takes one scalar operand
+// (the ring base) and no literal, so the mask has to come in a register. The
+// asm keeps the compiler from folding it back into a literal.
+__device__ __forceinline__ uint32_t ring_mask_vgpr() {
+    uint32_t m;
+    asm("v_mov_b32 %0, %1" : "=v"(m) : "i"(2 * kRingWords - 1));
+    return m;
+}
+
+template <bool PARTIAL>
+__device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &p, uint32_t ring,
+                                            uint32_t ring_mask, const uint2 *T,
+                                            uint16_t *stage_row, uint32_t lane, bool active) {
+    bool need = false;
+    if (!PARTIAL || active) {
+        const uint2 e = T[x & (kProbScale - 1)];
+        x = __umul24(e.x, x >> kProbBits) + e.y;
+        stage_row[lane] = (uint16_t)(e.x >> 16);
+        need = x < kStateLow;
+    }
+    const uint64_t mask = __ballot(need);
+    const uint32_t a = (((p + lane_prefix(mask)) << 1) & ring_mask) | ring;
+    const uint32_t w = *reinterpret_cast<lds_u16 *>(a);
+    x = __builtin_amdgcn_perm(x, w, need ? 0x05040100u : 0x07060504u);
+    p += (uint32_t)__popcll(mask);
+}
+
+// bf16 of (value of a code byte) * scale, two per dword; d holds two staged
+// 16-bit slots, the code bytes in bytes 1 and 3.
+template <bool E4M3>
+__device__ __forceinline__ uint32_t dequant2(uint32_t d, float scale) {
+    float v0, v1;
+    if (E4M3) {
+        v0 = __builtin_amdgcn_cvt_f32_fp8((int)d, 1);
+        v1 = __builtin_amdgcn_cvt_f32_fp8((int)d, 3);
+    } else {
+        v0 = (float)((int32_t)(d << 16) >> 24);
+        v1 = (float)((int32_t)d >> 24);
+    }
+    return bf16x2_bits(mul_value_uscale(v0, scale), mul_value_uscale(v1, scale));
+}
+
+// sign << 15 | exponent << 7 | mantissa for two elements: q holds, per
+// 16-bit half, exponent << 8 | sign+mantissa byte.
+__device__ __forceinline__ uint32_t merge2(uint32_t q) {
+    return ((q >> 1) & 0x7F807F80u) | ((q << 8) & 0x80008000u) | (q & 0x007F007Fu);
+}
+
+}  // namespace
+}  // namespace entq

@@ -205,6 +205,37 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
 entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uint8_t *sm_out,
                             int n_threads);
 
+/* ---- Fused decode + product with activations ----
+ *
+ * EntQuant expects fused kernels to make entropy-coded weights cheaper at
+ * inference [EntQuant, "Float8@2bits: Entropy Coding Enables Data-Free Model
+ * Compression", technical summary §5]; the discussion under the DFloat11
+ * write-up proposes a matrix multiply that decompresses each tile. For every
+ * tensor t of the plan, with W_t its weights as entq_decode(..., ENTQ_OUT_BF16)
+ * would write them (bf16, rows x cols):
+ *     Y_t[i][r] = sum_c X_t[i][c] * W_t[r][c]     (i < m, fp32 accumulation)
+ * The decoded weights are never written to memory.
+ *
+ * io[t]: d_x = bf16 activations X_t, m rows of cols values, row stride ldx
+ * elements (8-byte aligned, ldx a multiple of 4, ldx >= cols); d_y = fp32
+ * results Y_t, m rows of `rows` values, row stride ldy >= rows (4-byte
+ * aligned). All device memory, caller-owned; outputs of different tensors
+ * must not overlap. 1 <= m <= 16.
+ * Requirements on the plan's tensors (else ENTQ_EINVAL): kind INT8 or E4M3,
+ * cols a multiple of 256, chunk_symbols a multiple of cols (every chunk
+ * holds whole rows). d_chunk_status as in entq_decode. Enqueued on stream;
+ * the summation order is fixed (results are reproducible run to run). */
+typedef struct {
+    const void *d_x;
+    uint64_t ldx;
+    float *d_y;
+    uint64_t ldy;
+} entq_gemm_io;
+
+entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
+                             const float *d_scales, const entq_gemm_io *io, int m,
+                             int32_t *d_chunk_status, void *stream);
+
 /* ---- On-device encoder (one wavefront per chunk; same regions as the
  * host encoder, byte for byte) ----
  *

@@ -1,0 +1,191 @@
+"""GPU parity of the fused decode + product (entq_decode_gemm, through the C
+ABI). Expected values come from the oracle: its decoded bf16 weights times
+the activations in fp64. With one-hot activation rows every output is one
+product 1.0 * w, so the kernel must return the oracle's bf16 weights exactly;
+with random activations the fp32 accumulation may differ from the fp64 sum
+by at most cols * 2^-24 * sum |x w| (each of at most cols additions rounds
+once, products of two bf16 are exact in fp32)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-decode-gemm] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()
+    return E
+
+
+def _oracle_weights(b, specs):
+    """bf16 bits [rows, cols] of every tensor, decoded by the oracle from the
+    container's bytes."""
+    out = []
+    for t, sp in enumerate(specs):
+        ch = b.chunks[b.chunks["tensor"] == t]
+        desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"], ch["elem_offset"]],
+                        axis=1).astype(np.uint64)
+        sym, st = oracle.decode_tensor(b.blob, desc, b.freq[t], sp["rows"] * sp["cols"])
+        assert (st == 0).all()
+        w = oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"])
+        out.append(w.reshape(sp["rows"], sp["cols"]))
+    return out
+
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _setup(E, specs):
+    import torch
+    b = E.encode_batch(specs)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    scales = torch.from_numpy(np.concatenate([sp["scales"] for sp in specs])).cuda()
+    return b, p, blob, scales
+
+
+def _run(E, p, blob, scales, xs_host, specs, pad_x=0, pad_y=0):
+    """xs_host: list of float32 arrays [m, cols] (values already bf16)."""
+    import torch
+    xs, ys = [], []
+    for x, sp in zip(xs_host, specs):
+        m, c = x.shape
+        xd = torch.zeros(m, c + pad_x, dtype=torch.bfloat16)
+        xd[:, :c] = torch.from_numpy(x).to(torch.bfloat16)
+        xs.append(xd.cuda())
+        ys.append(torch.full((m, sp["rows"] + pad_y), float("nan"), dtype=torch.float32,
+                             device="cuda"))
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode_gemm(p, blob, scales, [x[:, :] for x in xs], ys, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    return [y.cpu().numpy() for y in ys]
+
+
+def _mixed_specs():
+    specs = []
+    # int8, 512 columns (2 blocks), 4 rows per chunk: 12 chunks, one partial group
+    sp = synth.random_int8_tensor(48, 512, 1.4, 700, 512 * 4)
+    specs.append(sp)
+    # e4m3, 768 columns (3 blocks, odd), 3 rows per chunk, last chunk one row
+    e = synth.e4m3_matrix(rows=40, cols=768)[0]
+    e["chunk_symbols"] = 768 * 3
+    specs.append(e)
+    # int8, 2816 columns (11 blocks), one row per chunk: 100 chunks, 7 groups
+    specs.append(synth.random_int8_tensor(100, 2816, 2.3, 702, 2816))
+    return specs
+
+
+def test_one_hot_activations_return_the_oracle_weights_exactly(E):
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    W = _oracle_weights(b, specs)
+    rng = np.random.default_rng(4)
+    for m in (1, 7, 16):
+        _say(f"one-hot, m={m}")
+        xs, cols_hit = [], []
+        for sp in specs:
+            c = rng.choice(sp["cols"], m, replace=False)
+            x = np.zeros((m, sp["cols"]), np.float32)
+            x[np.arange(m), c] = 1.0
+            xs.append(x)
+            cols_hit.append(c)
+        ys = _run(E, p, blob, scales, xs, specs)
+        for t, sp in enumerate(specs):
+            want = _f32(W[t][:, cols_hit[t]]).T          # [m, rows]
+            assert np.array_equal(ys[t].view(np.uint32), want.view(np.uint32)), (t, m)
+
+
+def test_random_activations_within_the_accumulation_bound(E):
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    W = _oracle_weights(b, specs)
+    rng = np.random.default_rng(5)
+    for m, pad_x, pad_y in ((16, 0, 0), (5, 12, 3), (1, 4, 0)):
+        _say(f"random, m={m}, padded strides {pad_x}/{pad_y}")
+        xs = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+                   & np.uint16(0xBFFF)) for sp in specs]  # finite bf16 values, |x| < 4
+        ys = _run(E, p, blob, scales, xs, specs, pad_x, pad_y)
+        for t, sp in enumerate(specs):
+            w = _f32(W[t]).astype(np.float64)
+            x = xs[t].astype(np.float64)
+            ref = x @ w.T
+            bound = sp["cols"] * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+            got = ys[t][:, :sp["rows"]]
+            assert (np.abs(got - ref) <= bound + 1e-30).all(), (t, m)
+            if pad_y:
+                assert np.isnan(ys[t][:, sp["rows"]:]).all()  # nothing written past the rows
+
+
+def test_results_are_reproducible(E):
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    rng = np.random.default_rng(6)
+    xs = [rng.standard_normal((16, sp["cols"])).astype(np.float32) for sp in specs]
+    a = _run(E, p, blob, scales, xs, specs)
+    c = _run(E, p, blob, scales, xs, specs)
+    for t in range(len(specs)):
+        assert np.array_equal(a[t].view(np.uint32), c[t].view(np.uint32))
+
+
+def test_rejects_chunks_that_split_rows(E):
+    import torch
+    sp = synth.random_int8_tensor(16, 512, 1.0, 703, 4096 + 64 * 3)  # not a multiple of cols
+    b, p, blob, scales = _setup(E, [sp])
+    x = torch.zeros(4, 512, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(4, 16, dtype=torch.float32, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm(p, blob, scales, [x], [y])
+
+
+def _chunk_rows_from_oracle(b, sp, t, rows):
+    """bf16 bits of the given weight rows, each decoded by the oracle from
+    the one chunk that holds it."""
+    cols, C = sp["cols"], sp["chunk_symbols"]
+    ch = b.chunks[b.chunks["tensor"] == t]
+    out = {}
+    for r in rows:
+        k = (r * cols) // C
+        c = ch[ch["elem_offset"] == k * C][0]
+        off, n, nw = int(c["byte_offset"]), int(c["n_symbols"]), int(c["n_words"])
+        states = b.blob[off:off + 256].view(np.uint32)
+        words = b.blob[off + 256:off + 256 + 2 * nw].view(np.uint16)
+        sym, st = oracle.decode_chunk(states, words, n, 64, b.freq[t])
+        assert st == 0
+        i0 = r * cols - k * C
+        row = sym[i0:i0 + cols]
+        out[r] = oracle.dequant_tensor(row, 1, cols, sp["kind"], sp["scales"][r:r + 1])
+    return out
+
+
+def test_llama2_70b_layer_sampled_rows(E):
+    import torch
+    _say("70B-shaped layer 0 with row-aligned chunks, m = 16")
+    specs = synth.llama2_70b_layer(0)
+    for sp in specs:
+        sp["chunk_symbols"] = sp["cols"] * max(1, 65536 // sp["cols"])
+    b, p, blob, scales = _setup(E, specs)
+    rng = np.random.default_rng(7)
+    xs = [(rng.standard_normal((16, sp["cols"])) * 0.5).astype(np.float32) for sp in specs]
+    xs = [_f32((x.view(np.uint32) >> 16).astype(np.uint16)) for x in xs]  # bf16 values
+    ys = _run(E, p, blob, scales, xs, specs)
+    for t, sp in enumerate(specs):
+        rows = sorted(set([0, sp["rows"] - 1] + list(rng.integers(0, sp["rows"], 6))))
+        W = _chunk_rows_from_oracle(b, sp, t, rows)
+        for r in rows:
+            w = _f32(W[r]).astype(np.float64)
+            x = xs[t].astype(np.float64)
+            ref = x @ w
+            bound = sp["cols"] * 2.0 ** -24 * (np.abs(x) @ np.abs(w))
+            assert (np.abs(ys[t][:, r] - ref) <= bound).all(), (t, r)
