@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # passes, calibrated against a plain copy), valid only for the kernel source
 # they were taken with (its SHA-256 is stored beside them).
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_bf16_llama2_70b_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "entropy_coded_weight_amd", "csrc", "entq_decode.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "entropy_coded_weight_amd", "csrc", f)
+                  for f in ("entq_decode.hip", "entq_stream.h")]
 METRIC = "decoded params/s and achieved HBM GB/s (% of peak) for 70B-shaped layer decode"
 
 
@@ -237,16 +238,24 @@ def d2d_copy_gbs(buf):
     return 2.0 * buf.numel() * buf.element_size() / float(np.median(times[1:])) / 1e9
 
 
+def kernel_sources_sha256():
+    """SHA-256 over the decode kernel's source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch from the committed counter record, or None when
     the kernel source has changed since the counters were taken."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        digest = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        digest = kernel_sources_sha256()
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != digest:
+    if rec.get("kernel_sources_sha256") != digest:
         return None
     return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
 
