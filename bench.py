@@ -54,11 +54,13 @@ def parse():
     ap.add_argument("--cpu-sample-tensors", type=int, default=5,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline")
     ap.add_argument("--threads", type=int, default=0)
-    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused"), default="decode",
+    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead"),
+                    default="decode",
                     help="decode: the layer-by-layer decode (the headline line); encode: the "
                          "on-device encoder over 70B-shaped layers; overlap: decode of layer "
                          "l+1 overlapped with layer l's projection GEMMs; fused: decode and "
-                         "product with m activation rows in one kernel vs decode + GEMM")
+                         "product with m activation rows in one kernel vs decode + GEMM; lmhead: "
+                         "the 32,000 x 8,192 output projection decoded on its own")
     ap.add_argument("--tokens", type=str, default="",
                     help="activation rows per GEMM, comma-separated; the first value is the "
                          "line's (overlap default 2048,256,16; fused default 16,4,1)")
@@ -84,6 +86,8 @@ def main():
         return bench_overlap(args)
     if args.path == "fused":
         return bench_fused(args)
+    if args.path == "lmhead":
+        return bench_lm_head(args)
     import torch
 
     import entropy_coded_weight_amd as E
@@ -687,6 +691,117 @@ def bench_fused(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+LMHEAD_METRIC = "decoded params/s for the LLaMA-2-70B output projection (32,000 x 8,192) decoded alone"
+
+
+def bench_lm_head(args):
+    """A single large tensor decoded on its own (the pages compress the
+    embedding and output projection separately from the blocks): the
+    LLaMA-2-70B output projection, int8 codes encoded on the device. A
+    tensor decoded alone has to fill the GPU with its own chunks, so it is
+    encoded in 32,768-symbol chunks (8,000 chunks, whole rows): the line's
+    value is that bf16 decode; 65,536 and 16,384 are timed beside it. Also
+    logits for m activation rows, fused (entq_decode_gemm) against decode +
+    torch.mm, on the 32,768 container."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    nthreads = args.threads or synth.default_threads()
+    conts = {}
+    for C in (32768, 65536, 16384):
+        specs = synth.llama2_70b_lm_head(nthreads=nthreads, chunk_symbols=C)
+        ds = [dict(sp, symbols=torch.from_numpy(
+            np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()).to(dev)) for sp in specs]
+        b = E.encode_batch_device(ds)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
+        conts[C] = (p, b.blob.clone(), torch.from_numpy(specs[0]["scales"]).to(dev),
+                    int(b.blob.numel()), int(p.n_chunks))
+        rows, cols = specs[0]["rows"], specs[0]["cols"]
+        del ds, b
+    torch.cuda.synchronize()
+    n = rows * cols
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, z in ev:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(z) for a, z in ev])) * 1e3  # us
+
+    reps = max(args.steps, 20)
+    dec = {}
+    for C, (p, blob, sc, nbytes, nch) in conts.items():
+        us = timed(lambda: E.decode(p, blob, out, E.OUT_BF16, sc, None, stream), reps)
+        alg = nbytes + 4.0 * rows + 2.0 * n
+        dec[C] = {"chunk_symbols": C, "chunks": nch, "compressed_bytes": nbytes,
+                  "decode_us": us, "params_per_s": n / (us / 1e6),
+                  "alg_gbs": alg / (us / 1e6) / 1e9}
+        log(f"lm head decode, {C}-symbol chunks ({nch}): {us:.1f} us, "
+            f"{dec[C]['alg_gbs']:.0f} GB/s")
+    p, blob, sc, nbytes, nch = conts[32768]
+    W = out.view(torch.bfloat16)
+    logits = []
+    gen = torch.Generator().manual_seed(0)
+    for m in [int(v) for v in (args.tokens or "16,1").split(",") if v]:
+        X = (torch.randn(m, cols, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+        Y = torch.empty(m, rows, dtype=torch.float32, device=dev)
+        Yb = torch.empty(m, rows, dtype=torch.bfloat16, device=dev)
+
+        def unfused():
+            E.decode(p, blob, out, E.OUT_BF16, sc, None, stream)
+            torch.mm(X, W.view(rows, cols).t(), out=Yb)
+
+        f_us = timed(lambda: E.decode_gemm(p, blob, sc, [X], [Y], None, stream), reps)
+        u_us = timed(unfused, reps)
+        logits.append({"m": m, "fused_us": f_us, "unfused_us": u_us, "speedup": u_us / f_us})
+        log(f"lm head logits m={m}: fused {f_us:.1f} us, decode + GEMM {u_us:.1f} us")
+    d0 = dec[32768]
+    rec = {
+        "metric": LMHEAD_METRIC,
+        "value": d0["params_per_s"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": args.warmup,
+        "ms_per_step": d0["decode_us"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f32->bf16",
+        "data": "synthetic (seeded int8 codes of the stated distribution; no trained weights)",
+        "config": {
+            "workload": "llama2-70b output projection 32000x8192 int8 rANS codes -> bf16, decoded alone, 32,768-symbol chunks",
+            "params": n,
+            "decode": list(dec.values()),
+            "logits": logits,
+            "timing": "median of per-launch HIP events",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": d0["alg_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": d0["alg_gbs"] / HBM_PEAK_GBS,
             "traffic": None,
         },
         "cpu_baseline": None,

@@ -166,7 +166,8 @@ LLAMA2_70B_LAYER = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192),
 LLAMA2_70B_LAYERS = 80
 
 # workload ids (first element of every stream key)
-W_TINY_LAPLACE, W_E4M3, W_13B_BLOCK, W_BF16_SPLIT, W_70B = 1, 2, 3, 4, 5
+W_TINY_LAPLACE, W_E4M3, W_13B_BLOCK, W_BF16_SPLIT, W_70B, W_70B_HEAD = 1, 2, 3, 4, 5, 6
+LLAMA2_70B_VOCAB = 32000
 
 
 def _scales(wid, layer, t, rows):
@@ -234,6 +235,19 @@ def llama2_70b_layer(layer: int, shapes=None, nthreads: int | None = None):
                         symbols=codes.view(np.uint8), scales=_scales(W_70B, layer, t, r),
                         dist=("normal", sigma)))
     return out
+
+
+def llama2_70b_lm_head(nthreads: int | None = None, chunk_symbols: int = 65536):
+    """Int8 codes for the LLaMA-2-70B output projection (vocabulary 32,000 x
+    hidden 8,192), a tensor compressed on its own: sigma ~ U[0.8, 3.0] code
+    units as for the layers, round(N(0, sigma)) clipped; per-row scales."""
+    r, c = LLAMA2_70B_VOCAB, 8192
+    sigma = uniform_scalar(0.8, 3.0, key(W_70B_HEAD, 0, 0, 2))
+    codes = int8_codes(lambda x, s=sigma: normal_cdf(x, s), r * c, key(W_70B_HEAD, 0, 0, 0),
+                       nthreads)
+    return [dict(name="lm_head", kind=KIND_INT8, rows=r, cols=c, chunk_symbols=chunk_symbols,
+                 symbols=codes.view(np.uint8), scales=_scales(W_70B_HEAD, 0, 0, r),
+                 dist=("normal", sigma))]
 
 
 def random_int8_tensor(rows: int, cols: int, sigma: float, seed: int, chunk_symbols: int):

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_rows
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -149,26 +150,6 @@ def test_rejects_chunks_that_split_rows(E):
         E.decode_gemm(p, blob, scales, [x], [y])
 
 
-def _chunk_rows_from_oracle(b, sp, t, rows):
-    """bf16 bits of the given weight rows, each decoded by the oracle from
-    the one chunk that holds it."""
-    cols, C = sp["cols"], sp["chunk_symbols"]
-    ch = b.chunks[b.chunks["tensor"] == t]
-    out = {}
-    for r in rows:
-        k = (r * cols) // C
-        c = ch[ch["elem_offset"] == k * C][0]
-        off, n, nw = int(c["byte_offset"]), int(c["n_symbols"]), int(c["n_words"])
-        states = b.blob[off:off + 256].view(np.uint32)
-        words = b.blob[off + 256:off + 256 + 2 * nw].view(np.uint16)
-        sym, st = oracle.decode_chunk(states, words, n, 64, b.freq[t])
-        assert st == 0
-        i0 = r * cols - k * C
-        row = sym[i0:i0 + cols]
-        out[r] = oracle.dequant_tensor(row, 1, cols, sp["kind"], sp["scales"][r:r + 1])
-    return out
-
-
 def test_llama2_70b_layer_sampled_rows(E):
     import torch
     _say("70B-shaped layer 0 with row-aligned chunks, m = 16")
@@ -182,7 +163,8 @@ def test_llama2_70b_layer_sampled_rows(E):
     ys = _run(E, p, blob, scales, xs, specs)
     for t, sp in enumerate(specs):
         rows = sorted(set([0, sp["rows"] - 1] + list(rng.integers(0, sp["rows"], 6))))
-        W = _chunk_rows_from_oracle(b, sp, t, rows)
+        W = oracle_rows.rows_from_oracle(b.blob, b.chunks[b.chunks["tensor"] == t], b.freq[t],
+                                         sp, rows)
         for r in rows:
             w = _f32(W[r]).astype(np.float64)
             x = xs[t].astype(np.float64)

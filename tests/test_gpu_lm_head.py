@@ -1,0 +1,80 @@
+"""GPU parity of a single large tensor decoded on its own: the LLaMA-2-70B
+output projection (32,000 x 8,192 int8 codes), through the bf16 decode and
+through the fused decode + product (logits for 16 activation rows).
+Expected values: the oracle, row by row from the chunks that hold them."""
+import numpy as np
+import pytest
+
+import oracle_rows
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-lm-head] {msg}", flush=True)
+
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()
+    return E
+
+
+def _container(E, chunk_symbols):
+    import torch
+    specs = synth.llama2_70b_lm_head(chunk_symbols=chunk_symbols)
+    b = E.encode_batch(specs)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    return specs, b, p, torch.from_numpy(b.blob).cuda(), torch.from_numpy(specs[0]["scales"]).cuda()
+
+
+def _rows(rng, n):
+    return sorted(set([0, 1, n - 1] + [int(v) for v in rng.integers(0, n, 9)]))
+
+
+def test_lm_head_bf16_decode(E):
+    import torch
+    _say("LM head 32000 x 8192, 65,536-symbol chunks, bf16 decode")
+    specs, b, p, blob, scales = _container(E, 65536)
+    sp = specs[0]
+    out = torch.empty(sp["rows"] * sp["cols"], dtype=torch.int16, device="cuda")
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, blob, out, E.OUT_BF16, scales, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    got = out.view(sp["rows"], sp["cols"])
+    rows = _rows(np.random.default_rng(8), sp["rows"])
+    want = oracle_rows.rows_from_oracle(b.blob, b.chunks, b.freq[0], sp, rows)
+    for r in rows:
+        assert np.array_equal(got[r].cpu().numpy().view(np.uint16), want[r]), r
+
+
+def test_lm_head_fused_logits(E):
+    import torch
+    _say("LM head, row-aligned 32,768-symbol chunks, fused logits for 16 rows")
+    specs, b, p, blob, scales = _container(E, 32768)
+    sp = specs[0]
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((16, sp["cols"])) * 0.5).astype(np.float32)
+    x = _f32((x.view(np.uint32) >> 16).astype(np.uint16))  # bf16 values
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    y = torch.full((16, sp["rows"]), float("nan"), dtype=torch.float32, device="cuda")
+    E.decode_gemm(p, blob, scales, [xd], [y])
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert not np.isnan(got).any()
+    rows = _rows(rng, sp["rows"])
+    W = oracle_rows.rows_from_oracle(b.blob, b.chunks, b.freq[0], sp, rows)
+    for r in rows:
+        w = _f32(W[r]).astype(np.float64)
+        ref = x.astype(np.float64) @ w
+        bound = sp["cols"] * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(w))
+        assert (np.abs(got[:, r] - ref) <= bound).all(), r
