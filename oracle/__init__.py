@@ -40,7 +40,7 @@ L = 1 << 16
 CONTAINER_LANES = 64
 
 KIND_INT8, KIND_E4M3, KIND_BF16EXP = 0, 1, 2
-STATUS_OK, STATUS_BAD_STATE, STATUS_BAD_WORDS = 0, 1, 2
+STATUS_OK, STATUS_BAD_STATE, STATUS_BAD_WORDS, STATUS_BAD_TABLE = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -324,6 +324,96 @@ def decode_container_bf16(c: Container, scales: np.ndarray):
     for td, sym in zip(c.tensors, syms):
         o = td["out_elem_offset"]
         so = td["scale_row_offset"]
+        out[o:o + td["n_symbols"]] = dequant_tensor(sym, td["rows"], td["cols"], td["kind"],
+                                                    scales[so:so + td["rows"]])
+    return out, status
+
+
+# --------------------------------------------------------------------------
+# per-chunk (adaptive) tables
+# --------------------------------------------------------------------------
+#
+# EntroLLM names adaptive entropy coding as its next step (EntroLLM summary,
+# "Significado y Afirmaciones"); the pages say no more. Reading taken here:
+# every chunk is coded with the table of its own symbol counts (rule C2
+# applied to the chunk), stored at the head of the chunk's region. The coder
+# itself is unchanged.
+#
+# Region of a chunk: u16 freq[256] (little-endian), u32 states[64], u16
+# words[n_words], zeros up to a 16-byte boundary.
+
+ADAPTIVE_TABLE_BYTES = 2 * 256
+
+
+def adaptive_region_bytes(n_words: int) -> int:
+    return (ADAPTIVE_TABLE_BYTES + 4 * CONTAINER_LANES + 2 * n_words + 15) // 16 * 16
+
+
+def encode_container_adaptive(specs, chunk_symbols_default: int = 65536) -> Container:
+    """As encode_container, but each chunk carries its own table; the
+    tensor records carry none (freq = None)."""
+    regions, tensors, rows_ = [], [], []
+    off = out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        sym = np.ascontiguousarray(sp["symbols"], dtype=np.uint8).ravel()
+        rows, cols = int(sp["rows"]), int(sp["cols"])
+        assert sym.size == rows * cols
+        C = int(sp.get("chunk_symbols", chunk_symbols_default))
+        for e0 in range(0, sym.size, C):
+            part = sym[e0:e0 + C]
+            freq = quantize_freqs(count_symbols(part))
+            states, words = encode_chunk(part, CONTAINER_LANES, freq)
+            region = np.zeros(adaptive_region_bytes(words.size), np.uint8)
+            region[:ADAPTIVE_TABLE_BYTES] = freq.astype("<u2").view(np.uint8)
+            s0 = ADAPTIVE_TABLE_BYTES
+            region[s0:s0 + 4 * CONTAINER_LANES] = states.astype("<u4").view(np.uint8)
+            w0 = s0 + 4 * CONTAINER_LANES
+            region[w0:w0 + 2 * words.size] = words.astype("<u2").view(np.uint8)
+            rows_.append((t, part.size, words.size, off, e0))
+            regions.append(region)
+            off += region.size
+        tensors.append(dict(kind=int(sp["kind"]), rows=rows, cols=cols, chunk_symbols=C,
+                            n_symbols=sym.size, out_elem_offset=out_off,
+                            scale_row_offset=scale_off, freq=None))
+        out_off += sym.size
+        scale_off += rows
+    blob = np.concatenate(regions) if regions else np.zeros(0, np.uint8)
+    chunks = np.array(rows_, dtype=np.uint64).reshape(-1, 5)
+    return Container(blob, tensors, chunks)
+
+
+def decode_adaptive_chunk(blob: np.ndarray, byte_offset: int, n: int, n_words: int):
+    """(symbols uint8[n], status) of one chunk region of an adaptive
+    container; status STATUS_BAD_TABLE if its table does not sum to 4096."""
+    r = blob[byte_offset:byte_offset + adaptive_region_bytes(n_words)]
+    freq = r[:ADAPTIVE_TABLE_BYTES].view("<u2").astype(np.uint16)
+    if not table_valid(freq):
+        return np.zeros(n, np.uint8), STATUS_BAD_TABLE
+    s0 = ADAPTIVE_TABLE_BYTES
+    states = r[s0:s0 + 4 * CONTAINER_LANES].view("<u4").astype(np.uint32)
+    w0 = s0 + 4 * CONTAINER_LANES
+    words = r[w0:w0 + 2 * n_words].view("<u2").astype(np.uint16)
+    return decode_chunk(states, words, n, CONTAINER_LANES, freq)
+
+
+def decode_container_adaptive_symbols(c: Container):
+    """(list of per-tensor symbol arrays, per-chunk status in container chunk
+    order) of an adaptive container."""
+    outs = [np.zeros(td["n_symbols"], np.uint8) for td in c.tensors]
+    status = np.zeros(c.n_chunks, np.int32)
+    for k, (t, n, nw, off, e0) in enumerate(c.chunks.astype(np.int64)):
+        sym, st = decode_adaptive_chunk(c.blob, int(off), int(n), int(nw))
+        outs[t][e0:e0 + n] = sym
+        status[k] = st
+    return outs, status
+
+
+def decode_container_adaptive_bf16(c: Container, scales: np.ndarray):
+    syms, status = decode_container_adaptive_symbols(c)
+    total = sum(t["n_symbols"] for t in c.tensors)
+    out = np.zeros(total, np.uint16)
+    for td, sym in zip(c.tensors, syms):
+        o, so = td["out_elem_offset"], td["scale_row_offset"]
         out[o:o + td["n_symbols"]] = dequant_tensor(sym, td["rows"], td["cols"], td["kind"],
                                                     scales[so:so + td["rows"]])
     return out, status

@@ -166,7 +166,7 @@ LLAMA2_70B_LAYER = [("q", 8192, 8192), ("k", 1024, 8192), ("v", 1024, 8192),
 LLAMA2_70B_LAYERS = 80
 
 # workload ids (first element of every stream key)
-W_TINY_LAPLACE, W_E4M3, W_13B_BLOCK, W_BF16_SPLIT, W_70B, W_70B_HEAD = 1, 2, 3, 4, 5, 6
+W_TINY_LAPLACE, W_E4M3, W_13B_BLOCK, W_BF16_SPLIT, W_70B, W_70B_HEAD, W_BANDED = 1, 2, 3, 4, 5, 6, 7
 LLAMA2_70B_VOCAB = 32000
 
 
@@ -248,6 +248,24 @@ def llama2_70b_lm_head(nthreads: int | None = None, chunk_symbols: int = 65536):
     return [dict(name="lm_head", kind=KIND_INT8, rows=r, cols=c, chunk_symbols=chunk_symbols,
                  symbols=codes.view(np.uint8), scales=_scales(W_70B_HEAD, 0, 0, r),
                  dist=("normal", sigma))]
+
+
+def banded_int8_tensor(rows: int, cols: int, band_rows: int, seed: int, chunk_symbols: int,
+                       lo: float = 0.3, hi: float = 4.0, nthreads: int | None = None):
+    """Int8 codes whose spread changes along the tensor: every band of
+    band_rows rows draws its own sigma ~ U[lo, hi] code units, round(N(0,
+    sigma)) clipped. A tensor of this kind is what per-chunk tables are for
+    (one table per tensor fits none of the bands)."""
+    parts = []
+    for b0 in range(0, rows, band_rows):
+        r = min(band_rows, rows - b0)
+        sigma = uniform_scalar(lo, hi, key(W_BANDED, seed, b0, 2))
+        parts.append(int8_codes(lambda x, s=sigma: normal_cdf(x, s), r * cols,
+                                key(W_BANDED, seed, b0, 0), nthreads))
+    codes = np.concatenate(parts) if parts else np.zeros(0, np.int8)
+    return dict(name=f"banded{seed}", kind=KIND_INT8, rows=rows, cols=cols,
+                chunk_symbols=chunk_symbols, symbols=codes.view(np.uint8),
+                scales=_scales(W_BANDED, seed, 0, rows), dist=("banded-normal", lo, hi, band_rows))
 
 
 def random_int8_tensor(rows: int, cols: int, sigma: float, seed: int, chunk_symbols: int):
