@@ -54,13 +54,14 @@ def parse():
     ap.add_argument("--cpu-sample-tensors", type=int, default=5,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline")
     ap.add_argument("--threads", type=int, default=0)
-    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead"),
+    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead", "adaptive"),
                     default="decode",
                     help="decode: the layer-by-layer decode (the headline line); encode: the "
                          "on-device encoder over 70B-shaped layers; overlap: decode of layer "
                          "l+1 overlapped with layer l's projection GEMMs; fused: decode and "
                          "product with m activation rows in one kernel vs decode + GEMM; lmhead: "
-                         "the 32,000 x 8,192 output projection decoded on its own")
+                         "the 32,000 x 8,192 output projection decoded on its own; adaptive: "
+                         "per-chunk tables against shared tables")
     ap.add_argument("--tokens", type=str, default="",
                     help="activation rows per GEMM, comma-separated; the first value is the "
                          "line's (overlap default 2048,256,16; fused default 16,4,1)")
@@ -88,6 +89,8 @@ def main():
         return bench_fused(args)
     if args.path == "lmhead":
         return bench_lm_head(args)
+    if args.path == "adaptive":
+        return bench_adaptive(args)
     import torch
 
     import entropy_coded_weight_amd as E
@@ -802,6 +805,126 @@ def bench_lm_head(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": d0["alg_gbs"] / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+ADAPTIVE_METRIC = ("decoded params/s and achieved HBM GB/s for 70B-shaped layer decode with "
+                   "per-chunk tables")
+
+
+def bench_adaptive(args):
+    """The 80-layer decode of the headline workload with every chunk coded
+    by its own table (entq_encode_tensor_adaptive / entq_plan_adaptive),
+    timed against the shared-table decode of the same codes in the same
+    process (one launch per layer, HIP events on the stream). Also one
+    70B-shaped layer of banded codes (the spread changes every 8 rows, sigma
+    ~ U[0.3, 4.0]), the case per-chunk tables are for: sizes and decode
+    times under both."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    nthreads = args.threads or synth.default_threads()
+
+    def build(specs, adaptive):
+        b = E.encode_batch_adaptive(specs, nthreads) if adaptive else E.encode_batch(specs, nthreads)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+        sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)
+        return p, torch.from_numpy(b.blob).to(dev), sc, int(b.blob.size), b.out_elems
+
+    t0 = time.time()
+    lay = {True: [], False: []}
+    for layer in range(args.layers):
+        specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
+        for adaptive in (True, False):
+            lay[adaptive].append(build(specs, adaptive))
+        if layer % 10 == 0 or layer == args.layers - 1:
+            log(f"adaptive: layer {layer} encoded both ways ({time.time() - t0:.1f}s)")
+    params = lay[True][0][4]
+    out = torch.empty(params, dtype=torch.int16, device=dev)
+
+    def time_pass(layers):
+        def run(ev=None):
+            for li, (p_, blob, sc_, _, _) in enumerate(layers):
+                if ev is not None:
+                    ev[li][0].record(stream)
+                E.decode(p_, blob, out, E.OUT_BF16, sc_, None, stream)
+                if ev is not None:
+                    ev[li][1].record(stream)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in layers] for _ in range(args.steps)]
+        t = time.perf_counter()
+        for st in range(args.steps):
+            run(ev[st])
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t) / args.steps
+        us = float(1e3 * np.mean([[e[0].elapsed_time(e[1]) for e in ev[st]]
+                                   for st in range(args.steps)]))
+        return ms, us
+
+    res = {}
+    for adaptive in (True, False):
+        ms, us = time_pass(lay[adaptive])
+        nbytes = float(np.mean([l[3] for l in lay[adaptive]]))
+        alg = nbytes + 4.0 * int(lay[adaptive][0][2].numel()) + 2.0 * params
+        res["per_chunk" if adaptive else "shared"] = {
+            "ms_per_step": ms, "us_per_layer": us, "compressed_bytes_per_layer": nbytes,
+            "bits_per_param": 8.0 * nbytes / params, "alg_gbs": alg / (us / 1e6) / 1e9}
+        log(f"adaptive={adaptive}: {ms:.3f} ms/step, {us:.1f} us/layer, "
+            f"{8.0 * nbytes / params:.4f} bits/param")
+    for k in lay:
+        lay[k].clear()
+    torch.cuda.empty_cache()
+    # banded codes: one layer's shapes, sigma changing every 8 rows
+    specs = [synth.banded_int8_tensor(r, c, 8, 20 + t, 65536, nthreads=nthreads)
+             for t, (_, r, c) in enumerate(synth.LLAMA2_70B_LAYER)]
+    banded = {}
+    for adaptive in (True, False):
+        one = [build(specs, adaptive)]
+        ms, us = time_pass(one)
+        banded["per_chunk" if adaptive else "shared"] = {
+            "us": us, "compressed_bytes": one[0][3], "bits_per_param": 8.0 * one[0][3] / params}
+        log(f"banded adaptive={adaptive}: {us:.1f} us, {8.0 * one[0][3] / params:.4f} bits/param")
+    r0 = res["per_chunk"]
+    rec = {
+        "metric": ADAPTIVE_METRIC,
+        "value": params * args.layers / (r0["ms_per_step"] / 1e3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r0["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f32->bf16",
+        "data": "synthetic (seeded int8 codes of the stated distributions; no trained weights)",
+        "config": {
+            "workload": "llama2-70b-shaped layer-by-layer decode, int8 rANS codes with per-chunk tables -> bf16",
+            "layers": args.layers,
+            "params_per_layer": params,
+            "chunk_symbols": 65536,
+            "per_chunk_vs_shared": res,
+            "banded_layer": banded,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": r0["alg_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": r0["alg_gbs"] / HBM_PEAK_GBS,
             "traffic": None,
         },
         "cpu_baseline": None,

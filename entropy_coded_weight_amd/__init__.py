@@ -91,6 +91,11 @@ def lib():
             "entq_region_offsets_device": (c.c_int, [vp, u64, u64, vp, vp, vp]),
             "entq_encode_device_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_decode_gemm": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
+            "entq_plan_adaptive": (c.c_int, [vp, c.c_int, vp, i64, u64, vp, c.c_size_t, vp,
+                                             c.POINTER(vp)]),
+            "entq_encode_tensor_adaptive": (c.c_int, [vp, u64, c.c_uint32, c.c_uint32, u64, vp,
+                                                      u64, vp, vp, c.c_int]),
+            "entq_encode_bound_adaptive": (u64, [u64, c.c_uint32]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -105,7 +110,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_build_freq", "entq_encode_bound", "entq_encode_tensor", "entq_bf16_split",
             "entq_count_symbols_device", "entq_encode_device_scratch_bytes", "entq_region_bytes",
             "entq_encode_device", "entq_pack_device", "entq_region_offsets_device",
-            "entq_encode_device_batch", "entq_decode_gemm"]
+            "entq_encode_device_batch", "entq_decode_gemm", "entq_plan_adaptive",
+            "entq_encode_tensor_adaptive", "entq_encode_bound_adaptive"]
 
 
 def _str(status: int) -> str:
@@ -152,13 +158,17 @@ class Plan:
     """A validated batch with its device workspace (a torch uint8 tensor that
     this object keeps alive)."""
 
-    def __init__(self, tensors: np.ndarray, freq_tables: np.ndarray, chunk_index: np.ndarray,
+    def __init__(self, tensors: np.ndarray, freq_tables, chunk_index: np.ndarray,
                  blob_bytes: int, device="cuda", stream=None):
+        """freq_tables None: the chunks carry their own tables
+        (entq_plan_adaptive)."""
         import torch
         tensors = np.ascontiguousarray(tensors, dtype=TENSOR_DESC)
         chunk_index = np.ascontiguousarray(chunk_index, dtype=CHUNK_DESC)
-        freq_tables = np.ascontiguousarray(freq_tables, dtype=np.uint16).reshape(-1, 256)
-        assert freq_tables.shape[0] == tensors.shape[0]
+        adaptive = freq_tables is None
+        if not adaptive:
+            freq_tables = np.ascontiguousarray(freq_tables, dtype=np.uint16).reshape(-1, 256)
+            assert freq_tables.shape[0] == tensors.shape[0]
         n_t, n_c = int(tensors.shape[0]), int(chunk_index.shape[0])
         ws_bytes = int(lib().entq_plan_workspace_bytes(n_t, n_c))
         raw = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=device)
@@ -166,12 +176,19 @@ class Plan:
         self.workspace = raw[shift:shift + ws_bytes]
         self._raw = raw
         h = ctypes.c_void_p()
-        st = lib().entq_plan(_ptr(tensors) if n_t else None, n_t,
-                             _ptr(freq_tables) if n_t else None,
-                             _ptr(chunk_index) if n_c else None, n_c, int(blob_bytes),
-                             self.workspace.data_ptr(), ws_bytes, _stream(stream),
-                             ctypes.byref(h))
-        _check(st, "entq_plan")
+        if adaptive:
+            st = lib().entq_plan_adaptive(_ptr(tensors) if n_t else None, n_t,
+                                          _ptr(chunk_index) if n_c else None, n_c,
+                                          int(blob_bytes), self.workspace.data_ptr(), ws_bytes,
+                                          _stream(stream), ctypes.byref(h))
+        else:
+            st = lib().entq_plan(_ptr(tensors) if n_t else None, n_t,
+                                 _ptr(freq_tables) if n_t else None,
+                                 _ptr(chunk_index) if n_c else None, n_c, int(blob_bytes),
+                                 self.workspace.data_ptr(), ws_bytes, _stream(stream),
+                                 ctypes.byref(h))
+        _check(st, "entq_plan_adaptive" if adaptive else "entq_plan")
+        self.adaptive = adaptive
         self._h = h
         self.n_tensors, self.n_chunks = n_t, n_c
         self.tensors = tensors
@@ -277,6 +294,25 @@ def encode_tensor(symbols: np.ndarray, chunk_symbols: int, freq: np.ndarray, ten
     return out[:written.value], chunks[:k]
 
 
+def encode_tensor_adaptive(symbols: np.ndarray, chunk_symbols: int, tensor_id: int = 0,
+                           base_offset: int = 0, n_threads: int | None = None):
+    """encode_tensor with per-chunk tables (each region starts with its own
+    u16 freq[256]). Returns (region bytes uint8, chunk descriptors)."""
+    symbols = np.ascontiguousarray(symbols).view(np.uint8).ravel()
+    n = symbols.size
+    cap = int(lib().entq_encode_bound_adaptive(n, chunk_symbols))
+    out = np.empty(max(cap, 16), np.uint8)
+    k = -(-n // chunk_symbols)
+    chunks = np.zeros(max(k, 1), CHUNK_DESC)
+    written = ctypes.c_uint64()
+    _check(lib().entq_encode_tensor_adaptive(_ptr(symbols) if n else None, n, chunk_symbols,
+                                             tensor_id, base_offset, _ptr(out), out.size,
+                                             _ptr(chunks), ctypes.byref(written),
+                                             n_threads or default_threads()),
+           "entq_encode_tensor_adaptive")
+    return out[:written.value], chunks[:k]
+
+
 def bf16_split(words: np.ndarray, n_threads: int | None = None):
     words = np.ascontiguousarray(words).view(np.uint16).ravel()
     e = np.empty(words.size, np.uint8)
@@ -333,6 +369,28 @@ def encode_batch(specs, n_threads: int | None = None) -> Batch:
     blob = np.concatenate(regions) if regions else np.zeros(0, np.uint8)
     chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
     return Batch(blob, tens, freqs, chunks)
+
+
+def encode_batch_adaptive(specs, n_threads: int | None = None) -> Batch:
+    """encode_batch with per-chunk tables; the Batch's freq is None (pass it
+    to plan() as such)."""
+    regions, descs = [], []
+    tens = np.zeros(len(specs), TENSOR_DESC)
+    off = out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        sym = np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()
+        rows, cols, C = int(sp["rows"]), int(sp["cols"]), int(sp["chunk_symbols"])
+        assert sym.size == rows * cols
+        r, ch = encode_tensor_adaptive(sym, C, t, off, n_threads)
+        regions.append(r)
+        descs.append(ch)
+        off += r.size
+        tens[t] = (int(sp["kind"]), rows, cols, C, sym.size, out_off, scale_off)
+        out_off += sym.size
+        scale_off += rows
+    blob = np.concatenate(regions) if regions else np.zeros(0, np.uint8)
+    chunks = np.concatenate(descs) if descs else np.zeros(0, CHUNK_DESC)
+    return Batch(blob, tens, None, chunks)
 
 
 # --------------------------------------------------------------------------

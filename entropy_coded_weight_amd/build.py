@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libentq.so")
 
-SOURCES = ["entq_decode.hip", "entq_decode_gemm.hip", "entq_plan.cpp", "entq_encode.cpp",
+SOURCES = ["entq_decode.hip", "entq_decode_gemm.hip", "entq_decode_adaptive.hip", "entq_plan.cpp",
+           "entq_encode.cpp",
            "entq_encode_dev.hip"]
 
 

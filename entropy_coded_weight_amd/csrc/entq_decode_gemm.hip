@@ -227,7 +227,7 @@ extern "C" {
 entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
                              int32_t *d_chunk_status, void *stream) {
-    if (!plan || !io || m < 1 || m > (int)entq::kGemmM) return ENTQ_EINVAL;
+    if (!plan || plan->adaptive || !io || m < 1 || m > (int)entq::kGemmM) return ENTQ_EINVAL;
     if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
     if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
     for (int t = 0; t < plan->n_tensors; ++t) {

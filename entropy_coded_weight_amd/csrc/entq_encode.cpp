@@ -61,6 +61,19 @@ inline uint32_t div_freq(uint32_t x, uint64_t recip) {
     return (uint32_t)(((unsigned __int128)x * recip) >> 44);
 }
 
+// The coding constants of a table; false if it does not sum to 4096.
+bool make_code(const uint16_t freq[256], SymCode code[256]) {
+    uint32_t total = 0;
+    for (int s = 0; s < 256; ++s) {
+        code[s].freq = freq[s];
+        code[s].start = total;
+        code[s].x_limit = (uint64_t)freq[s] << 20;  // ((L >> 12) << 16) * f
+        code[s].recip = freq[s] ? ((1ull << 44) / freq[s]) + 1 : 0;
+        total += freq[s];
+    }
+    return total == entq::kProbScale;
+}
+
 // Encodes one chunk: symbols sym[0..n) on lanes i mod 64, walked back to
 // front (the decoder reads front to back). Emitted words are stored from the
 // end of `scratch` towards its start, so scratch[*first .. cap) ends up in
@@ -156,28 +169,30 @@ uint64_t entq_encode_bound(uint64_t n_symbols, uint32_t chunk_symbols) {
     return k * (entq::kStateBytes + ENTQ_REGION_ALIGN) + 2 * n_symbols;
 }
 
-entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chunk_symbols,
-                               const uint16_t freq[256], uint32_t tensor_id,
+
+}  // extern "C"
+
+namespace {
+
+// The tensor encoder. freq == nullptr: every chunk is coded with the table of
+// its own counts (entq_build_freq), stored as the first ENTQ_TABLE_BYTES of
+// its region.
+entq_status encode_tensor_impl(const uint8_t *symbols, uint64_t n, uint32_t chunk_symbols,
+                               const uint16_t *freq, uint32_t tensor_id,
                                uint64_t base_offset, uint8_t *out, uint64_t out_cap,
                                entq_chunk_desc *chunks_out, uint64_t *bytes_written,
                                int n_threads) {
-    if (!freq || !bytes_written || (n && (!symbols || !out || !chunks_out)))
+    if (!bytes_written || (n && (!symbols || !out || !chunks_out)))
         return ENTQ_EINVAL;
     if (chunk_symbols == 0 || chunk_symbols % entq::kLanes || chunk_symbols > entq::kMaxChunkSymbols)
         return ENTQ_EINVAL;
     if (base_offset % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
     *bytes_written = 0;
     if (n == 0) return ENTQ_OK;
-    uint32_t total = 0;
-    SymCode code[256];
-    for (int s = 0; s < 256; ++s) {
-        code[s].freq = freq[s];
-        code[s].start = total;
-        code[s].x_limit = (uint64_t)freq[s] << 20;  // ((L >> 12) << 16) * f
-        code[s].recip = freq[s] ? ((1ull << 44) / freq[s]) + 1 : 0;
-        total += freq[s];
-    }
-    if (total != entq::kProbScale) return ENTQ_EBADTABLE;
+    const bool adaptive = freq == nullptr;
+    const uint32_t head = adaptive ? ENTQ_TABLE_BYTES : 0;
+    SymCode shared[256];
+    if (!adaptive && !make_code(freq, shared)) return ENTQ_EBADTABLE;
 
     const uint64_t n_chunks = (n + chunk_symbols - 1) / chunk_symbols;
     const int nt = pick_threads(n_threads, n_chunks);
@@ -190,12 +205,22 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
     parallel_ranges(nt, n_chunks, [&](int t, uint64_t kb, uint64_t ke) {
         Part &part = parts[t];
         // worst case (one word per symbol); untouched pages cost nothing
-        part.bytes.reserve((ke - kb) * (entq::kStateBytes + ENTQ_REGION_ALIGN + 2ull * chunk_symbols));
+        part.bytes.reserve((ke - kb) * (head + entq::kStateBytes + ENTQ_REGION_ALIGN + 2ull * chunk_symbols));
         std::vector<uint16_t> scratch(chunk_symbols);
         uint32_t lanes[64];
+        SymCode own[256];
+        uint16_t own_freq[256];
         for (uint64_t k = kb; k < ke && part.ok; ++k) {
             const uint64_t e0 = k * chunk_symbols;
             const uint32_t cn = (uint32_t)std::min<uint64_t>(chunk_symbols, n - e0);
+            const SymCode *code = shared;
+            if (adaptive) {
+                uint64_t counts[256] = {0};
+                for (uint32_t i = 0; i < cn; ++i) counts[symbols[e0 + i]]++;
+                entq_build_freq(counts, own_freq);
+                make_code(own_freq, own);
+                code = own;
+            }
             uint32_t first = 0;
             if (!encode_chunk(symbols + e0, cn, code, lanes, scratch.data(), chunk_symbols, &first)) {
                 part.ok = false;
@@ -203,10 +228,11 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
             }
             const uint32_t nw = chunk_symbols - first;
             const uint64_t at = part.bytes.size();
-            part.bytes.resize(at + region_size(nw), 0);
+            part.bytes.resize(at + head + region_size(nw), 0);
             uint8_t *r = part.bytes.data() + at;
-            std::memcpy(r, lanes, entq::kStateBytes);  // little-endian host
-            std::memcpy(r + entq::kStateBytes, scratch.data() + first, 2ull * nw);
+            if (adaptive) std::memcpy(r, own_freq, ENTQ_TABLE_BYTES);  // little-endian host
+            std::memcpy(r + head, lanes, entq::kStateBytes);
+            std::memcpy(r + head + entq::kStateBytes, scratch.data() + first, 2ull * nw);
             local_off[k] = at;
             entq_chunk_desc &d = chunks_out[k];
             d.tensor = tensor_id;
@@ -237,6 +263,35 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
     }
     *bytes_written = total_bytes;
     return ENTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chunk_symbols,
+                               const uint16_t freq[256], uint32_t tensor_id,
+                               uint64_t base_offset, uint8_t *out, uint64_t out_cap,
+                               entq_chunk_desc *chunks_out, uint64_t *bytes_written,
+                               int n_threads) {
+    if (!freq) return ENTQ_EINVAL;
+    return encode_tensor_impl(symbols, n, chunk_symbols, freq, tensor_id, base_offset, out,
+                              out_cap, chunks_out, bytes_written, n_threads);
+}
+
+entq_status entq_encode_tensor_adaptive(const uint8_t *symbols, uint64_t n,
+                                        uint32_t chunk_symbols, uint32_t tensor_id,
+                                        uint64_t base_offset, uint8_t *out, uint64_t out_cap,
+                                        entq_chunk_desc *chunks_out, uint64_t *bytes_written,
+                                        int n_threads) {
+    return encode_tensor_impl(symbols, n, chunk_symbols, nullptr, tensor_id, base_offset, out,
+                              out_cap, chunks_out, bytes_written, n_threads);
+}
+
+uint64_t entq_encode_bound_adaptive(uint64_t n_symbols, uint32_t chunk_symbols) {
+    if (chunk_symbols == 0) return 0;
+    uint64_t k = (n_symbols + chunk_symbols - 1) / chunk_symbols;
+    return entq_encode_bound(n_symbols, chunk_symbols) + k * ENTQ_TABLE_BYTES;
 }
 
 entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uint8_t *sm_out,

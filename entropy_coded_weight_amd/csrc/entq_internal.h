@@ -96,6 +96,7 @@ struct entq_plan_s {
     const entq::DevTask *d_tasks;
     void *host_staging;         // kept alive until destroy (async copy source)
     std::vector<entq::HostTensor> host_tensors;
+    bool adaptive = false;      // chunk regions carry their own tables
 };
 
 // Launchers implemented in entq_decode.hip.
@@ -104,6 +105,9 @@ enum DecodeMode { kModeCodes = 0, kModeBf16 = 1, kModeSplit = 2 };
 int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
                   const float *scales, const uint8_t *signmant, int32_t *status,
                   void *stream);
+// Decode of a plan whose chunks carry their own tables (entq_decode_adaptive.hip).
+int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, void *out,
+                           const float *scales, int32_t *status, void *stream);
 // Fused decode + product with activations (entq_decode_gemm.hip).
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
                        const entq_gemm_io *io, int n_rows, int32_t *status, void *stream);

@@ -70,13 +70,21 @@ const char *entq_status_str(entq_status s) {
     return "unknown status";
 }
 
-entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint16_t *freq_tables,
+}  // extern "C"
+
+namespace {
+
+// The plan builder behind entq_plan and entq_plan_adaptive. adaptive: every
+// chunk region starts with its own table (freq_tables unused), the decode
+// goes through decode_adaptive, which needs whole 256-symbol blocks.
+entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint16_t *freq_tables,
                       const entq_chunk_desc *chunk_index, int64_t n_chunks, uint64_t blob_bytes,
-                      void *d_workspace, size_t workspace_bytes, void *stream, entq_plan_t **out) {
+                      void *d_workspace, size_t workspace_bytes, void *stream, entq_plan_t **out,
+                      bool adaptive) {
     if (!out) return ENTQ_EINVAL;
     *out = nullptr;
     if (n_tensors < 0 || n_chunks < 0) return ENTQ_EINVAL;
-    if (n_tensors > 0 && (!tensors || !freq_tables)) return ENTQ_EINVAL;
+    if (n_tensors > 0 && (!tensors || (!adaptive && !freq_tables))) return ENTQ_EINVAL;
     if (n_chunks > 0 && !chunk_index) return ENTQ_EINVAL;
     if (n_chunks > (int64_t)UINT32_MAX) return ENTQ_EINVAL;
     if (!d_workspace) return ENTQ_EINVAL;
@@ -93,9 +101,16 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
             return ENTQ_EINVAL;
         if ((uint64_t)td.rows * td.cols != td.n_symbols) return ENTQ_EINVAL;
         if (td.n_symbols == 0) continue;
-        uint32_t sum = 0;
-        for (int s = 0; s < 256; ++s) sum += freq_tables[(size_t)t * 256 + s];
-        if (sum != entq::kProbScale) return ENTQ_EBADTABLE;
+        if (adaptive) {
+            if (td.kind == ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
+            if (td.chunk_symbols % entq::kBlockSyms || td.cols % entq::kBlockSyms ||
+                td.out_elem_offset % 16)
+                return ENTQ_EINVAL;
+        } else {
+            uint32_t sum = 0;
+            for (int s = 0; s < 256; ++s) sum += freq_tables[(size_t)t * 256 + s];
+            if (sum != entq::kProbScale) return ENTQ_EBADTABLE;
+        }
         kinds_mask |= 1u << td.kind;
         if (td.out_elem_offset > UINT64_MAX - td.n_symbols) return ENTQ_EINVAL;
         out_elems = std::max(out_elems, td.out_elem_offset + td.n_symbols);
@@ -129,7 +144,8 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
         if (cd.elem_offset % td.chunk_symbols || cd.elem_offset >= td.n_symbols) return ENTQ_EBADINDEX;
         const uint64_t expect = std::min<uint64_t>(td.chunk_symbols, td.n_symbols - cd.elem_offset);
         if (cd.n_symbols != expect) return ENTQ_EBADINDEX;
-        if (cd.byte_offset > blob_bytes || region_size(cd.n_words) > blob_bytes - cd.byte_offset)
+        const uint64_t rb = region_size(cd.n_words) + (adaptive ? ENTQ_TABLE_BYTES : 0);
+        if (cd.byte_offset > blob_bytes || rb > blob_bytes - cd.byte_offset)
             return ENTQ_EBADINDEX;
         int64_t &slot = slot_of[cd.tensor][cd.elem_offset / td.chunk_symbols];
         if (slot >= 0) return ENTQ_EBADINDEX;  // two chunks for one place
@@ -219,7 +235,7 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
     for (int t = 0; t < n_tensors; ++t) {
         const uint16_t *f = freq_tables + (size_t)t * 256;
         entq::SlotEntry *T = tables + (size_t)t * entq::kProbScale;
-        if (tensors[t].n_symbols) {
+        if (tensors[t].n_symbols && !adaptive) {
             uint32_t start = 0;
             for (uint32_t s = 0; s < 256; ++s) {
                 for (uint32_t k = 0; k < f[s]; ++k) {
@@ -291,8 +307,28 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint
     p->d_tasks = reinterpret_cast<const entq::DevTask *>(ws + lay.tasks);
     p->host_staging = img;
     p->host_tensors = std::move(host_tensors);
+    p->adaptive = adaptive;
     *out = p;
     return ENTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors, const uint16_t *freq_tables,
+                      const entq_chunk_desc *chunk_index, int64_t n_chunks, uint64_t blob_bytes,
+                      void *d_workspace, size_t workspace_bytes, void *stream, entq_plan_t **out) {
+    return plan_impl(tensors, n_tensors, freq_tables, chunk_index, n_chunks, blob_bytes,
+                     d_workspace, workspace_bytes, stream, out, false);
+}
+
+entq_status entq_plan_adaptive(const entq_tensor_desc *tensors, int n_tensors,
+                               const entq_chunk_desc *chunk_index, int64_t n_chunks,
+                               uint64_t blob_bytes, void *d_workspace, size_t workspace_bytes,
+                               void *stream, entq_plan_t **out) {
+    return plan_impl(tensors, n_tensors, nullptr, chunk_index, n_chunks, blob_bytes, d_workspace,
+                     workspace_bytes, stream, out, true);
 }
 
 void entq_plan_destroy(entq_plan_t *plan) {
@@ -327,6 +363,9 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
         if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
         mode = entq::kModeBf16;
     }
+    if (plan->adaptive)
+        return (entq_status)entq::launch_decode_adaptive(plan, mode, d_compressed, d_out,
+                                                         d_scales, d_chunk_status, stream);
     return (entq_status)entq::launch_decode(plan, mode, d_compressed, d_out, d_scales, nullptr,
                                             d_chunk_status, stream);
 }
@@ -334,7 +373,7 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
 entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                    const uint8_t *d_signmant, uint16_t *d_out,
                                    int32_t *d_chunk_status, void *stream) {
-    if (!plan) return ENTQ_EINVAL;
+    if (!plan || plan->adaptive) return ENTQ_EINVAL;
     if (plan->kinds_mask & ~(1u << ENTQ_SYM_BF16EXP)) return ENTQ_EINVAL;
     if (plan->n_chunks == 0) return ENTQ_OK;
     if (!d_exp_stream || !d_signmant || !d_out) return ENTQ_EINVAL;

@@ -71,6 +71,7 @@ extern "C" {
 #define ENTQ_LANES 64u
 #define ENTQ_STATE_LOW 65536u
 #define ENTQ_REGION_ALIGN 16u
+#define ENTQ_TABLE_BYTES 512u   /* a per-chunk table: u16 freq[256] */
 
 typedef enum {
     ENTQ_OK = 0,
@@ -92,6 +93,7 @@ typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
 #define ENTQ_CHUNK_OK 0
 #define ENTQ_CHUNK_BAD_STATE 1  /* a lane did not end at 2^16              */
 #define ENTQ_CHUNK_BAD_WORDS 2  /* words ran out or were not all consumed  */
+#define ENTQ_CHUNK_BAD_TABLE 3  /* (per-chunk tables) the chunk's table does not sum to 4096 */
 
 /* One tensor of a batch (40 bytes). rows x cols row-major; n_symbols must be
  * rows * cols. Output element i of the tensor goes to out[out_elem_offset +
@@ -142,6 +144,22 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors,
                       uint64_t blob_bytes,
                       void *d_workspace, size_t workspace_bytes, void *stream,
                       entq_plan_t **out);
+
+/* A plan over chunks that carry their own tables. EntroLLM names adaptive
+ * entropy coding as its next step [EntroLLM summary, "Significado y
+ * Afirmaciones"]; here every chunk is coded with the table of its own counts.
+ * The region of a chunk is u16 freq[256] (ENTQ_TABLE_BYTES, sum 4096), then
+ * the 64 states and the words as in a shared-table region, zero-padded to 16
+ * bytes (entq_encode_tensor_adaptive writes it). Same arguments as entq_plan
+ * without tables; tensors must be INT8 or E4M3 with chunk_symbols and cols
+ * multiples of 256 and out_elem_offset a multiple of 16 (else ENTQ_EINVAL).
+ * entq_decode works on such a plan (a chunk whose table does not sum to 4096
+ * gets ENTQ_CHUNK_BAD_TABLE and no output); entq_decode_bf16_split and
+ * entq_decode_gemm reject it. */
+entq_status entq_plan_adaptive(const entq_tensor_desc *tensors, int n_tensors,
+                               const entq_chunk_desc *chunk_index, int64_t n_chunks,
+                               uint64_t blob_bytes, void *d_workspace, size_t workspace_bytes,
+                               void *stream, entq_plan_t **out);
 
 /* Decodes every chunk of the plan in one launch.
  *   d_compressed  device blob (16-byte aligned, blob_bytes long)
@@ -199,6 +217,18 @@ entq_status entq_encode_tensor(const uint8_t *symbols, uint64_t n, uint32_t chun
                                uint64_t base_offset, uint8_t *out, uint64_t out_cap,
                                entq_chunk_desc *chunks_out, uint64_t *bytes_written,
                                int n_threads);
+
+/* entq_encode_tensor with per-chunk tables: chunk k is coded with
+ * entq_build_freq of its own counts, written as the first ENTQ_TABLE_BYTES
+ * of its region (see entq_plan_adaptive). */
+entq_status entq_encode_tensor_adaptive(const uint8_t *symbols, uint64_t n,
+                                        uint32_t chunk_symbols, uint32_t tensor_id,
+                                        uint64_t base_offset, uint8_t *out, uint64_t out_cap,
+                                        entq_chunk_desc *chunks_out, uint64_t *bytes_written,
+                                        int n_threads);
+
+/* Upper bound on the bytes of one tensor with per-chunk tables. */
+uint64_t entq_encode_bound_adaptive(uint64_t n_symbols, uint32_t chunk_symbols);
 
 /* Splits bf16 words into exponent bytes ((w >> 7) & 0xFF) and sign+mantissa
  * bytes ((w >> 15) << 7 | (w & 0x7F)). */

@@ -1,0 +1,146 @@
+"""GPU parity of the per-chunk-table (adaptive) decode through the C ABI:
+codes and bf16 output equal the oracle's adaptive decode; a chunk whose
+table is corrupt reports ENTQ_CHUNK_BAD_TABLE while its neighbours decode;
+a whole 70B-shaped layer is checked on sampled chunks."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-adaptive] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()
+    return E
+
+
+def _plan(E, c, blob=None):
+    import torch
+    tens = np.zeros(len(c.tensors), E.TENSOR_DESC)
+    for t, td in enumerate(c.tensors):
+        tens[t] = (td["kind"], td["rows"], td["cols"], td["chunk_symbols"], td["n_symbols"],
+                   td["out_elem_offset"], td["scale_row_offset"])
+    ch = np.zeros(c.n_chunks, E.CHUNK_DESC)
+    ch["tensor"], ch["n_symbols"], ch["n_words"] = c.chunks[:, 0], c.chunks[:, 1], c.chunks[:, 2]
+    ch["byte_offset"], ch["elem_offset"] = c.chunks[:, 3], c.chunks[:, 4]
+    b = c.blob if blob is None else blob
+    return E.plan(tens, None, ch, b.size), torch.from_numpy(b).cuda()
+
+
+def _decode(E, p, blob, total, out_kind, scales=None):
+    import torch
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    if out_kind == E.OUT_CODES:
+        out = torch.zeros(total, dtype=torch.uint8, device="cuda")
+        E.decode(p, blob, out, E.OUT_CODES, None, status)
+    else:
+        out = torch.zeros(total, dtype=torch.int16, device="cuda")
+        E.decode(p, blob, out, E.OUT_BF16, torch.from_numpy(scales).cuda(), status)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    return (o.view(np.uint16) if o.dtype == np.int16 else o), status.cpu().numpy()
+
+
+def _specs():
+    specs = [synth.random_int8_tensor(r, c, 0.6 + 0.5 * i, 140 + i, C)
+             for i, (r, c, C) in enumerate([(3, 256, 256), (17, 512, 4096), (5, 4352, 4096),
+                                            (33, 1024, 65536)])]
+    one = synth.random_int8_tensor(16, 256, 1.0, 150, 1024)
+    one["symbols"] = np.full(one["symbols"].shape, 77, np.uint8)
+    allb = synth.random_int8_tensor(64, 512, 1.0, 151, 4096)
+    allb["symbols"] = synth.random_bytes(64 * 512, 151).view(np.uint8)
+    e = synth.e4m3_matrix(rows=48, cols=768)[0]
+    e["chunk_symbols"] = 768 * 4
+    specs += [one, allb, e, synth.banded_int8_tensor(48, 2816, 4, 6, 2816 * 4)]
+    return specs
+
+
+def test_codes_and_bf16_match_the_oracle(E):
+    specs = _specs()
+    _say(f"{len(specs)} tensors, per-chunk tables")
+    c = oracle.encode_container_adaptive(specs)
+    p, blob = _plan(E, c)
+    total = sum(td["n_symbols"] for td in c.tensors)
+    syms, st = oracle.decode_container_adaptive_symbols(c)
+    assert (st == 0).all()
+    got, gst = _decode(E, p, blob, total, E.OUT_CODES)
+    np.testing.assert_array_equal(got, np.concatenate(syms))
+    np.testing.assert_array_equal(gst, st)
+    scales = np.concatenate([np.asarray(s["scales"], np.float32) for s in specs])
+    want, _ = oracle.decode_container_adaptive_bf16(c, scales)
+    got, gst = _decode(E, p, blob, total, E.OUT_BF16, scales)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(gst, st)
+
+
+def test_corrupt_table_is_reported_per_chunk(E):
+    sp = synth.random_int8_tensor(32, 512, 1.5, 152, 1024)
+    c = oracle.encode_container_adaptive([sp])
+    blob = c.blob.copy()
+    off = int(c.chunks[3, 3])
+    blob[off + 2 * 130] ^= 4   # chunk 3's table no longer sums to 4096
+    bad = oracle.Container(blob, c.tensors, c.chunks)
+    syms, st = oracle.decode_container_adaptive_symbols(bad)
+    assert st.tolist() == [0, 0, 0, oracle.STATUS_BAD_TABLE] + [0] * (c.n_chunks - 4)
+    p, b = _plan(E, bad, blob)
+    got, gst = _decode(E, p, b, sp["rows"] * sp["cols"], E.OUT_CODES)
+    np.testing.assert_array_equal(gst, st)
+    src = sp["symbols"]
+    for k, (t, n, nw, o, e0) in enumerate(c.chunks.astype(np.int64)):
+        if st[k] == 0:
+            np.testing.assert_array_equal(got[e0:e0 + n], src[e0:e0 + n])
+        else:
+            assert (got[e0:e0 + n] == 0).all()  # no output for the rejected chunk
+
+
+def test_other_calls_reject_adaptive_plans(E):
+    import torch
+    c = oracle.encode_container_adaptive([synth.random_int8_tensor(16, 512, 1.0, 153, 1024)])
+    p, blob = _plan(E, c)
+    x = torch.zeros(2, 512, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(2, 16, dtype=torch.float32, device="cuda")
+    scales = torch.ones(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm(p, blob, scales, [x], [y])
+    out = torch.zeros(16 * 512, dtype=torch.int16, device="cuda")
+    sm = torch.zeros(16 * 512, dtype=torch.uint8, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_bf16_split(p, blob, sm, out)
+
+
+def test_llama2_70b_layer_sampled_chunks(E):
+    import torch
+    _say("70B-shaped layer 0 with per-chunk tables (library host encoder)")
+    specs = synth.llama2_70b_layer(0)
+    b = E.encode_batch_adaptive(specs)
+    p = E.plan(b.tensors, None, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    scales = np.concatenate([s["scales"] for s in specs])
+    total = sum(s["rows"] * s["cols"] for s in specs)
+    got, gst = _decode(E, p, blob, total, E.OUT_BF16, scales)
+    assert (gst == 0).all()
+    rng = np.random.default_rng(10)
+    picks = sorted(set([0, len(b.chunks) - 1] + [int(v) for v in rng.integers(0, len(b.chunks), 14)]))
+    for k in picks:
+        ch = b.chunks[k]
+        t, n, e0 = int(ch["tensor"]), int(ch["n_symbols"]), int(ch["elem_offset"])
+        sym, st = oracle.decode_adaptive_chunk(b.blob, int(ch["byte_offset"]), n, int(ch["n_words"]))
+        assert st == 0
+        sp = specs[t]
+        o = int(b.tensors[t]["out_elem_offset"])
+        cols = sp["cols"]
+        r0, r1 = e0 // cols, (e0 + n - 1) // cols       # the rows the chunk touches
+        full = np.zeros((r1 - r0 + 1) * cols, np.uint8)
+        full[e0 - r0 * cols:e0 - r0 * cols + n] = sym
+        want = oracle.dequant_tensor(full, r1 - r0 + 1, cols, sp["kind"], sp["scales"][r0:r1 + 1])
+        np.testing.assert_array_equal(got[o + e0:o + e0 + n], want[e0 - r0 * cols:e0 - r0 * cols + n])
