@@ -64,7 +64,7 @@ def parse():
                          "per-chunk tables against shared tables")
     ap.add_argument("--tokens", type=str, default="",
                     help="activation rows per GEMM, comma-separated; the first value is the "
-                         "line's (overlap default 2048,256,16; fused default 16,4,1)")
+                         "line's (overlap default 2048,256,16; fused default 16,4,1,32,64)")
     ap.add_argument("--encode-layers", type=int, default=4,
                     help="resident layers of source codes the encode steps cycle through")
     ap.add_argument("--row-chunk-max", type=int, default=32768,
@@ -607,7 +607,7 @@ def bench_fused(args):
     stream = torch.cuda.current_stream()
     gen = torch.Generator().manual_seed(0)
     results = []
-    for m in [int(v) for v in (args.tokens or "16,4,1").split(",") if v]:
+    for m in [int(v) for v in (args.tokens or "16,4,1,32,64").split(",") if v]:
         X = (torch.randn(m, 8192, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         H = (torch.randn(m, 28672, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         xs = [H if n == "down" else X for n, r, c, o in views]

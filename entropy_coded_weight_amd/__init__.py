@@ -233,7 +233,7 @@ def decode(p: Plan, compressed, out, out_kind: int, scales=None, chunk_status=No
 def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
     """Y_t = X_t . W_t^T for every tensor t of the plan, W_t the bf16 weights
     the bf16 decode would write, without writing them: xs[t] is a device
-    bfloat16 tensor [m, ldx >= cols] (m <= 16, the same m for all), ys[t] a
+    bfloat16 tensor [m, ldx >= cols] (m <= 64, the same m for all), ys[t] a
     device float32 tensor [m, ldy >= rows]."""
     import torch
     assert len(xs) == len(ys) == p.n_tensors

@@ -18,8 +18,9 @@
 // row: after a block the workgroup holds a 16-row x 256-column weight tile.
 // Each wave then multiplies a 16-column slice of it (its wave index picks
 // the slice) with the matching activation columns on the matrix cores,
-// v_mfma_f32_16x16x16_bf16 (A = activations, m <= 16 rows padded with
-// zeros; B = the slice, one column per weight row), accumulating in fp32.
+// v_mfma_f32_16x16x16_bf16 (A = 16 activation rows, m <= 64 rows in up to
+// four groups, the last padded with zeros; B = the slice, one column per
+// weight row), accumulating in fp32.
 // At the end of each weight row the 16 waves' partial sums are added in LDS
 // (fixed order) and written out.
 #include <hip/hip_runtime.h>
@@ -33,6 +34,7 @@ namespace {
 
 constexpr int kGemmMaxTensors = 16;  // tensors per launch
 constexpr uint32_t kGemmM = 16;      // activation rows of one MFMA tile
+constexpr int kGemmMaxGroups = 4;    // up to 64 activation rows per launch
 
 struct GemmTensor {
     const uint16_t *x;   // bf16 activations
@@ -57,6 +59,7 @@ struct GemmArgs {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+template <int MT>  // groups of 16 activation rows
 __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restrict__ tables,
                                                         const DevChunk *__restrict__ chunks,
                                                         const uint8_t *__restrict__ blob,
@@ -110,11 +113,11 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     __syncthreads();  // the slot table
 
     const uint32_t ring_mask = ring_mask_vgpr();
-    // A operand: activation row (lane mod 16), columns 4 (lane / 16) .. +3 of
-    // this wave's 16-column slice of each block
+    // A operand: activation row (lane mod 16) of each group of 16, columns
+    // 4 (lane / 16) .. +3 of this wave's 16-column slice of each block
     const uint32_t a_row = lane & 15;
-    const bool a_live = a_row < args.m;
     const uint16_t *xa = gt.x + (uint64_t)a_row * gt.ldx + 16u * wave + 4u * (lane >> 4);
+    const uint64_t group_stride = 16ull * gt.ldx;
     // B operand: weight row (lane mod 16) of the tile, same columns
     const uint32_t b_off = (lane & 15) * kBlockSyms + 16u * wave + 4u * (lane >> 4);
     const uint32_t rows_per_chunk = gt.rows_per_chunk;
@@ -122,16 +125,24 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     for (uint32_t r = 0; r < rows_per_chunk; ++r) {
         const bool live = r < my_rows;  // uniform per wave
         const float scale = live ? scales[ch.scale_row + r] : 0.f;
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float4_t acc[MT];
+#pragma unroll
+        for (int g = 0; g < MT; ++g) acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
         for (uint32_t kb = 0; kb < blocks_per_row; ++kb) {
             const uint32_t buf = kb & 1;
             uint16_t *row_tile = TILE[buf][wave];
             if (live) {
                 if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
             }
-            // this block's activation slice (in flight while the block decodes)
-            uint2 a = make_uint2(0, 0);
-            if (a_live) a = *reinterpret_cast<const uint2 *>(xa + (uint64_t)kb * kBlockSyms);
+            // this block's activation slices (in flight while the block decodes)
+            uint2 a[MT];
+#pragma unroll
+            for (int g = 0; g < MT; ++g) {
+                a[g] = make_uint2(0, 0);
+                if (16u * g + a_row < args.m)
+                    a[g] = *reinterpret_cast<const uint2 *>(xa + g * group_stride +
+                                                            (uint64_t)kb * kBlockSyms);
+            }
             if (live) {
 #pragma unroll
                 for (uint32_t t = 0; t < kBlockSteps; ++t)
@@ -146,26 +157,32 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
             }
             __syncthreads();  // the tile of this block is complete
             const uint2 bw = *reinterpret_cast<const uint2 *>(&TILE[buf][0][0] + b_off);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
-                                                            __builtin_bit_cast(short4_t, bw), acc,
-                                                            0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < MT; ++g)
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(short4_t, a[g]), __builtin_bit_cast(short4_t, bw), acc[g],
+                    0, 0, 0);
         }
-        // end of a weight row: add the 16 waves' partial sums, fixed order
-        __syncthreads();  // every wave's last product has read its tile
+        // end of a weight row: add the 16 waves' partial sums, fixed order,
+        // one group of activation rows at a time
         float *part = reinterpret_cast<float *>(&TILE[0][0][0]);
-        *reinterpret_cast<float4_t *>(part + 256u * wave + 4u * lane) = acc;
-        __syncthreads();
-        if (threadIdx.x < 256) {
-            const uint32_t e = threadIdx.x;  // element of the 16x16 result
-            float sum = 0.f;
-            for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) sum += part[256u * w + e];
-            // lane l of a wave held rows 4 (l / 16) + i, column l mod 16
-            const uint32_t l = e >> 2, i = e & 3;
-            const uint32_t mrow = 4u * (l >> 4) + i;  // activation row
-            const uint32_t c = l & 15;                // chunk of the group
-            const uint64_t wrow = (uint64_t)(first + c) * rows_per_chunk + r;  // weight row
-            if (mrow < args.m && first + c < gt.n_chunks && wrow < gt.rows)
-                gt.y[(uint64_t)mrow * gt.ldy + wrow] = sum;
+#pragma unroll
+        for (int g = 0; g < MT; ++g) {
+            __syncthreads();  // the tiles (or the previous group's sums) are read
+            *reinterpret_cast<float4_t *>(part + 256u * wave + 4u * lane) = acc[g];
+            __syncthreads();
+            if (threadIdx.x < 256) {
+                const uint32_t e = threadIdx.x;  // element of the 16x16 result
+                float sum = 0.f;
+                for (uint32_t w = 0; w < (uint32_t)kWaves; ++w) sum += part[256u * w + e];
+                // lane l of a wave held rows 4 (l / 16) + i, column l mod 16
+                const uint32_t l = e >> 2, i = e & 3;
+                const uint32_t mrow = 16u * g + 4u * (l >> 4) + i;  // activation row
+                const uint32_t c = l & 15;                          // chunk of the group
+                const uint64_t wrow = (uint64_t)(first + c) * rows_per_chunk + r;  // weight row
+                if (mrow < args.m && first + c < gt.n_chunks && wrow < gt.rows)
+                    gt.y[(uint64_t)mrow * gt.ldy + wrow] = sum;
+            }
         }
         __syncthreads();  // the partial sums are read before the next tile
     }
@@ -185,11 +202,24 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
     GemmArgs args = {};
     args.m = (uint32_t)m;
     uint64_t blocks = 0;
+    const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
     auto flush = [&]() -> int {
         if (args.n_tensors == 0) return ENTQ_OK;
-        hipLaunchKernelGGL(decode_gemm, dim3((unsigned)blocks), dim3(kThreads), 0,
-                           (hipStream_t)stream, plan->d_tables, plan->d_chunks,
-                           static_cast<const uint8_t *>(blob), scales, status, args);
+        const dim3 grid((unsigned)blocks), block(kThreads);
+        const uint8_t *b = static_cast<const uint8_t *>(blob);
+        hipStream_t st = (hipStream_t)stream;
+        if (groups_m == 1)
+            hipLaunchKernelGGL(decode_gemm<1>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
+                               b, scales, status, args);
+        else if (groups_m == 2)
+            hipLaunchKernelGGL(decode_gemm<2>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
+                               b, scales, status, args);
+        else if (groups_m == 3)
+            hipLaunchKernelGGL(decode_gemm<3>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
+                               b, scales, status, args);
+        else
+            hipLaunchKernelGGL(decode_gemm<4>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
+                               b, scales, status, args);
         args.n_tensors = 0;
         blocks = 0;
         return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
@@ -227,7 +257,8 @@ extern "C" {
 entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
                              int32_t *d_chunk_status, void *stream) {
-    if (!plan || plan->adaptive || !io || m < 1 || m > (int)entq::kGemmM) return ENTQ_EINVAL;
+    if (!plan || plan->adaptive || !io || m < 1 || m > (int)entq::kGemmM * entq::kGemmMaxGroups)
+        return ENTQ_EINVAL;
     if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
     if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
     for (int t = 0; t < plan->n_tensors; ++t) {

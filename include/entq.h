@@ -250,7 +250,7 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * elements (8-byte aligned, ldx a multiple of 4, ldx >= cols); d_y = fp32
  * results Y_t, m rows of `rows` values, row stride ldy >= rows (4-byte
  * aligned). All device memory, caller-owned; outputs of different tensors
- * must not overlap. 1 <= m <= 16.
+ * must not overlap. 1 <= m <= 64.
  * Requirements on the plan's tensors (else ENTQ_EINVAL): kind INT8 or E4M3,
  * cols a multiple of 256, chunk_symbols a multiple of cols (every chunk
  * holds whole rows). d_chunk_status as in entq_decode. Enqueued on stream;

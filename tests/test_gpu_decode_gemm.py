@@ -93,7 +93,7 @@ def test_one_hot_activations_return_the_oracle_weights_exactly(E):
     b, p, blob, scales = _setup(E, specs)
     W = _oracle_weights(b, specs)
     rng = np.random.default_rng(4)
-    for m in (1, 7, 16):
+    for m in (1, 7, 16, 17, 40, 64):
         _say(f"one-hot, m={m}")
         xs, cols_hit = [], []
         for sp in specs:
@@ -113,7 +113,7 @@ def test_random_activations_within_the_accumulation_bound(E):
     b, p, blob, scales = _setup(E, specs)
     W = _oracle_weights(b, specs)
     rng = np.random.default_rng(5)
-    for m, pad_x, pad_y in ((16, 0, 0), (5, 12, 3), (1, 4, 0)):
+    for m, pad_x, pad_y in ((16, 0, 0), (5, 12, 3), (1, 4, 0), (33, 8, 1), (64, 0, 0)):
         _say(f"random, m={m}, padded strides {pad_x}/{pad_y}")
         xs = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
                    & np.uint16(0xBFFF)) for sp in specs]  # finite bf16 values, |x| < 4
@@ -138,6 +138,16 @@ def test_results_are_reproducible(E):
     c = _run(E, p, blob, scales, xs, specs)
     for t in range(len(specs)):
         assert np.array_equal(a[t].view(np.uint32), c[t].view(np.uint32))
+
+
+def test_rejects_more_than_64_activation_rows(E):
+    import torch
+    specs = _mixed_specs()[:1]
+    b, p, blob, scales = _setup(E, specs)
+    x = torch.zeros(65, specs[0]["cols"], dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(65, specs[0]["rows"], dtype=torch.float32, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm(p, blob, scales, [x], [y])
 
 
 def test_rejects_chunks_that_split_rows(E):
