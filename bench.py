@@ -557,12 +557,34 @@ FUSED_METRIC = ("tokens/s through the 80-layer 70B-shaped projection stack with 
                 "weights decoded inside the GEMM (entq_decode_gemm)")
 
 
+def oracle_tensor_sample(blob, chunks, freq, spec, n_chunks):
+    """The oracle decoding + dequantising the first n_chunks chunks of one
+    tensor (shared tables; chunks: that tensor's CHUNK_DESC rows, byte
+    offsets into blob) to bf16 bits. Returns (bits, seconds, elements);
+    the chunks hold whole rows or the rows they touch are completed with
+    zeros before the dequantiser."""
+    import oracle
+    ch = np.sort(chunks, order="elem_offset")[:n_chunks]
+    desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"], ch["elem_offset"]],
+                    axis=1).astype(np.uint64)
+    n = int(ch["elem_offset"][-1]) + int(ch["n_symbols"][-1])
+    t = time.perf_counter()
+    sym, st = oracle.decode_tensor(blob, desc, freq, n)
+    assert (st == 0).all()
+    cols = int(spec["cols"])
+    rows = -(-n // cols)
+    full = np.zeros(rows * cols, np.uint8)
+    full[:n] = sym
+    bits = oracle.dequant_tensor(full, rows, cols, spec["kind"], spec["scales"][:rows])[:n]
+    return bits, time.perf_counter() - t, n
+
+
 def compressed_layers_row_aligned(args, E, synth, dev, torch):
     """The 80 layers encoded on the device with chunks of whole rows (8 rows
     of 8192 columns, 2 rows of 28672), as the fused kernel needs."""
     nthreads = args.threads or synth.default_threads()
     t0 = time.time()
-    layers, out_elems, tens = [], 0, None
+    layers, out_elems, tens, meta0 = [], 0, None, None
     for layer in range(args.layers):
         specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
         for sp in specs:
@@ -574,12 +596,14 @@ def compressed_layers_row_aligned(args, E, synth, dev, torch):
         sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)
         layers.append((p, b.blob.clone(), sc))
         out_elems, tens = b.out_elems, b.tensors
+        if layer == 0:
+            meta0 = (b.chunks, b.freq, [dict(sp, symbols=None) for sp in specs])
         del ds, b
         if layer % 10 == 0 or layer == args.layers - 1:
             log(f"layer {layer} encoded on the device, row-aligned chunks ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return layers, out_elems, tens
+    return layers, out_elems, tens, meta0
 
 
 def bench_fused(args):
@@ -597,7 +621,7 @@ def bench_fused(args):
     E.lib()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    layers, out_elems, tens = compressed_layers_row_aligned(args, E, synth, dev, torch)
+    layers, out_elems, tens, meta0 = compressed_layers_row_aligned(args, E, synth, dev, torch)
     names = [n for n, _, _ in synth.LLAMA2_70B_LAYER]
     views = [(names[t], int(tens["rows"][t]), int(tens["cols"][t]), int(tens["out_elem_offset"][t]))
              for t in range(len(tens))]
@@ -659,6 +683,9 @@ def bench_fused(args):
         log(f"fused m={m}: " + ", ".join(f"{k} {v:.3f}" for k, v in row.items() if k != "m"))
         results.append(row)
         del X, H, xs, ys, yb
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = fused_cpu_baseline(E, layers[0], meta0, views, stream, torch, dev)
     r0 = results[0]
     # algorithmic bytes of one fused launch: compressed layer + scales + the
     # activations read + the fp32 results written
@@ -696,12 +723,52 @@ def bench_fused(args):
             "frac": gbs / HBM_PEAK_GBS,
             "traffic": None,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
 
 LMHEAD_METRIC = "decoded params/s for the LLaMA-2-70B output projection (32,000 x 8,192) decoded alone"
+
+
+def fused_cpu_baseline(E, layer0, meta0, views, stream, torch, dev, m=16, n_tensors=4):
+    """The oracle (single-threaded C decode + dequant, then a one-thread fp64
+    product) for the first n_tensors tensors of layer 0 and m = 16
+    activation rows, timed on this host; the GPU's fused results for the
+    same tensors must lie within the fp32 accumulation bound of it."""
+    from threadpoolctl import threadpool_limits
+    p0, blob_d, sc_d = layer0
+    chunks, freq, specs = meta0
+    blob = blob_d.cpu().numpy()
+    gen = torch.Generator().manual_seed(1)
+    X = (torch.randn(m, 8192, generator=gen) * 0.5).to(torch.bfloat16)
+    H = (torch.randn(m, 28672, generator=gen) * 0.5).to(torch.bfloat16)
+    xs = [(H if n == "down" else X).to(dev) for n, r, c, o in views]
+    ys = [torch.empty(m, r, dtype=torch.float32, device=dev) for n, r, c, o in views]
+    E.decode_gemm(p0, blob_d, sc_d, xs, ys, None, stream)
+    torch.cuda.synchronize()
+    xf = X.float().numpy().astype(np.float64)
+    spent, params, ok = 0.0, 0, True
+    with threadpool_limits(1):
+        for t in range(n_tensors):
+            sp = specs[t]
+            ch = chunks[chunks["tensor"] == t]
+            bits, dt, n = oracle_tensor_sample(blob, ch, freq[t], sp, len(ch))
+            t0 = time.perf_counter()
+            w = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            w = w.reshape(sp["rows"], sp["cols"])
+            ref = xf @ w.T
+            spent += dt + time.perf_counter() - t0
+            bound = sp["cols"] * 2.0 ** -24 * (np.abs(xf) @ np.abs(w).T)
+            ok &= bool((np.abs(ys[t].cpu().numpy() - ref) <= bound).all())
+            params += n
+    log(f"cpu oracle, fused sample: {params} weights x {m} rows in {spent:.2f}s "
+        f"({params / spent / 1e6:.1f} M weights/s); GPU within bound: {ok}")
+    if not ok:
+        raise SystemExit("fused results differ from the oracle beyond the accumulation bound")
+    return {"value": params / spent, "unit": "weights/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, first {n_tensors} tensors ({params} weights), m = {m}: "
+                      "single-threaded C oracle decode + dequant, fp64 product on one thread"}
 
 
 def bench_lm_head(args):
@@ -732,6 +799,8 @@ def bench_lm_head(args):
         p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
         conts[C] = (p, b.blob.clone(), torch.from_numpy(specs[0]["scales"]).to(dev),
                     int(b.blob.numel()), int(p.n_chunks))
+        if C == 32768:
+            meta = (b.chunks, b.freq[0], dict(specs[0], symbols=None))
         rows, cols = specs[0]["rows"], specs[0]["cols"]
         del ds, b
     torch.cuda.synchronize()
@@ -778,6 +847,21 @@ def bench_lm_head(args):
         u_us = timed(unfused, reps)
         logits.append({"m": m, "fused_us": f_us, "unfused_us": u_us, "speedup": u_us / f_us})
         log(f"lm head logits m={m}: fused {f_us:.1f} us, decode + GEMM {u_us:.1f} us")
+    cpu = None
+    if not args.no_cpu_baseline:
+        p, blob, sc, nbytes, nch = conts[32768]
+        E.decode(p, blob, out, E.OUT_BF16, sc, None, stream)
+        torch.cuda.synchronize()
+        ch, freq, spec = meta
+        bits, dt, n_s = oracle_tensor_sample(blob.cpu().numpy(), ch, freq, spec, 4000)
+        ok = bool(np.array_equal(out[:n_s].cpu().numpy().view(np.uint16), bits))
+        log(f"cpu oracle, lm head sample: {n_s} params in {dt:.2f}s ({n_s / dt / 1e6:.1f} M "
+            f"params/s); matches GPU: {ok}")
+        if not ok:
+            raise SystemExit("LM-head decode differs from the oracle on the CPU-baseline sample")
+        cpu = {"value": n_s / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+               "sample": f"first 4,000 chunks ({n_s} params) of the 32,768-symbol container: "
+                         "single-threaded C oracle decode + dequant + RNE bf16"}
     d0 = dec[32768]
     rec = {
         "metric": LMHEAD_METRIC,
@@ -807,7 +891,7 @@ def bench_lm_head(args):
             "frac": d0["alg_gbs"] / HBM_PEAK_GBS,
             "traffic": None,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
@@ -843,10 +927,13 @@ def bench_adaptive(args):
 
     t0 = time.time()
     lay = {True: [], False: []}
+    sample = None
     for layer in range(args.layers):
         specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
         for adaptive in (True, False):
             lay[adaptive].append(build(specs, adaptive))
+        if layer == 0 and not args.no_cpu_baseline:
+            sample = (E.encode_batch_adaptive(specs[:3], nthreads), specs[:3])
         if layer % 10 == 0 or layer == args.layers - 1:
             log(f"adaptive: layer {layer} encoded both ways ({time.time() - t0:.1f}s)")
     params = lay[True][0][4]
@@ -884,6 +971,9 @@ def bench_adaptive(args):
             "bits_per_param": 8.0 * nbytes / params, "alg_gbs": alg / (us / 1e6) / 1e9}
         log(f"adaptive={adaptive}: {ms:.3f} ms/step, {us:.1f} us/layer, "
             f"{8.0 * nbytes / params:.4f} bits/param")
+    cpu = None
+    if sample is not None:
+        cpu = adaptive_cpu_baseline(E, sample, lay[True][0], out, stream, torch)
     for k in lay:
         lay[k].clear()
     torch.cuda.empty_cache()
@@ -927,9 +1017,42 @@ def bench_adaptive(args):
             "frac": r0["alg_gbs"] / HBM_PEAK_GBS,
             "traffic": None,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def adaptive_cpu_baseline(E, sample, layer0, out, stream, torch):
+    """The oracle's per-chunk-table decode + dequant of layer 0's first three
+    tensors (from the library's container, which the tests prove equal to
+    the oracle's), timed on this host and compared with the GPU's bf16."""
+    import oracle
+    b, specs = sample
+    p0, blob_d, sc_d, _, _ = layer0
+    E.decode(p0, blob_d, out, E.OUT_BF16, sc_d, None, stream)
+    torch.cuda.synchronize()
+    n = sum(s_["rows"] * s_["cols"] for s_ in specs)
+    gpu = out[:n].cpu().numpy().view(np.uint16)
+    t = time.perf_counter()
+    parts = []
+    for ti, sp in enumerate(specs):
+        sym = np.zeros(sp["rows"] * sp["cols"], np.uint8)
+        for ch in b.chunks[b.chunks["tensor"] == ti]:
+            s_, st = oracle.decode_adaptive_chunk(b.blob, int(ch["byte_offset"]),
+                                                  int(ch["n_symbols"]), int(ch["n_words"]))
+            assert st == 0
+            e0 = int(ch["elem_offset"])
+            sym[e0:e0 + s_.size] = s_
+        parts.append(oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"]))
+    dt = time.perf_counter() - t
+    ok = bool(np.array_equal(np.concatenate(parts), gpu))
+    log(f"cpu oracle, per-chunk tables: {n} params in {dt:.2f}s ({n / dt / 1e6:.1f} M params/s); "
+        f"matches GPU: {ok}")
+    if not ok:
+        raise SystemExit("per-chunk-table decode differs from the oracle on the CPU-baseline sample")
+    return {"value": n / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, first 3 tensors ({n} params): single-threaded C oracle "
+                      "per-chunk-table decode + dequant + RNE bf16"}
 
 
 if __name__ == "__main__":
