@@ -43,6 +43,10 @@ CHUNK_DESC = np.dtype([("tensor", "<u4"), ("n_symbols", "<u4"), ("n_words", "<u4
 assert TENSOR_DESC.itemsize == 40 and CHUNK_DESC.itemsize == 32
 # entq_gemm_io (include/entq.h): device pointers as integers
 GEMM_IO = np.dtype([("x", "<u8"), ("ldx", "<u8"), ("y", "<u8"), ("ldy", "<u8")])
+# entq_count_job / entq_pack_job (include/entq.h): device pointers as integers
+COUNT_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("counts", "<u8")])
+PACK_JOB = np.dtype([("scratch", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
+                     ("reserved", "<u4"), ("n_words", "<u8"), ("offsets", "<u8")])
 # entq_encode_job (include/entq.h): device pointers as integers
 ENCODE_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
                        ("reserved", "<u4"), ("freq", "<u8"), ("scratch", "<u8"),
@@ -96,6 +100,8 @@ def lib():
             "entq_encode_tensor_adaptive": (c.c_int, [vp, u64, c.c_uint32, c.c_uint32, u64, vp,
                                                       u64, vp, vp, c.c_int]),
             "entq_encode_bound_adaptive": (u64, [u64, c.c_uint32]),
+            "entq_count_symbols_device_batch": (c.c_int, [vp, c.c_int, vp]),
+            "entq_pack_device_batch": (c.c_int, [vp, c.c_int, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -111,7 +117,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_count_symbols_device", "entq_encode_device_scratch_bytes", "entq_region_bytes",
             "entq_encode_device", "entq_pack_device", "entq_region_offsets_device",
             "entq_encode_device_batch", "entq_decode_gemm", "entq_plan_adaptive",
-            "entq_encode_tensor_adaptive", "entq_encode_bound_adaptive"]
+            "entq_encode_tensor_adaptive", "entq_encode_bound_adaptive",
+            "entq_count_symbols_device_batch", "entq_pack_device_batch"]
 
 
 def _str(status: int) -> str:
@@ -430,6 +437,27 @@ def pack_device(scratch, n: int, chunk_symbols: int, n_words, offsets, blob, str
                                   _ptr(blob) or None, _stream(stream)), "entq_pack_device")
 
 
+def count_symbols_device_batch(jobs, stream=None):
+    """jobs: list of (symbols, counts) device tensors (counts int64 [256],
+    zeroed by the caller); one launch per 16 arrays."""
+    arr = np.zeros(len(jobs), COUNT_JOB)
+    for i, (sym, counts) in enumerate(jobs):
+        arr[i] = (_ptr(sym), sym.numel(), _ptr(counts))
+    _check(lib().entq_count_symbols_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                                 _stream(stream)),
+           "entq_count_symbols_device_batch")
+
+
+def pack_device_batch(jobs, blob, stream=None):
+    """jobs: list of (scratch, n, chunk_symbols, n_words, offsets) as for
+    pack_device; all write into blob; one launch per 16 tensors."""
+    arr = np.zeros(len(jobs), PACK_JOB)
+    for i, (scratch, n, C, nw, offs) in enumerate(jobs):
+        arr[i] = (_ptr(scratch), int(n), int(C), 0, _ptr(nw), _ptr(offs))
+    _check(lib().entq_pack_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                        _ptr(blob), _stream(stream)), "entq_pack_device_batch")
+
+
 def encode_device_batch(jobs, stream=None):
     """jobs: list of (symbols, chunk_symbols, freq, scratch, n_words) with
     device tensors (freq: device uint16/int16 [256]); one launch per 16
@@ -507,8 +535,9 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         events.append((name, a, b))
 
     with torch.cuda.stream(s):
-        for t, sp in enumerate(specs):
-            timed("count", lambda: count_symbols_device(sp["symbols"], counts[t], s))
+        cjobs = [(sp["symbols"], counts[t]) for t, sp in enumerate(specs) if shapes[t][3]]
+        if cjobs:
+            timed("count", lambda: count_symbols_device_batch(cjobs, s))
         s.synchronize()
         host_counts = counts.cpu().numpy().view(np.uint64)
         freqs = np.zeros((max(T, 1), 256), np.uint16)
@@ -530,13 +559,15 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         if k_all:
             timed("offsets", lambda: region_offsets_device(nw_d[:k_all], offs_d[:k_all], end_d,
                                                            0, s))
-        k0 = 0
+        pjobs, k0 = [], 0
         for t, sp in enumerate(specs):
             rows, cols, C, n, k = shapes[t]
             if k:
-                timed("pack", lambda: pack_device(scratch[scr_off[t]:scr_off[t + 1]], n, C,
-                                                  nw_d[k0:k0 + k], offs_d[k0:k0 + k], blob, s))
+                pjobs.append((scratch[scr_off[t]:scr_off[t + 1]], n, C, nw_d[k0:k0 + k],
+                              offs_d[k0:k0 + k]))
             k0 += k
+        if pjobs:
+            timed("pack", lambda: pack_device_batch(pjobs, blob, s))
         s.synchronize()
         nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
         offs = offs_d[:k_all].cpu().numpy().view(np.uint64)

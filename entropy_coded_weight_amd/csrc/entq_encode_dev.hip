@@ -253,12 +253,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_chunks(EncJobs jobs, EncFr
 // of the chunk's word area), zeros up to the next 16-byte boundary. The
 // region is written one dword per thread and pass; when the words start at
 // an odd word index, each dword is funnelled from two source dwords.
-__global__ __launch_bounds__(256) void pack_chunks(const uint8_t *__restrict__ scratch,
-                                                   uint32_t chunk_symbols,
-                                                   const uint32_t *__restrict__ n_words,
-                                                   const uint64_t *__restrict__ offsets,
-                                                   uint8_t *__restrict__ blob) {
-    const uint64_t k = blockIdx.x;
+__device__ __forceinline__ void pack_one(const uint8_t *__restrict__ scratch,
+                                         uint32_t chunk_symbols,
+                                         const uint32_t *__restrict__ n_words,
+                                         const uint64_t *__restrict__ offsets,
+                                         uint8_t *__restrict__ blob, uint64_t k) {
     const uint32_t nw = n_words[k];
     if (nw > chunk_symbols) return;  // a chunk the encoder rejected (frequency-0 symbol)
     const uint8_t *area = scratch + k * scratch_stride(chunk_symbols);
@@ -291,6 +290,35 @@ __global__ __launch_bounds__(256) void pack_chunks(const uint8_t *__restrict__ s
             D[d] = v;
         }
     }
+}
+
+__global__ __launch_bounds__(256) void pack_chunks(const uint8_t *__restrict__ scratch,
+                                                   uint32_t chunk_symbols,
+                                                   const uint32_t *__restrict__ n_words,
+                                                   const uint64_t *__restrict__ offsets,
+                                                   uint8_t *__restrict__ blob) {
+    pack_one(scratch, chunk_symbols, n_words, offsets, blob, blockIdx.x);
+}
+
+// Several tensors in one launch (one blob): job j packs its chunks with
+// workgroups first_block .. first_block + n_chunks - 1.
+struct PackJob {
+    const uint8_t *scratch;
+    const uint32_t *n_words;
+    const uint64_t *offsets;
+    uint32_t chunk_symbols, first_block;
+};
+struct PackJobs {
+    PackJob job[kMaxEncJobs];
+    uint32_t n_jobs;
+};
+
+__global__ __launch_bounds__(256) void pack_chunks_batch(PackJobs jobs, uint8_t *__restrict__ blob) {
+    uint32_t j = 0;
+    while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
+    const PackJob &pj = jobs.job[j];
+    pack_one(pj.scratch, pj.chunk_symbols, pj.n_words, pj.offsets, blob,
+             blockIdx.x - pj.first_block);
 }
 
 // Region offsets: offsets[k] = base + the region bytes of chunks 0..k-1
@@ -340,10 +368,12 @@ __global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *_
 constexpr int kCountThreads = 512;
 constexpr int kCountBytesPerLane = 64;
 
-__global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__restrict__ symbols,
-                                                             uint64_t n,
-                                                             unsigned long long *__restrict__ counts) {
-    __shared__ uint32_t H[256 * 64];
+// The histogram of one workgroup's share of a byte array: block bid of
+// nblocks takes lane rounds bid * kCountThreads + t, + nblocks *
+// kCountThreads, ...; block 0 also takes the last n % 64 bytes.
+__device__ __forceinline__ void count_share(uint32_t *H, const uint8_t *__restrict__ symbols,
+                                            uint64_t n, unsigned long long *__restrict__ counts,
+                                            uint64_t bid, uint64_t nblocks) {
     const uint32_t lane_off = (threadIdx.x & 63u) * 4u;  // byte offset of the lane's column
     for (uint32_t i = threadIdx.x; i < 256u * 64u / 4u; i += kCountThreads)
         reinterpret_cast<uint4 *>(H)[i] = make_uint4(0, 0, 0, 0);
@@ -357,8 +387,8 @@ __global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__re
         for (int c = 0; c < 4; ++c) add_byte((u >> (8 * c)) & 0xFFu);
     };
     const uint64_t n_full = n / kCountBytesPerLane;  // whole 64-byte lane rounds
-    const uint64_t stride = (uint64_t)gridDim.x * kCountThreads;
-    for (uint64_t r = (uint64_t)blockIdx.x * kCountThreads + threadIdx.x; r < n_full; r += stride) {
+    const uint64_t stride = nblocks * kCountThreads;
+    for (uint64_t r = bid * kCountThreads + threadIdx.x; r < n_full; r += stride) {
         const uint4 *src = reinterpret_cast<const uint4 *>(symbols + r * kCountBytesPerLane);
         uint4 v[4];
         for (int q = 0; q < 4; ++q) v[q] = src[q];
@@ -369,8 +399,8 @@ __global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__re
             add4(v[q].w);
         }
     }
-    // the last n % 64 bytes, one per thread of workgroup 0
-    if (blockIdx.x == 0) {
+    // the last n % 64 bytes, one per thread of the first workgroup
+    if (bid == 0) {
         const uint64_t tail = n_full * kCountBytesPerLane + threadIdx.x;
         if (tail < n) add_byte(symbols[tail]);
     }
@@ -381,6 +411,45 @@ __global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__re
             sum += H[threadIdx.x * 64u + ((j + threadIdx.x) & 63u)];
         if (sum) atomicAdd(&counts[threadIdx.x], (unsigned long long)sum);
     }
+}
+
+__global__ __launch_bounds__(kCountThreads) void count_bytes(const uint8_t *__restrict__ symbols,
+                                                             uint64_t n,
+                                                             unsigned long long *__restrict__ counts) {
+    __shared__ uint32_t H[256 * 64];
+    count_share(H, symbols, n, counts, blockIdx.x, gridDim.x);
+}
+
+// Several arrays in one launch: job j owns workgroups first_block ..
+// first_block + blocks - 1.
+struct CountJob {
+    const uint8_t *symbols;
+    unsigned long long *counts;
+    uint64_t n;
+    uint32_t first_block, blocks;
+};
+struct CountJobs {
+    CountJob job[kMaxEncJobs];
+    uint32_t n_jobs;
+};
+
+__global__ __launch_bounds__(kCountThreads) void count_bytes_batch(CountJobs jobs) {
+    __shared__ uint32_t H[256 * 64];
+    uint32_t j = 0;
+    while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
+    const CountJob &cj = jobs.job[j];
+    count_share(H, cj.symbols, cj.n, cj.counts, blockIdx.x - cj.first_block, cj.blocks);
+}
+
+// Workgroups for counting n bytes: two per CU on 256 CUs at most, fewer for
+// small inputs (at least 16 lane rounds per thread); a lane column counts at
+// most n / (64 blocks) bytes, more blocks keep that below 2^32.
+inline uint64_t count_blocks(uint64_t n) {
+    const uint64_t rounds = n / kCountBytesPerLane;
+    uint64_t blocks = (rounds + 16ull * kCountThreads - 1) / (16ull * kCountThreads);
+    if (blocks > 512) blocks = 512;
+    const uint64_t min_blocks = (n >> 37) + 1;
+    return blocks < min_blocks ? min_blocks : blocks;
 }
 
 }  // namespace
@@ -394,19 +463,83 @@ entq_status entq_count_symbols_device(const uint8_t *d_symbols, uint64_t n, uint
     if (n && (uintptr_t)d_symbols % 16) return ENTQ_EALIGN;
     if ((uintptr_t)d_counts % 8) return ENTQ_EALIGN;
     if (n == 0) return ENTQ_OK;
-    // Two workgroups per CU on 256 CUs, fewer for small inputs (at least 16
-    // lane rounds per thread). A lane column counts at most n / (64 blocks)
-    // bytes; more blocks keep that below 2^32.
-    const uint64_t rounds = n / entq::kCountBytesPerLane;
-    uint64_t blocks = (rounds + 16ull * entq::kCountThreads - 1) / (16ull * entq::kCountThreads);
-    if (blocks > 512) blocks = 512;
-    const uint64_t min_blocks = (n >> 37) + 1;
-    if (blocks < min_blocks) blocks = min_blocks;
+    const uint64_t blocks = entq::count_blocks(n);
     if (blocks > 0x7FFFFFFF) return ENTQ_EINVAL;
     hipLaunchKernelGGL(entq::count_bytes, dim3((unsigned)blocks), dim3(entq::kCountThreads), 0,
                        (hipStream_t)stream, d_symbols, n,
                        reinterpret_cast<unsigned long long *>(d_counts));
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_count_symbols_device_batch(const entq_count_job *jobs, int n_jobs,
+                                            void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    for (int j = 0; j < n_jobs; ++j) {
+        if (!jobs[j].d_counts || (jobs[j].n_symbols && !jobs[j].d_symbols)) return ENTQ_EINVAL;
+        if ((jobs[j].n_symbols && (uintptr_t)jobs[j].d_symbols % 16) ||
+            (uintptr_t)jobs[j].d_counts % 8)
+            return ENTQ_EALIGN;
+    }
+    entq::CountJobs batch = {};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::count_bytes_batch, dim3((unsigned)blocks),
+                           dim3(entq::kCountThreads), 0, (hipStream_t)stream, batch);
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        if (jobs[j].n_symbols == 0) continue;
+        const uint64_t b = entq::count_blocks(jobs[j].n_symbols);
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + b > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {jobs[j].d_symbols,
+                                     reinterpret_cast<unsigned long long *>(jobs[j].d_counts),
+                                     jobs[j].n_symbols, (uint32_t)blocks, (uint32_t)b};
+        blocks += b;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_pack_device_batch(const entq_pack_job *jobs, int n_jobs, void *d_blob,
+                                   void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    if (n_jobs && !d_blob) return ENTQ_EINVAL;
+    if ((uintptr_t)d_blob % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_pack_job &pj = jobs[j];
+        const uint32_t C = pj.chunk_symbols;
+        if (C == 0 || C % entq::kLanes || C > entq::kMaxChunkSymbols) return ENTQ_EINVAL;
+        if (pj.n_symbols == 0) continue;
+        if (!pj.d_scratch || !pj.d_n_words || !pj.d_byte_offsets) return ENTQ_EINVAL;
+        if ((uintptr_t)pj.d_scratch % 16 || (uintptr_t)pj.d_n_words % 4 ||
+            (uintptr_t)pj.d_byte_offsets % 8)
+            return ENTQ_EALIGN;
+        if ((pj.n_symbols + C - 1) / C > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    }
+    entq::PackJobs batch = {};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::pack_chunks_batch, dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, batch, static_cast<uint8_t *>(d_blob));
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_pack_job &pj = jobs[j];
+        if (pj.n_symbols == 0) continue;
+        const uint64_t k = (pj.n_symbols + pj.chunk_symbols - 1) / pj.chunk_symbols;
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + k > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {static_cast<const uint8_t *>(pj.d_scratch), pj.d_n_words,
+                                     pj.d_byte_offsets, pj.chunk_symbols, (uint32_t)blocks};
+        blocks += k;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
 }
 
 uint64_t entq_region_bytes(uint32_t n_words) {

@@ -330,6 +330,32 @@ typedef struct {
  * 0xFFFFFFFF instead of an error code. Empty tensors are skipped. */
 entq_status entq_encode_device_batch(const entq_encode_job *jobs, int n_jobs, void *stream);
 
+/* Byte counts of several device arrays in one launch (one per 16 arrays):
+ * job j adds the counts of d_symbols[0 .. n_symbols) (16-byte aligned) to
+ * d_counts[256] (device u64, 8-byte aligned, zeroed by the caller). */
+typedef struct {
+    const uint8_t *d_symbols;
+    uint64_t n_symbols;
+    uint64_t *d_counts;
+} entq_count_job;
+
+entq_status entq_count_symbols_device_batch(const entq_count_job *jobs, int n_jobs,
+                                            void *stream);
+
+/* entq_pack_device for several tensors writing into one blob, in one launch
+ * per 16 tensors; each job as that call's arguments (device pointers). */
+typedef struct {
+    const void *d_scratch;
+    uint64_t n_symbols;
+    uint32_t chunk_symbols;
+    uint32_t reserved;
+    const uint32_t *d_n_words;
+    const uint64_t *d_byte_offsets;
+} entq_pack_job;
+
+entq_status entq_pack_device_batch(const entq_pack_job *jobs, int n_jobs, void *d_blob,
+                                   void *stream);
+
 /* Writes the regions of an encoded tensor into d_blob (device, 16-byte
  * aligned): region k (64 states, the chunk's words in decoding order, zero
  * padding) at byte d_byte_offsets[k] (device u64, multiples of 16, regions
