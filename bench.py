@@ -67,6 +67,8 @@ def parse():
                          "line's (overlap default 2048,256,16; fused default 16,4,1,32,64)")
     ap.add_argument("--encode-layers", type=int, default=4,
                     help="resident layers of source codes the encode steps cycle through")
+    ap.add_argument("--split-chunk-rows", type=int, default=1,
+                    help="fused: rows per chunk of the lone BF16 8192 x 8192 split case")
     ap.add_argument("--row-chunk-max", type=int, default=32768,
                     help="fused: a chunk holds as many whole rows as fit in this many symbols")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -683,6 +685,7 @@ def bench_fused(args):
         log(f"fused m={m}: " + ", ".join(f"{k} {v:.3f}" for k, v in row.items() if k != "m"))
         results.append(row)
         del X, H, xs, ys, yb
+    split = fused_bf16_split_case(E, synth, torch, dev, stream, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = fused_cpu_baseline(E, layers[0], meta0, views, stream, torch, dev)
@@ -714,6 +717,7 @@ def bench_fused(args):
             "compressed_bytes_per_layer": blob_mean,
             "chunking": f"whole rows, at most {args.row_chunk_max} symbols per chunk",
             "results": results,
+            "bf16_split_8192x8192": split,
         },
         "roofline": {
             "bound": "hbm",
@@ -729,6 +733,57 @@ def bench_fused(args):
 
 
 LMHEAD_METRIC = "decoded params/s for the LLaMA-2-70B output projection (32,000 x 8,192) decoded alone"
+
+
+def fused_bf16_split_case(E, synth, torch, dev, stream, args, m=16, chunk_rows=None):
+    """BF16 weights 8192 x 8192 stored as a coded exponent stream + raw
+    sign+mantissa bytes (chunk_rows-row chunks: a tensor on its own needs
+    enough chunks to fill the GPU, 16 per fused workgroup), m = 16
+    activation rows: fused
+    (entq_decode_gemm_bf16_split) against entq_decode_bf16_split + torch.mm,
+    and the split decode alone; medians of per-launch HIP events."""
+    rows = cols = 8192
+    w = synth.bf16_weights(rows, cols)[0]["bf16"]
+    e, sm = E.bf16_split(w)
+    chunk_rows = chunk_rows or args.split_chunk_rows
+    b = E.encode_batch([dict(kind=E.KIND_BF16EXP, rows=rows, cols=cols, symbols=e,
+                             chunk_symbols=cols * chunk_rows)])
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).to(dev)
+    smd = torch.from_numpy(sm).to(dev)
+    out = torch.empty(rows * cols, dtype=torch.int16, device=dev)
+    X = (torch.randn(m, cols, generator=torch.Generator().manual_seed(2)) * 0.5).to(
+        torch.bfloat16).to(dev)
+    Y = torch.empty(m, rows, dtype=torch.float32, device=dev)
+    Yb = torch.empty(m, rows, dtype=torch.bfloat16, device=dev)
+    W = out.view(torch.bfloat16).view(rows, cols)
+
+    def med(fn, reps=max(args.steps, 20)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, z in ev:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(z) for a, z in ev])) * 1e3
+
+    def unfused():
+        E.decode_bf16_split(p, blob, smd, out, None, stream)
+        torch.mm(X, W.t(), out=Yb)
+
+    r = {"m": m, "chunk_rows": chunk_rows, "compressed_exponent_bytes": int(b.blob.size),
+         "fused_us": med(lambda: E.decode_gemm_bf16_split(p, blob, smd, [X], [Y], None, stream)),
+         "unfused_us": med(unfused),
+         "split_decode_only_us": med(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))}
+    r["speedup"] = r["unfused_us"] / r["fused_us"]
+    log(f"bf16 split 8192x8192 m={m}: fused {r['fused_us']:.1f} us, split decode + GEMM "
+        f"{r['unfused_us']:.1f} us, split decode alone {r['split_decode_only_us']:.1f} us")
+    p.close()
+    return r
 
 
 def fused_cpu_baseline(E, layer0, meta0, views, stream, torch, dev, m=16, n_tensors=4):

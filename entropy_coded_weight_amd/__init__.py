@@ -102,6 +102,7 @@ def lib():
             "entq_encode_bound_adaptive": (u64, [u64, c.c_uint32]),
             "entq_count_symbols_device_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_pack_device_batch": (c.c_int, [vp, c.c_int, vp, vp]),
+            "entq_decode_gemm_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -118,7 +119,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_encode_device", "entq_pack_device", "entq_region_offsets_device",
             "entq_encode_device_batch", "entq_decode_gemm", "entq_plan_adaptive",
             "entq_encode_tensor_adaptive", "entq_encode_bound_adaptive",
-            "entq_count_symbols_device_batch", "entq_pack_device_batch"]
+            "entq_count_symbols_device_batch", "entq_pack_device_batch",
+            "entq_decode_gemm_bf16_split"]
 
 
 def _str(status: int) -> str:
@@ -237,11 +239,7 @@ def decode(p: Plan, compressed, out, out_kind: int, scales=None, chunk_status=No
     _check(st, "entq_decode")
 
 
-def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
-    """Y_t = X_t . W_t^T for every tensor t of the plan, W_t the bf16 weights
-    the bf16 decode would write, without writing them: xs[t] is a device
-    bfloat16 tensor [m, ldx >= cols] (m <= 64, the same m for all), ys[t] a
-    device float32 tensor [m, ldy >= rows]."""
+def _gemm_io(p: Plan, xs, ys):
     import torch
     assert len(xs) == len(ys) == p.n_tensors
     m = xs[0].shape[0] if xs else 0
@@ -251,10 +249,30 @@ def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=N
         assert x.dim() == 2 and y.dim() == 2 and x.shape[0] == m and y.shape[0] == m
         assert x.stride(1) == 1 and y.stride(1) == 1
         io[t] = (_ptr(x), x.stride(0), _ptr(y), y.stride(0))
+    return io, m
+
+
+def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
+    """Y_t = X_t . W_t^T for every tensor t of the plan, W_t the bf16 weights
+    the bf16 decode would write, without writing them: xs[t] is a device
+    bfloat16 tensor [m, ldx >= cols] (m <= 64, the same m for all), ys[t] a
+    device float32 tensor [m, ldy >= rows]."""
+    io, m = _gemm_io(p, xs, ys)
     st = lib().entq_decode_gemm(p.handle, _ptr(compressed), _ptr(scales) or None,
                                 _ptr(io) if len(xs) else None, int(m),
                                 _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm")
+
+
+def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=None,
+                           stream=None):
+    """decode_gemm for BF16 weights given as a coded exponent stream plus raw
+    sign+mantissa bytes (as decode_bf16_split takes them)."""
+    io, m = _gemm_io(p, xs, ys)
+    st = lib().entq_decode_gemm_bf16_split(p.handle, _ptr(exp_stream), _ptr(signmant),
+                                           _ptr(io) if len(xs) else None, int(m),
+                                           _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_gemm_bf16_split")
 
 
 def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):

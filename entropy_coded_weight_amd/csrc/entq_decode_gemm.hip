@@ -59,11 +59,14 @@ struct GemmArgs {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-template <int MT>  // groups of 16 activation rows
+// MT: groups of 16 activation rows. SPLIT: the weights are BF16 rebuilt from
+// a coded exponent stream and raw sign+mantissa bytes (no scales).
+template <int MT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restrict__ tables,
                                                         const DevChunk *__restrict__ chunks,
                                                         const uint8_t *__restrict__ blob,
                                                         const float *__restrict__ scales,
+                                                        const uint8_t *__restrict__ signmant,
                                                         int32_t *__restrict__ status,
                                                         GemmArgs args) {
     __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kWaves][kRingWords];
@@ -124,7 +127,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
 
     for (uint32_t r = 0; r < rows_per_chunk; ++r) {
         const bool live = r < my_rows;  // uniform per wave
-        const float scale = live ? scales[ch.scale_row + r] : 0.f;
+        const float scale = (live && !SPLIT) ? scales[ch.scale_row + r] : 0.f;
+        // sign+mantissa bytes of this lane's four columns of each block
+        const uint8_t *sm_row = signmant + ch.out_elem + (uint64_t)r * cols + 4u * lane;
         float4_t acc[MT];
 #pragma unroll
         for (int g = 0; g < MT; ++g) acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -134,7 +139,10 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
             if (live) {
                 if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
             }
-            // this block's activation slices (in flight while the block decodes)
+            // this block's activation slices and sign+mantissa bytes (in flight
+            // while the block decodes)
+            uint32_t sm4 = 0;
+            if (SPLIT && live) sm4 = *reinterpret_cast<const uint32_t *>(sm_row + kb * kBlockSyms);
             uint2 a[MT];
 #pragma unroll
             for (int g = 0; g < MT; ++g) {
@@ -147,10 +155,16 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
 #pragma unroll
                 for (uint32_t t = 0; t < kBlockSteps; ++t)
                     stream_step<false>(x, s.p, s.ring, ring_mask, T, row_tile + 64u * t, lane, true);
-                // lane k: columns 4k .. 4k+3 of the block, dequantised in place
+                // lane k: columns 4k .. 4k+3 of the block, made bf16 in place
                 const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
-                const uint2 w = gt.e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
-                                        : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
+                uint2 w;
+                if (SPLIT)  // per 16-bit half: exponent << 8 | sign+mantissa
+                    w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
+                                   merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
+                else if (gt.e4m3)
+                    w = make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale));
+                else
+                    w = make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
                 *reinterpret_cast<uint2 *>(row_tile + 4u * lane) = w;
             } else {
                 *reinterpret_cast<uint2 *>(row_tile + 4u * lane) = make_uint2(0, 0);
@@ -195,31 +209,43 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     wait_vm<0>();  // no global->LDS load may outlive the workgroup
 }
 
+template <bool SPLIT>
+void launch_groups(int groups_m, dim3 grid, hipStream_t st, const entq_plan_t *plan,
+                   const uint8_t *blob, const float *scales, const uint8_t *signmant,
+                   int32_t *status, const GemmArgs &args) {
+    const dim3 block(kThreads);
+    if (groups_m == 1)
+        hipLaunchKernelGGL((decode_gemm<1, SPLIT>), grid, block, 0, st, plan->d_tables,
+                           plan->d_chunks, blob, scales, signmant, status, args);
+    else if (groups_m == 2)
+        hipLaunchKernelGGL((decode_gemm<2, SPLIT>), grid, block, 0, st, plan->d_tables,
+                           plan->d_chunks, blob, scales, signmant, status, args);
+    else if (groups_m == 3)
+        hipLaunchKernelGGL((decode_gemm<3, SPLIT>), grid, block, 0, st, plan->d_tables,
+                           plan->d_chunks, blob, scales, signmant, status, args);
+    else
+        hipLaunchKernelGGL((decode_gemm<4, SPLIT>), grid, block, 0, st, plan->d_tables,
+                           plan->d_chunks, blob, scales, signmant, status, args);
+}
+
 }  // namespace
 
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
-                       const entq_gemm_io *io, int m, int32_t *status, void *stream) {
+                       const uint8_t *signmant, const entq_gemm_io *io, int m, int32_t *status,
+                       void *stream) {
     GemmArgs args = {};
     args.m = (uint32_t)m;
     uint64_t blocks = 0;
     const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
     auto flush = [&]() -> int {
         if (args.n_tensors == 0) return ENTQ_OK;
-        const dim3 grid((unsigned)blocks), block(kThreads);
         const uint8_t *b = static_cast<const uint8_t *>(blob);
-        hipStream_t st = (hipStream_t)stream;
-        if (groups_m == 1)
-            hipLaunchKernelGGL(decode_gemm<1>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
-                               b, scales, status, args);
-        else if (groups_m == 2)
-            hipLaunchKernelGGL(decode_gemm<2>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
-                               b, scales, status, args);
-        else if (groups_m == 3)
-            hipLaunchKernelGGL(decode_gemm<3>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
-                               b, scales, status, args);
+        if (signmant)
+            launch_groups<true>(groups_m, dim3((unsigned)blocks), (hipStream_t)stream, plan, b,
+                                scales, signmant, status, args);
         else
-            hipLaunchKernelGGL(decode_gemm<4>, grid, block, 0, st, plan->d_tables, plan->d_chunks,
-                               b, scales, status, args);
+            launch_groups<false>(groups_m, dim3((unsigned)blocks), (hipStream_t)stream, plan, b,
+                                 scales, signmant, status, args);
         args.n_tensors = 0;
         blocks = 0;
         return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
@@ -254,24 +280,53 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
 
 extern "C" {
 
-entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
-                             const float *d_scales, const entq_gemm_io *io, int m,
-                             int32_t *d_chunk_status, void *stream) {
+namespace {
+
+// Checks shared by both entry points; kinds_ok tells which symbol kinds the
+// call takes.
+entq_status check_gemm_args(const entq_plan_t *plan, const entq_gemm_io *io, int m,
+                            bool split) {
     if (!plan || plan->adaptive || !io || m < 1 || m > (int)entq::kGemmM * entq::kGemmMaxGroups)
         return ENTQ_EINVAL;
-    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
-    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
     for (int t = 0; t < plan->n_tensors; ++t) {
         const entq::HostTensor &h = plan->host_tensors[t];
         if (h.n_symbols == 0) continue;
-        if (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3) return ENTQ_EINVAL;
+        if (split ? h.kind != ENTQ_SYM_BF16EXP
+                  : (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3))
+            return ENTQ_EINVAL;
         if (h.cols == 0 || h.cols % entq::kBlockSyms || h.chunk_symbols % h.cols) return ENTQ_EINVAL;
         if (h.chunk_base > 0xFFFFFFFFll || h.n_chunks > 0xFFFFFFFFll) return ENTQ_EINVAL;
         const entq_gemm_io &g = io[t];
         if (!g.d_x || !g.d_y || g.ldx < h.cols || g.ldy < h.rows) return ENTQ_EINVAL;
         if ((uintptr_t)g.d_x % 8 || g.ldx % 4 || (uintptr_t)g.d_y % 4) return ENTQ_EALIGN;
     }
-    return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, io, m,
+    return ENTQ_OK;
+}
+
+}  // namespace
+
+entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
+                             const float *d_scales, const entq_gemm_io *io, int m,
+                             int32_t *d_chunk_status, void *stream) {
+    const entq_status st = check_gemm_args(plan, io, m, false);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, nullptr, io, m,
+                                                 d_chunk_status, stream);
+}
+
+entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
+                                        const uint8_t *d_signmant, const entq_gemm_io *io,
+                                        int m, int32_t *d_chunk_status, void *stream) {
+    const entq_status st = check_gemm_args(plan, io, m, true);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_exp_stream || !d_signmant)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_signmant % 16) return ENTQ_EALIGN;
+    for (int t = 0; t < plan->n_tensors; ++t)
+        if (plan->host_tensors[t].n_symbols && plan->host_tensors[t].out_elem_offset % 16)
+            return ENTQ_EALIGN;
+    return (entq_status)entq::launch_decode_gemm(plan, d_exp_stream, nullptr, d_signmant, io, m,
                                                  d_chunk_status, stream);
 }
 

@@ -72,6 +72,7 @@ struct HostTensor {
     uint64_t n_symbols;
     int64_t chunk_base;     // its first DevChunk (chunks in element order)
     int64_t n_chunks;
+    uint64_t out_elem_offset;
 };
 
 }  // namespace entq
@@ -110,7 +111,8 @@ int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, 
                            const float *scales, int32_t *status, void *stream);
 // Fused decode + product with activations (entq_decode_gemm.hip).
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
-                       const entq_gemm_io *io, int n_rows, int32_t *status, void *stream);
+                       const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
+                       int32_t *status, void *stream);
 // Workgroups of the decode kernels that fit on the current device at once
 // (compute units x workgroups per compute unit); 0 if HIP cannot tell.
 int64_t resident_workgroups();

@@ -276,7 +276,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     for (int t = 0; t < n_tensors; ++t) {
         const entq_tensor_desc &td = tensors[t];
         host_tensors[t] = {td.kind, td.rows, td.cols, td.chunk_symbols, td.n_symbols,
-                           chunk_base[t], (int64_t)slot_of[t].size()};
+                           chunk_base[t], (int64_t)slot_of[t].size(), td.out_elem_offset};
     }
     // the plan object exists before the copy is enqueued, so that no failure
     // after it has to free the copy's source

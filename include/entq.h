@@ -251,7 +251,8 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * results Y_t, m rows of `rows` values, row stride ldy >= rows (4-byte
  * aligned). All device memory, caller-owned; outputs of different tensors
  * must not overlap. 1 <= m <= 64.
- * Requirements on the plan's tensors (else ENTQ_EINVAL): kind INT8 or E4M3,
+ * Requirements on the plan's tensors (else ENTQ_EINVAL): kind INT8 or E4M3 (BF16
+ * exponent streams: entq_decode_gemm_bf16_split),
  * cols a multiple of 256, chunk_symbols a multiple of cols (every chunk
  * holds whole rows). d_chunk_status as in entq_decode. Enqueued on stream;
  * the summation order is fixed (results are reproducible run to run). */
@@ -265,6 +266,17 @@ typedef struct {
 entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
                              int32_t *d_chunk_status, void *stream);
+
+/* The same product for BF16 weights stored as a coded exponent stream plus
+ * raw sign+mantissa bytes [DFloat11 write-up, "Formato DFloat11"]: W_t is
+ * the bf16 that entq_decode_bf16_split would write (bit-exact original
+ * weights), d_signmant as for that call (16-byte aligned, indexed like its
+ * output). The plan's non-empty tensors must all be ENTQ_SYM_BF16EXP with
+ * out_elem_offset a multiple of 16; the other requirements and io[] as for
+ * entq_decode_gemm. */
+entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
+                                        const uint8_t *d_signmant, const entq_gemm_io *io,
+                                        int m, int32_t *d_chunk_status, void *stream);
 
 /* ---- On-device encoder (one wavefront per chunk; same regions as the
  * host encoder, byte for byte) ----

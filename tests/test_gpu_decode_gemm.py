@@ -181,3 +181,71 @@ def test_llama2_70b_layer_sampled_rows(E):
             ref = x @ w
             bound = sp["cols"] * 2.0 ** -24 * (np.abs(x) @ np.abs(w))
             assert (np.abs(ys[t][:, r] - ref) <= bound).all(), (t, r)
+
+
+def _bf16_setup(E, rows, cols, C):
+    import torch
+    w = synth.bf16_weights(rows, cols)[0]["bf16"]
+    e, sm = oracle.bf16_split(w)
+    spec = dict(kind=oracle.KIND_BF16EXP, rows=rows, cols=cols, symbols=e, chunk_symbols=C)
+    b = E.encode_batch([spec])
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    # the oracle's own decode of the exponent stream, merged, is the source
+    ch = b.chunks
+    desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"], ch["elem_offset"]],
+                    axis=1).astype(np.uint64)
+    sym, st = oracle.decode_tensor(b.blob, desc, b.freq[0], rows * cols)
+    assert (st == 0).all()
+    assert np.array_equal(oracle.bf16_merge(sym, sm), w)
+    return (p, torch.from_numpy(b.blob).cuda(), torch.from_numpy(sm).cuda(),
+            w.reshape(rows, cols))
+
+
+def _run_split(E, p, blob, sm, x, rows):
+    import torch
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    y = torch.full((x.shape[0], rows), float("nan"), dtype=torch.float32, device="cuda")
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode_gemm_bf16_split(p, blob, sm, [xd], [y], status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    return y.cpu().numpy()
+
+
+def test_bf16_split_one_hot_returns_the_source_weights(E):
+    rows, cols = 72, 768                 # 3 blocks per row; 4-row chunks, the last one short
+    p, blob, sm, w = _bf16_setup(E, rows, cols, cols * 4)
+    rng = np.random.default_rng(11)
+    for m in (1, 16, 33):
+        _say(f"bf16 split one-hot, m={m}")
+        c = rng.choice(cols, m, replace=False)
+        x = np.zeros((m, cols), np.float32)
+        x[np.arange(m), c] = 1.0
+        y = _run_split(E, p, blob, sm, x, rows)
+        assert np.array_equal(y.view(np.uint32), _f32(w[:, c]).T.view(np.uint32)), m
+
+
+def test_bf16_split_8192x8192_within_the_accumulation_bound(E):
+    _say("bf16 split 8192x8192, 8-row chunks, m = 16")
+    rows = cols = 8192
+    p, blob, sm, w = _bf16_setup(E, rows, cols, 65536)
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((16, cols)) * 0.5).astype(np.float32)
+    x = _f32((x.view(np.uint32) >> 16).astype(np.uint16))
+    y = _run_split(E, p, blob, sm, x, rows)
+    picks = sorted(set([0, rows - 1] + [int(v) for v in rng.integers(0, rows, 30)]))
+    wf = _f32(w[picks]).astype(np.float64)
+    ref = x.astype(np.float64) @ wf.T
+    bound = cols * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(wf).T)
+    assert (np.abs(y[:, picks] - ref) <= bound).all()
+
+
+def test_bf16_split_rejects_code_tensors(E):
+    import torch
+    specs = _mixed_specs()[:1]
+    b, p, blob, scales = _setup(E, specs)
+    x = torch.zeros(2, specs[0]["cols"], dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(2, specs[0]["rows"], dtype=torch.float32, device="cuda")
+    sm = torch.zeros(specs[0]["rows"] * specs[0]["cols"], dtype=torch.uint8, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_bf16_split(p, blob, sm, [x], [y])
