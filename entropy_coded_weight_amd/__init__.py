@@ -165,7 +165,9 @@ def default_threads() -> int:
 
 class Plan:
     """A validated batch with its device workspace (a torch uint8 tensor that
-    this object keeps alive)."""
+    this object keeps alive). The workspace is uploaded on ``stream`` (the
+    current stream by default): work on another stream must be ordered after
+    it, and the Plan must outlive every decode that uses it."""
 
     def __init__(self, tensors: np.ndarray, freq_tables, chunk_index: np.ndarray,
                  blob_bytes: int, device="cuda", stream=None):

@@ -98,6 +98,7 @@ struct entq_plan_s {
     void *host_staging;         // kept alive until destroy (async copy source)
     std::vector<entq::HostTensor> host_tensors;
     bool adaptive = false;      // chunk regions carry their own tables
+    void *upload_done = nullptr;  // hipEvent_t recorded after the workspace upload
 };
 
 // Launchers implemented in entq_decode.hip.

@@ -285,12 +285,24 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
         std::free(img);
         return ENTQ_ENOMEM;
     }
-    if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
-        hipSuccess) {
+    // the host image stays alive until the copy from it has completed: destroy
+    // waits for this event before freeing it
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
         delete p;
         std::free(img);
         return ENTQ_EHIP;
     }
+    if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
+            hipSuccess ||
+        hipEventRecord(ev, (hipStream_t)stream) != hipSuccess) {
+        hipStreamSynchronize((hipStream_t)stream);  // a copy may have been enqueued
+        hipEventDestroy(ev);
+        delete p;
+        std::free(img);
+        return ENTQ_EHIP;
+    }
+    p->upload_done = ev;
     uint8_t *ws = (uint8_t *)d_workspace;
     p->n_tensors = n_tensors;
     p->n_chunks = n_chunks;
@@ -333,6 +345,10 @@ entq_status entq_plan_adaptive(const entq_tensor_desc *tensors, int n_tensors,
 
 void entq_plan_destroy(entq_plan_t *plan) {
     if (!plan) return;
+    if (plan->upload_done) {
+        hipEventSynchronize((hipEvent_t)plan->upload_done);  // the upload read host_staging
+        hipEventDestroy((hipEvent_t)plan->upload_done);
+    }
     std::free(plan->host_staging);
     delete plan;
 }

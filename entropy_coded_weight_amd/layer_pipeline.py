@@ -41,6 +41,16 @@ class LayerPipeline:
                         for _ in range(2)]
         self.decode_stream = decode_stream or torch.cuda.Stream(self.device)
         self.compute_stream = compute_stream or torch.cuda.Stream(self.device)
+        # the plans' workspace uploads and the blobs' copies were enqueued on
+        # the current stream: order both streams after them
+        here = torch.cuda.current_stream(self.device)
+        self.decode_stream.wait_stream(here)
+        self.compute_stream.wait_stream(here)
+        # the buffers are used on both streams: their memory is not handed out
+        # again before the work queued there has finished
+        for buf in self.buffers:
+            buf.record_stream(self.decode_stream)
+            buf.record_stream(self.compute_stream)
         self.decoded = [torch.cuda.Event() for _ in range(2)]
         self.consumed = [torch.cuda.Event() for _ in range(2)]
 

@@ -137,7 +137,10 @@ size_t entq_plan_workspace_bytes(int n_tensors, int64_t n_chunks);
  *   d_workspace  device, >= entq_plan_workspace_bytes(), 256-byte aligned
  * Checks also that tensor outputs do not overlap. Returns ENTQ_OK and a new
  * plan in *out, or an error and *out = NULL. Host inputs may be freed after
- * return. */
+ * return. The upload is ordered on `stream` only: a decode enqueued on
+ * another stream must be ordered after it (an event or a stream wait).
+ * entq_plan_destroy waits for the upload to finish before it frees the
+ * plan's host copy. */
 entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors,
                       const uint16_t *freq_tables,
                       const entq_chunk_desc *chunk_index, int64_t n_chunks,
