@@ -44,10 +44,9 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-def asm(source: str = "entq_decode.hip", out: str | None = None) -> str:
-    """Device assembly of one source (for inspection)."""
-    out = out or os.path.join(ROOT, "_work", os.path.splitext(source)[0] + ".s")
-    os.makedirs(os.path.dirname(out), exist_ok=True)
+def asm(out: str, source: str = "entq_decode.hip") -> str:
+    """Device assembly of one source into the file `out` (for inspection)."""
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     cmd = [hipcc(), *compile_flags(), "--cuda-device-only", "-S", "-o", out,
            os.path.join(CSRC, source)]
     subprocess.check_call(cmd)
