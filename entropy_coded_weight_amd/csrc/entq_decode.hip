@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
     const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
-    __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kWaves][kRingWords];
+    __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
     __shared__ WaveStage<MODE> STG[kWaves];
 
@@ -184,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         Stream s;
         s.words_g = region + kStateBytes;
         s.ring = lds_addr(RING[wave]);
+        s.pos = s.ring >> 1;
         s.nw = ch.n_words;
         s.nw8 = (ch.n_words + 7u) & ~7u;  // the region is padded to 16 bytes
         s.p = 0;
@@ -214,7 +215,6 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
         const uint8_t *sm_g = signmant + ch.out_elem;
 
-        const uint32_t ring_mask = ring_mask_vgpr();
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
             if (++done == prio_at) {
@@ -225,9 +225,11 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 else __builtin_amdgcn_s_setprio(0);
             }
             if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
+            const uint32_t pos0 = s.pos;
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
-                stream_step<false>(x, s.p, s.ring, ring_mask, T, G.stage + 64u * t, lane, true);
+                stream_step<false>(x, s.pos, T, G.stage + 64u * t, lane, true);
+            ring_advance(s, pos0);
             // lane k: symbols 4k .. 4k+3 of the block (bytes 1, 3, 5, 7)
             const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
             if (MODE == kModeCodes) {
@@ -268,9 +270,10 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 ++scale_row;
                 scale = *scale_row;
             }
+            const uint32_t pos0 = s.pos;
             for (uint32_t t = 0; 64u * t < rest; ++t)
-                stream_step<true>(x, s.p, s.ring, ring_mask, T, G.stage + 64u * t, lane,
-                                  64u * t + lane < rest);
+                stream_step<true>(x, s.pos, T, G.stage + 64u * t, lane, 64u * t + lane < rest);
+            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
             const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
             for (uint32_t m = 0; m < 4; ++m) {

@@ -39,8 +39,7 @@ struct alignas(16) AdaptiveWave {
 
 // One decode step with the chunk's own maps; otherwise as stream_step.
 template <bool PARTIAL>
-__device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &p, uint32_t ring,
-                                              uint32_t ring_mask, const uint8_t *SYM,
+__device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &pos, const uint8_t *SYM,
                                               const uint32_t *ENT, uint16_t *stage_row,
                                               uint32_t lane, bool active) {
     bool need = false;
@@ -53,10 +52,9 @@ __device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &p, uint32_t
         need = x < kStateLow;
     }
     const uint64_t mask = __ballot(need);
-    const uint32_t a = (((p + lane_prefix(mask)) << 1) & ring_mask) | ring;
-    const uint32_t w = *reinterpret_cast<lds_u16 *>(a);
+    const uint32_t w = *reinterpret_cast<lds_u16 *>((pos + lane_prefix(mask)) << 1);
     x = __builtin_amdgcn_perm(x, w, need ? 0x05040100u : 0x07060504u);
-    p += (uint32_t)__popcll(mask);
+    pos += (uint32_t)__popcll(mask);
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -115,7 +113,7 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
     const DevTensor *__restrict__ tensors, const DevChunk *__restrict__ chunks, uint32_t n_chunks,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
     int32_t *__restrict__ status) {
-    __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kAdWaves][kRingWords];
+    __shared__ __attribute__((aligned(16))) uint16_t RING[kAdWaves][kRingWords];
     __shared__ AdaptiveWave WV[kAdWaves];
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,6 +132,7 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         Stream s;
         s.words_g = body + kStateBytes;
         s.ring = lds_addr(RING[wave]);
+        s.pos = s.ring >> 1;
         s.nw = ch.n_words;
         s.nw8 = (ch.n_words + 7u) & ~7u;  // the region is padded to 16 bytes
         s.p = 0;
@@ -158,14 +157,14 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         uint32_t col = ch.col0;  // a multiple of kBlockSyms
         uint16_t *o16 = static_cast<uint16_t *>(out) + ch.out_elem;
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
-        const uint32_t ring_mask = ring_mask_vgpr();
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
             if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
+            const uint32_t pos0 = s.pos;
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
-                adaptive_step<false>(x, s.p, s.ring, ring_mask, W.sym, W.ent, W.stage + 64u * t,
-                                     lane, true);
+                adaptive_step<false>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane, true);
+            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
             if (MODE == kModeCodes) {
                 reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
@@ -191,9 +190,11 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
                 ++scale_row;
                 scale = *scale_row;
             }
+            const uint32_t pos0 = s.pos;
             for (uint32_t t = 0; 64u * t < rest; ++t)
-                adaptive_step<true>(x, s.p, s.ring, ring_mask, W.sym, W.ent, W.stage + 64u * t,
-                                    lane, 64u * t + lane < rest);
+                adaptive_step<true>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane,
+                                    64u * t + lane < rest);
+            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
             const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
             for (uint32_t m = 0; m < 4; ++m) {

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                                                         const uint8_t *__restrict__ signmant,
                                                         int32_t *__restrict__ status,
                                                         GemmArgs args) {
-    __shared__ __attribute__((aligned(2 * kRingWords))) uint16_t RING[kWaves][kRingWords];
+    __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
     // two tiles of 16 weight rows x 256 columns (bf16), used in turn; at the
     // end of a weight row the same bytes hold the 16 waves' partial sums
@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
         const uint8_t *region = blob + ch.byte_offset;
         s.words_g = region + kStateBytes;
         s.ring = lds_addr(RING[wave]);
+        s.pos = s.ring >> 1;
         s.nw = ch.n_words;
         s.nw8 = (ch.n_words + 7u) & ~7u;
         x = reinterpret_cast<const uint32_t *>(region)[lane];
@@ -115,7 +116,6 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     }
     __syncthreads();  // the slot table
 
-    const uint32_t ring_mask = ring_mask_vgpr();
     // A operand: activation row (lane mod 16) of each group of 16, columns
     // 4 (lane / 16) .. +3 of this wave's 16-column slice of each block
     const uint32_t a_row = lane & 15;
@@ -152,9 +152,11 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                                                             (uint64_t)kb * kBlockSyms);
             }
             if (live) {
+                const uint32_t pos0 = s.pos;
 #pragma unroll
                 for (uint32_t t = 0; t < kBlockSteps; ++t)
-                    stream_step<false>(x, s.p, s.ring, ring_mask, T, row_tile + 64u * t, lane, true);
+                    stream_step<false>(x, s.pos, T, row_tile + 64u * t, lane, true);
+                ring_advance(s, pos0);
                 // lane k: columns 4k .. 4k+3 of the block, made bf16 in place
                 const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
                 uint2 w;

@@ -59,19 +59,23 @@ __device__ __forceinline__ void load_table(uint2 *T, const SlotEntry *tables, ui
 // the word ring and the decode step
 // ---------------------------------------------------------------------------
 
-// Word ring of one wave: kRingWords 16-bit words in LDS at a 2 KB-aligned
-// base, so that "base | (index mod kRingWords) * 2" is one v_and_or. It is
+// Word ring of one wave: word i of the chunk's stream sits at ring index
+// i mod kRingSpan, and the unit at index 0 is also kept at kRingSpan ..
+// kRingSpan + kRingUnit - 1 (a mirror), so that the reads of a block -- at
+// most kBlockSyms words from a start below kRingSpan -- never wrap: a word's
+// LDS address is (ring position + lane offset) * 2, with no mask. The ring is
 // refilled in units of kRingUnit words (32 lanes x 16 bytes, one direct
-// global->LDS load) and kept at most kRingLead words ahead of the read
-// pointer, which leaves one unit of room for the unit in flight. A block
-// reads at most kBlockSyms words, so a unit issued at one block's start is
-// not needed before the next block's start.
-constexpr uint32_t kRingWords = 1024;
+// global->LDS load, two for the unit at index 0) and kept at most kRingLead
+// words ahead of the read pointer, which leaves one unit of room for the
+// unit in flight. A block reads at most kBlockSyms words, so a unit issued at
+// one block's start is not needed before the next block's start.
 constexpr uint32_t kRingUnit = 256;
-constexpr uint32_t kRingLead = kRingWords - kRingUnit;
+constexpr uint32_t kRingSpan = 3 * kRingUnit;
+constexpr uint32_t kRingWords = kRingSpan + kRingUnit;
+constexpr uint32_t kRingLead = kRingSpan - kRingUnit;
 static_assert(kRingLead >= 2 * kBlockSyms, "a block must find its words loaded a block early");
 static_assert(kRingUnit == 32 * 8, "one unit = 32 lanes x 8 words");
-static_assert((kRingWords & (kRingWords - 1)) == 0, "ring index wraps with a mask");
+static_assert(kRingSpan % kRingUnit == 0 && kBlockSyms <= kRingUnit, "the mirror covers a block");
 
 // One 16-byte global->LDS load per active lane: lane l's bytes land at LDS
 // address lds_base + 16 l. The compiler does not see this load, so it inserts
@@ -105,6 +109,7 @@ typedef __attribute__((address_space(3))) const uint16_t lds_u16;
 struct Stream {
     const uint8_t *words_g;     // the chunk's word stream in global memory
     uint32_t ring;              // LDS byte address of the wave's ring
+    uint32_t pos;               // LDS address / 2 of word p: ring / 2 + p mod kRingSpan
     uint32_t nw, nw8;           // words, and words rounded up to 8 (16 bytes)
     uint32_t p;                 // words consumed
     uint32_t issued, landed;    // words loaded into the ring / known landed
@@ -115,8 +120,18 @@ struct Stream {
 // whose 16 bytes lie inside the chunk's region).
 __device__ __forceinline__ void ring_fill(const Stream &s, uint32_t lane) {
     const uint32_t w = s.issued + 8u * lane;
-    if (lane < kRingUnit / 8 && w < s.nw8)
-        dma16(s.words_g + 2u * w, s.ring + 2u * (s.issued & (kRingWords - 1)));
+    const uint32_t at = s.issued % kRingSpan;
+    if (lane < kRingUnit / 8 && w < s.nw8) {
+        dma16(s.words_g + 2u * w, s.ring + 2u * at);
+        if (at == 0) dma16(s.words_g + 2u * w, s.ring + 2u * kRingSpan);  // the mirror
+    }
+}
+
+// After a block's steps advanced s.pos from pos0: count the words consumed
+// and bring the ring position back below the span.
+__device__ __forceinline__ void ring_advance(Stream &s, uint32_t pos0) {
+    s.p += s.pos - pos0;
+    if (s.pos >= (s.ring >> 1) + kRingSpan) s.pos -= kRingSpan;
 }
 
 // Block start, slow path: makes sure this block's words have landed, tops
@@ -140,21 +155,13 @@ __device__ __forceinline__ void ring_service(Stream &s, uint32_t lane) {
 
 // One decode step of a wave: lane j decodes its next symbol (stores the
 // high half of its table entry in the stage) and renormalises from the
-// ring. Every lane reads the ring (no branch on the mask); lanes that
-// renormalise shift the word in, the others keep x (v_perm with a per-lane
-// selector).
-// The ring's byte-index mask in a VGPR: v_and_or_b32 takes one scalar operand
-// (the ring base) and no literal, so the mask has to come in a register. The
-// asm keeps the compiler from folding it back into a literal.
-__device__ __forceinline__ uint32_t ring_mask_vgpr() {
-    uint32_t m;
-    asm("v_mov_b32 %0, %1" : "=v"(m) : "i"(2 * kRingWords - 1));
-    return m;
-}
-
+// ring. Every lane reads the ring (no branch on the mask; a lane that does
+// not renormalise reads a word at or before the step's last one); lanes
+// that renormalise shift the word in, the others keep x (v_perm with a
+// per-lane selector). pos is the ring position of the step's first word;
+// within a block it stays below kRingSpan + kBlockSyms, inside the mirror.
 template <bool PARTIAL>
-__device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &p, uint32_t ring,
-                                            uint32_t ring_mask, const uint2 *T,
+__device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &pos, const uint2 *T,
                                             uint16_t *stage_row, uint32_t lane, bool active) {
     bool need = false;
     if (!PARTIAL || active) {
@@ -164,10 +171,9 @@ __device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &p, uint32_t r
         need = x < kStateLow;
     }
     const uint64_t mask = __ballot(need);
-    const uint32_t a = (((p + lane_prefix(mask)) << 1) & ring_mask) | ring;
-    const uint32_t w = *reinterpret_cast<lds_u16 *>(a);
+    const uint32_t w = *reinterpret_cast<lds_u16 *>((pos + lane_prefix(mask)) << 1);
     x = __builtin_amdgcn_perm(x, w, need ? 0x05040100u : 0x07060504u);
-    p += (uint32_t)__popcll(mask);
+    pos += (uint32_t)__popcll(mask);
 }
 
 // bf16 of (value of a code byte) * scale, two per dword; d holds two staged
