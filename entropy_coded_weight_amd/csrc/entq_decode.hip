@@ -181,20 +181,10 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         const uint8_t *region = blob + ch.byte_offset;
-        Stream s;
-        s.words_g = region + kStateBytes;
-        s.ring = lds_addr(RING[wave]);
-        s.pos = s.ring >> 1;
-        s.nw = ch.n_words;
-        s.nw8 = (ch.n_words + 7u) & ~7u;  // the region is padded to 16 bytes
-        s.p = 0;
-        s.issued = 0;
         const uint32_t n = ch.n_symbols;
         uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
-        while (s.issued < s.nw && s.issued < kRingLead) {
-            ring_fill(s, lane);
-            s.issued += kRingUnit;
-        }
+        Stream s;
+        ring_open(s, region + kStateBytes, lds_addr(RING[wave]), ch.n_words, lane);
         // first block's sign+mantissa bytes (a partial block reads them from
         // global memory instead)
         if (MODE == kModeSplit && n >= kBlockSyms && lane < kBlockSyms / 16)
@@ -203,11 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         // state load has completed and places no wait of its own in the loop
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
         s.landed = s.issued;
-        {
-            const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
-            const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
-            s.horizon = a < b ? a : b;
-        }
+        ring_horizon(s);
         const float *scale_row = scales + ch.scale_row;
         float scale = (MODE == kModeBf16) ? *scale_row : 0.f;
         uint32_t col = ch.col0;  // a multiple of kBlockSyms on this path
@@ -224,12 +210,10 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 else if (prio == 1) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
             }
-            if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
-            const uint32_t pos0 = s.pos;
+            if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
                 stream_step<false>(x, s.pos, T, G.stage + 64u * t, lane, true);
-            ring_advance(s, pos0);
             // lane k: symbols 4k .. 4k+3 of the block (bytes 1, 3, 5, 7)
             const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
             if (MODE == kModeCodes) {
@@ -265,15 +249,13 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         // the last, partial block: one symbol per lane and step, element-wise output
         const uint32_t rest = n - full_blocks * kBlockSyms;
         if (rest) {
-            if (s.p > s.horizon) ring_service(s, lane);
+            if (s.pos > s.hpos) ring_service(s, lane);
             if (MODE == kModeBf16 && col == cols) {
                 ++scale_row;
                 scale = *scale_row;
             }
-            const uint32_t pos0 = s.pos;
             for (uint32_t t = 0; 64u * t < rest; ++t)
                 stream_step<true>(x, s.pos, T, G.stage + 64u * t, lane, 64u * t + lane < rest);
-            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(G.stage + 4u * lane);
             const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
             for (uint32_t m = 0; m < 4; ++m) {
@@ -294,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         }
         const uint64_t bad_state = __ballot(x != kStateLow);
         if (status && lane == 0)
-            status[ch.status_index] = (s.p != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+            status[ch.status_index] = (ring_consumed(s) != s.nw) ? ENTQ_CHUNK_BAD_WORDS
                                       : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
         wait_vm<0>();  // no global->LDS load may outlive the chunk (corrupt input stops early)
     }

@@ -129,27 +129,13 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
             continue;
         }
         const uint8_t *body = region + ENTQ_TABLE_BYTES;
-        Stream s;
-        s.words_g = body + kStateBytes;
-        s.ring = lds_addr(RING[wave]);
-        s.pos = s.ring >> 1;
-        s.nw = ch.n_words;
-        s.nw8 = (ch.n_words + 7u) & ~7u;  // the region is padded to 16 bytes
-        s.p = 0;
-        s.issued = 0;
         const uint32_t n = ch.n_symbols;
         uint32_t x = reinterpret_cast<const uint32_t *>(body)[lane];
-        while (s.issued < s.nw && s.issued < kRingLead) {
-            ring_fill(s, lane);
-            s.issued += kRingUnit;
-        }
+        Stream s;
+        ring_open(s, body + kStateBytes, lds_addr(RING[wave]), ch.n_words, lane);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states and the first ring units
         s.landed = s.issued;
-        {
-            const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
-            const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
-            s.horizon = a < b ? a : b;
-        }
+        ring_horizon(s);
         const bool e4m3 = td.kind == ENTQ_SYM_E4M3;
         const uint32_t cols = td.cols;
         const float *scale_row = scales + ch.scale_row;
@@ -159,12 +145,10 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
-            if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
-            const uint32_t pos0 = s.pos;
+            if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
                 adaptive_step<false>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane, true);
-            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
             if (MODE == kModeCodes) {
                 reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
@@ -185,16 +169,14 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         // the last, partial block (a tensor's last chunk): element-wise output
         const uint32_t rest = n - full_blocks * kBlockSyms;
         if (rest) {
-            if (s.p > s.horizon) ring_service(s, lane);
+            if (s.pos > s.hpos) ring_service(s, lane);
             if (MODE == kModeBf16 && col == cols) {
                 ++scale_row;
                 scale = *scale_row;
             }
-            const uint32_t pos0 = s.pos;
             for (uint32_t t = 0; 64u * t < rest; ++t)
                 adaptive_step<true>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane,
                                     64u * t + lane < rest);
-            ring_advance(s, pos0);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
             const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
             for (uint32_t m = 0; m < 4; ++m) {
@@ -212,7 +194,7 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         }
         const uint64_t bad_state = __ballot(x != kStateLow);
         if (status && lane == 0)
-            status[ch.status_index] = (s.p != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+            status[ch.status_index] = (ring_consumed(s) != s.nw) ? ENTQ_CHUNK_BAD_WORDS
                                       : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
         wait_vm<0>();  // no global->LDS load may outlive the chunk
         wave_sync();   // the maps are rebuilt for the next chunk

@@ -96,24 +96,12 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
         ch = chunks[gt.chunk_base + first + wave];
         my_rows = ch.n_symbols / cols;
         const uint8_t *region = blob + ch.byte_offset;
-        s.words_g = region + kStateBytes;
-        s.ring = lds_addr(RING[wave]);
-        s.pos = s.ring >> 1;
-        s.nw = ch.n_words;
-        s.nw8 = (ch.n_words + 7u) & ~7u;
         x = reinterpret_cast<const uint32_t *>(region)[lane];
-        while (s.issued < s.nw && s.issued < kRingLead) {
-            ring_fill(s, lane);
-            s.issued += kRingUnit;
-        }
+        ring_open(s, region + kStateBytes, lds_addr(RING[wave]), ch.n_words, lane);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states and the first ring units
     s.landed = s.issued;
-    {
-        const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
-        const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
-        s.horizon = a < b ? a : b;
-    }
+    ring_horizon(s);
     __syncthreads();  // the slot table
 
     // A operand: activation row (lane mod 16) of each group of 16, columns
@@ -137,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
             const uint32_t buf = kb & 1;
             uint16_t *row_tile = TILE[buf][wave];
             if (live) {
-                if (__builtin_expect(s.p > s.horizon, 0)) ring_service(s, lane);
+                if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
             }
             // this block's activation slices and sign+mantissa bytes (in flight
             // while the block decodes)
@@ -152,11 +140,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                                                             (uint64_t)kb * kBlockSyms);
             }
             if (live) {
-                const uint32_t pos0 = s.pos;
 #pragma unroll
                 for (uint32_t t = 0; t < kBlockSteps; ++t)
                     stream_step<false>(x, s.pos, T, row_tile + 64u * t, lane, true);
-                ring_advance(s, pos0);
                 // lane k: columns 4k .. 4k+3 of the block, made bf16 in place
                 const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
                 uint2 w;
@@ -205,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     if (has_chunk) {
         const uint64_t bad_state = __ballot(x != kStateLow);
         if (status && lane == 0)
-            status[ch.status_index] = (s.p != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+            status[ch.status_index] = (ring_consumed(s) != s.nw) ? ENTQ_CHUNK_BAD_WORDS
                                       : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
     }
     wait_vm<0>();  // no global->LDS load may outlive the workgroup

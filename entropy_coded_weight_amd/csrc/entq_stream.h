@@ -105,16 +105,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
 
-// Uniform bookkeeping of one chunk on the streaming path.
+// Uniform bookkeeping of one chunk on the streaming path. The steps advance
+// only pos; the stream index of the next word is base + pos - ring / 2.
 struct Stream {
     const uint8_t *words_g;     // the chunk's word stream in global memory
     uint32_t ring;              // LDS byte address of the wave's ring
-    uint32_t pos;               // LDS address / 2 of word p: ring / 2 + p mod kRingSpan
+    uint32_t pos;               // LDS address / 2 of the next word to read
+    uint32_t base;              // stream index of the word at ring index 0
     uint32_t nw, nw8;           // words, and words rounded up to 8 (16 bytes)
-    uint32_t p;                 // words consumed
     uint32_t issued, landed;    // words loaded into the ring / known landed
-    uint32_t horizon;           // the ring needs attention once p passes this
+    uint32_t hpos;              // ring_service is due once pos passes this
 };
+
+// Words consumed so far.
+__device__ __forceinline__ uint32_t ring_consumed(const Stream &s) {
+    return s.base + s.pos - (s.ring >> 1);
+}
 
 // Loads words [issued, issued + kRingUnit) of the chunk into the ring (lanes
 // whose 16 bytes lie inside the chunk's region).
@@ -127,30 +133,52 @@ __device__ __forceinline__ void ring_fill(const Stream &s, uint32_t lane) {
     }
 }
 
-// After a block's steps advanced s.pos from pos0: count the words consumed
-// and bring the ring position back below the span.
-__device__ __forceinline__ void ring_advance(Stream &s, uint32_t pos0) {
-    s.p += s.pos - pos0;
-    if (s.pos >= (s.ring >> 1) + kRingSpan) s.pos -= kRingSpan;
+// The next point at which a block start needs ring_service: once a block
+// could read past the landed words, or the ring could take another unit, or
+// the read position reaches the end of the span (a block must start below it).
+__device__ __forceinline__ void ring_horizon(Stream &s) {
+    const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
+    const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
+    const uint32_t h = (a < b ? a : b) - s.base;  // both are at or past the consumed words
+    s.hpos = (s.ring >> 1) + (h < kRingSpan ? h : kRingSpan - 1);
 }
 
-// Block start, slow path: makes sure this block's words have landed, tops
-// the ring up to kRingLead words ahead and sets the next horizon.
+// Chunk start: the stream of a region's words, its first units in flight.
+// The caller waits for them (vmcnt(0)) and then calls ring_horizon.
+__device__ __forceinline__ void ring_open(Stream &s, const uint8_t *words_g, uint32_t ring,
+                                          uint32_t n_words, uint32_t lane) {
+    s.words_g = words_g;
+    s.ring = ring;
+    s.pos = ring >> 1;
+    s.base = 0;
+    s.nw = n_words;
+    s.nw8 = (n_words + 7u) & ~7u;  // the region is padded to 16 bytes
+    s.issued = 0;
+    while (s.issued < s.nw && s.issued < kRingLead) {
+        ring_fill(s, lane);
+        s.issued += kRingUnit;
+    }
+}
+
+// Block start, slow path: moves the read position back below the span,
+// makes sure this block's words have landed, tops the ring up to kRingLead
+// words ahead and sets the next horizon.
 __device__ __forceinline__ void ring_service(Stream &s, uint32_t lane) {
-    const uint32_t need_to = (s.p + kBlockSyms < s.nw) ? s.p + kBlockSyms : s.nw;
+    if (s.pos - (s.ring >> 1) >= kRingSpan) {
+        s.pos -= kRingSpan;
+        s.base += kRingSpan;
+    }
+    const uint32_t p = ring_consumed(s);
+    const uint32_t need_to = (p + kBlockSyms < s.nw) ? p + kBlockSyms : s.nw;
     if (s.landed < need_to) {
         wait_vm<1>();  // everything but the previous block's store
         s.landed = s.issued;
     }
-    while (s.issued < s.nw && s.issued < s.p + kRingLead) {
+    while (s.issued < s.nw && s.issued < p + kRingLead) {
         ring_fill(s, lane);
         s.issued += kRingUnit;
     }
-    // next time: once a block could read past the landed words, or the ring
-    // could take another unit
-    const uint32_t a = (s.landed >= s.nw) ? 0xFFFFFFFFu : s.landed - kBlockSyms;
-    const uint32_t b = (s.issued >= s.nw) ? 0xFFFFFFFFu : s.issued - kRingLead;
-    s.horizon = a < b ? a : b;
+    ring_horizon(s);
 }
 
 // One decode step of a wave: lane j decodes its next symbol (stores the
