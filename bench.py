@@ -1042,6 +1042,39 @@ def bench_adaptive(args):
         banded["per_chunk" if adaptive else "shared"] = {
             "us": us, "compressed_bytes": one[0][3], "bits_per_param": 8.0 * one[0][3] / params}
         log(f"banded adaptive={adaptive}: {us:.1f} us, {8.0 * one[0][3] / params:.4f} bits/param")
+        del one
+    # BF16 exponent stream (8192 x 8192 weights ~ N(0, 0.02)) under both tables
+    w = synth.bf16_weights()[0]
+    e, sm = E.bf16_split(w["bf16"], nthreads)
+    espec = [dict(kind=E.KIND_BF16EXP, rows=w["rows"], cols=w["cols"], chunk_symbols=65536,
+                  symbols=e)]
+    sm_d = torch.from_numpy(sm).to(dev)
+    nw = w["bf16"].size
+    outw = torch.empty(nw, dtype=torch.int16, device=dev)
+    want = torch.from_numpy(w["bf16"].view(np.int16)).to(dev)
+    exp_split = {}
+    for adaptive in (True, False):
+        b_ = E.encode_batch_adaptive(espec, nthreads) if adaptive else E.encode_batch(espec, nthreads)
+        p_ = E.plan(b_.tensors, b_.freq, b_.chunks, b_.blob.size)
+        blob_ = torch.from_numpy(b_.blob).to(dev)
+        for _ in range(args.warmup + 1):
+            E.decode_bf16_split(p_, blob_, sm_d, outw, None, stream)
+        torch.cuda.synchronize()
+        assert torch.equal(outw, want), "exponent-stream decode differs from the source"
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(20)]
+        for a_, z_ in ev:
+            a_.record(stream)
+            E.decode_bf16_split(p_, blob_, sm_d, outw, None, stream)
+            z_.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a_.elapsed_time(z_) for a_, z_ in ev])) * 1e3
+        exp_split["per_chunk" if adaptive else "shared"] = {
+            "us": us, "exp_stream_bytes": int(b_.blob.size),
+            "exp_bits_per_weight": 8.0 * b_.blob.size / nw}
+        log(f"bf16 exponent stream 8192x8192 adaptive={adaptive}: {us:.1f} us, "
+            f"{8.0 * b_.blob.size / nw:.4f} exponent bits/weight")
+        del p_, blob_
     r0 = res["per_chunk"]
     rec = {
         "metric": ADAPTIVE_METRIC,
@@ -1063,6 +1096,7 @@ def bench_adaptive(args):
             "chunk_symbols": 65536,
             "per_chunk_vs_shared": res,
             "banded_layer": banded,
+            "bf16_exponent_stream_8192x8192": exp_split,
         },
         "roofline": {
             "bound": "hbm",

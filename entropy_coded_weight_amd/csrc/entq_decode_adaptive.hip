@@ -112,7 +112,7 @@ template <int MODE>
 __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
     const DevTensor *__restrict__ tensors, const DevChunk *__restrict__ chunks, uint32_t n_chunks,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
-    int32_t *__restrict__ status) {
+    const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
     __shared__ __attribute__((aligned(16))) uint16_t RING[kAdWaves][kRingWords];
     __shared__ AdaptiveWave WV[kAdWaves];
 
@@ -143,9 +143,15 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         uint32_t col = ch.col0;  // a multiple of kBlockSyms
         uint16_t *o16 = static_cast<uint16_t *>(out) + ch.out_elem;
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
+        // sign+mantissa bytes of the chunk's elements (split mode)
+        const uint8_t *sm_g = (MODE == kModeSplit) ? signmant + ch.out_elem : nullptr;
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
             if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
+            // this lane's four sign+mantissa bytes of the block, in flight
+            // while the block decodes
+            uint32_t sm4 = 0;
+            if (MODE == kModeSplit) sm4 = *reinterpret_cast<const uint32_t *>(sm_g + 4u * lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
                 adaptive_step<false>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane, true);
@@ -153,6 +159,13 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
             if (MODE == kModeCodes) {
                 reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
                 o8 += kBlockSyms;
+            } else if (MODE == kModeSplit) {
+                // per 16-bit half: exponent << 8 | sign+mantissa
+                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
+                                           merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
+                reinterpret_cast<uint2 *>(o16)[lane] = w;
+                o16 += kBlockSyms;
+                sm_g += kBlockSyms;
             } else {
                 if (col == cols) {
                     col = 0;
@@ -185,6 +198,9 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
                 const uint32_t sym = (sym4 >> (8 * m)) & 0xFFu;
                 if (MODE == kModeCodes) {
                     o8[i] = (uint8_t)sym;
+                } else if (MODE == kModeSplit) {
+                    const uint32_t sm = sm_g[i];
+                    o16[i] = (uint16_t)(((sm & 0x80u) << 8) | (sym << 7) | (sm & 0x7Fu));
                 } else {
                     const float v = e4m3 ? __builtin_amdgcn_cvt_f32_fp8((int)sym, 0)
                                          : (float)(int8_t)sym;
@@ -204,16 +220,18 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
 }  // namespace
 
 int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, void *out,
-                           const float *scales, int32_t *status, void *stream) {
+                           const float *scales, const uint8_t *signmant, int32_t *status,
+                           void *stream) {
     if (plan->n_chunks == 0) return ENTQ_OK;
     if (plan->n_chunks > 0xFFFFFFFFll) return ENTQ_EINVAL;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return ENTQ_EHIP;
+    const void *k = (mode == kModeBf16)    ? (const void *)decode_adaptive<kModeBf16>
+                    : (mode == kModeSplit) ? (const void *)decode_adaptive<kModeSplit>
+                                           : (const void *)decode_adaptive<kModeCodes>;
     int per_cu = 0;
-    const void *k = (mode == kModeBf16) ? (const void *)decode_adaptive<kModeBf16>
-                                        : (const void *)decode_adaptive<kModeCodes>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kAdThreads, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
@@ -221,14 +239,17 @@ int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, 
     const int64_t grid = std::min<int64_t>(need, (int64_t)cus * per_cu);
     const uint32_t nc = (uint32_t)plan->n_chunks;
     const uint8_t *b = static_cast<const uint8_t *>(blob);
+    const dim3 g((unsigned)grid), blk(kAdThreads);
+    const hipStream_t st = (hipStream_t)stream;
     if (mode == kModeBf16)
-        hipLaunchKernelGGL(decode_adaptive<kModeBf16>, dim3((unsigned)grid), dim3(kAdThreads), 0,
-                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, nc, b, out,
-                           scales, status);
+        hipLaunchKernelGGL(decode_adaptive<kModeBf16>, g, blk, 0, st, plan->d_tensors,
+                           plan->d_chunks, nc, b, out, scales, signmant, status);
+    else if (mode == kModeSplit)
+        hipLaunchKernelGGL(decode_adaptive<kModeSplit>, g, blk, 0, st, plan->d_tensors,
+                           plan->d_chunks, nc, b, out, scales, signmant, status);
     else
-        hipLaunchKernelGGL(decode_adaptive<kModeCodes>, dim3((unsigned)grid), dim3(kAdThreads), 0,
-                           (hipStream_t)stream, plan->d_tensors, plan->d_chunks, nc, b, out,
-                           scales, status);
+        hipLaunchKernelGGL(decode_adaptive<kModeCodes>, g, blk, 0, st, plan->d_tensors,
+                           plan->d_chunks, nc, b, out, scales, signmant, status);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
 }
 

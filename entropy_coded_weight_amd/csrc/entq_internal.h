@@ -109,7 +109,8 @@ int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out
                   void *stream);
 // Decode of a plan whose chunks carry their own tables (entq_decode_adaptive.hip).
 int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, void *out,
-                           const float *scales, int32_t *status, void *stream);
+                           const float *scales, const uint8_t *signmant, int32_t *status,
+                           void *stream);
 // Fused decode + product with activations (entq_decode_gemm.hip).
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
                        const uint8_t *signmant, const entq_gemm_io *io, int n_rows,

@@ -102,10 +102,9 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
         if ((uint64_t)td.rows * td.cols != td.n_symbols) return ENTQ_EINVAL;
         if (td.n_symbols == 0) continue;
         if (adaptive) {
-            if (td.kind == ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
-            if (td.chunk_symbols % entq::kBlockSyms || td.cols % entq::kBlockSyms ||
-                td.out_elem_offset % 16)
-                return ENTQ_EINVAL;
+            // whole 256-symbol blocks; bf16 rows (scales) of whole blocks
+            if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return ENTQ_EINVAL;
+            if (td.kind != ENTQ_SYM_BF16EXP && td.cols % entq::kBlockSyms) return ENTQ_EINVAL;
         } else {
             uint32_t sum = 0;
             for (int s = 0; s < 256; ++s) sum += freq_tables[(size_t)t * 256 + s];
@@ -381,7 +380,8 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
     }
     if (plan->adaptive)
         return (entq_status)entq::launch_decode_adaptive(plan, mode, d_compressed, d_out,
-                                                         d_scales, d_chunk_status, stream);
+                                                         d_scales, nullptr, d_chunk_status,
+                                                         stream);
     return (entq_status)entq::launch_decode(plan, mode, d_compressed, d_out, d_scales, nullptr,
                                             d_chunk_status, stream);
 }
@@ -389,13 +389,17 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
 entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                    const uint8_t *d_signmant, uint16_t *d_out,
                                    int32_t *d_chunk_status, void *stream) {
-    if (!plan || plan->adaptive) return ENTQ_EINVAL;
+    if (!plan) return ENTQ_EINVAL;
     if (plan->kinds_mask & ~(1u << ENTQ_SYM_BF16EXP)) return ENTQ_EINVAL;
     if (plan->n_chunks == 0) return ENTQ_OK;
     if (!d_exp_stream || !d_signmant || !d_out) return ENTQ_EINVAL;
     if ((uintptr_t)d_exp_stream % ENTQ_REGION_ALIGN || (uintptr_t)d_out % 16 ||
         (uintptr_t)d_signmant % 16)
         return ENTQ_EALIGN;
+    if (plan->adaptive)
+        return (entq_status)entq::launch_decode_adaptive(plan, entq::kModeSplit, d_exp_stream,
+                                                         d_out, nullptr, d_signmant,
+                                                         d_chunk_status, stream);
     return (entq_status)entq::launch_decode(plan, entq::kModeSplit, d_exp_stream, d_out, nullptr,
                                             d_signmant, d_chunk_status, stream);
 }

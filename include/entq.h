@@ -154,11 +154,12 @@ entq_status entq_plan(const entq_tensor_desc *tensors, int n_tensors,
  * The region of a chunk is u16 freq[256] (ENTQ_TABLE_BYTES, sum 4096), then
  * the 64 states and the words as in a shared-table region, zero-padded to 16
  * bytes (entq_encode_tensor_adaptive writes it). Same arguments as entq_plan
- * without tables; tensors must be INT8 or E4M3 with chunk_symbols and cols
- * multiples of 256 and out_elem_offset a multiple of 16 (else ENTQ_EINVAL).
- * entq_decode works on such a plan (a chunk whose table does not sum to 4096
- * gets ENTQ_CHUNK_BAD_TABLE and no output); entq_decode_bf16_split and
- * entq_decode_gemm reject it. */
+ * without tables; every tensor needs chunk_symbols a multiple of 256 and
+ * out_elem_offset a multiple of 16, and INT8 and E4M3 tensors cols a multiple
+ * of 256 (else ENTQ_EINVAL). entq_decode and, for a plan of BF16EXP tensors,
+ * entq_decode_bf16_split work on such a plan (a chunk whose table does not
+ * sum to 4096 gets ENTQ_CHUNK_BAD_TABLE and no output); entq_decode_gemm and
+ * entq_decode_gemm_bf16_split reject it. */
 entq_status entq_plan_adaptive(const entq_tensor_desc *tensors, int n_tensors,
                                const entq_chunk_desc *chunk_index, int64_t n_chunks,
                                uint64_t blob_bytes, void *d_workspace, size_t workspace_bytes,
@@ -178,10 +179,12 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
                         entq_outkind out_kind, const float *d_scales,
                         int32_t *d_chunk_status, void *stream);
 
-/* Decodes a plan whose tensors are all ENTQ_SYM_BF16EXP into bf16 words:
- * the coded exponent bytes come from d_exp_stream (the blob), the raw
- * sign+mantissa byte of output element i is d_signmant[i] (same indexing as
- * d_out). d_out and d_signmant are 16-byte aligned. */
+/* Decodes a plan whose tensors are all ENTQ_SYM_BF16EXP into bf16 words
+ * [DFloat11 write-up, "Formato DFloat11"]: the coded exponent bytes come
+ * from d_exp_stream (the blob), the raw sign+mantissa byte of output element
+ * i is d_signmant[i] (same indexing as d_out). d_out and d_signmant are
+ * 16-byte aligned. The plan may be a shared-table (entq_plan) or a
+ * per-chunk-table (entq_plan_adaptive) one. */
 entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                    const uint8_t *d_signmant, uint16_t *d_out,
                                    int32_t *d_chunk_status, void *stream);

@@ -419,5 +419,20 @@ def decode_container_adaptive_bf16(c: Container, scales: np.ndarray):
     return out, status
 
 
+def decode_container_adaptive_split(c: Container, signmant: np.ndarray):
+    """(bf16 words, per-chunk status) of an adaptive container of BF16EXP
+    tensors: each tensor's decoded exponent bytes merged with its raw
+    sign+mantissa bytes, signmant being indexed like the output [DFloat11
+    write-up, "Formato DFloat11"]. Composition of the adaptive decode and
+    bf16_merge, nothing else."""
+    syms, status = decode_container_adaptive_symbols(c)
+    total = max((t["out_elem_offset"] + t["n_symbols"] for t in c.tensors), default=0)
+    out = np.zeros(total, np.uint16)
+    for td, sym in zip(c.tensors, syms):
+        o, n = td["out_elem_offset"], td["n_symbols"]
+        out[o:o + n] = bf16_merge(sym, np.ascontiguousarray(signmant[o:o + n], np.uint8))
+    return out, status
+
+
 def _isnan_bits(u: int) -> bool:
     return (u & 0x7F800000) == 0x7F800000 and (u & 0x007FFFFF) != 0

@@ -1,7 +1,8 @@
 """GPU parity of the per-chunk-table (adaptive) decode through the C ABI:
-codes and bf16 output equal the oracle's adaptive decode; a chunk whose
-table is corrupt reports ENTQ_CHUNK_BAD_TABLE while its neighbours decode;
-a whole 70B-shaped layer is checked on sampled chunks."""
+codes and bf16 output equal the oracle's adaptive decode; BF16 exponent
+streams with per-chunk tables rebuild every bf16 word; a chunk whose table
+is corrupt reports ENTQ_CHUNK_BAD_TABLE while its neighbours decode; a whole
+70B-shaped layer is checked on sampled chunks."""
 import numpy as np
 import pytest
 
@@ -144,3 +145,44 @@ def test_llama2_70b_layer_sampled_chunks(E):
         full[e0 - r0 * cols:e0 - r0 * cols + n] = sym
         want = oracle.dequant_tensor(full, r1 - r0 + 1, cols, sp["kind"], sp["scales"][r0:r1 + 1])
         np.testing.assert_array_equal(got[o + e0:o + e0 + n], want[e0 - r0 * cols:e0 - r0 * cols + n])
+
+
+def test_exponent_streams_with_per_chunk_tables(E):
+    """entq_decode_bf16_split on a per-chunk-table plan: a 2048 x 8192 BF16
+    matrix and a random (high-entropy) stream with a ragged last block; the
+    bf16 words equal the source and the oracle's merge, the codes output the
+    exponent bytes. The fused product still rejects such a plan."""
+    import torch
+    w1 = synth.bf16_weights(2048, 8192)[0]["bf16"]
+    rng = np.random.default_rng(21)
+    w2 = rng.integers(0, 1 << 16, size=3 * 70_001 + 5, dtype=np.uint64).astype(np.uint16)
+    specs, sms, exps = [], [], []
+    for w, cols in ((w1, 8192), (w2, w2.size)):
+        e, sm = oracle.bf16_split(w)
+        specs.append(dict(kind=oracle.KIND_BF16EXP, rows=w.size // cols, cols=cols, symbols=e,
+                          chunk_symbols=65536))
+        sms.append(sm)
+        exps.append(e)
+    _say(f"exponent streams, per-chunk tables: {w1.size + w2.size} weights")
+    c = oracle.encode_container_adaptive(specs)
+    sm_all = np.concatenate(sms)
+    want, st = oracle.decode_container_adaptive_split(c, sm_all)
+    assert (st == 0).all()
+    np.testing.assert_array_equal(want, np.concatenate([w1, w2]))
+    p, blob = _plan(E, c)
+    total = w1.size + w2.size
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    out = torch.zeros(total, dtype=torch.int16, device="cuda")
+    E.decode_bf16_split(p, blob, torch.from_numpy(sm_all).cuda(), out, status)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), want)
+    np.testing.assert_array_equal(status.cpu().numpy(), st)
+    got, gst = _decode(E, p, blob, total, E.OUT_CODES)
+    np.testing.assert_array_equal(got, np.concatenate(exps))
+    np.testing.assert_array_equal(gst, st)
+    x = torch.zeros(1, 8192, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(1, 2048, dtype=torch.float32, device="cuda")
+    x2 = torch.zeros(1, w2.size + 3, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.zeros(1, 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_bf16_split(p, blob, torch.from_numpy(sm_all).cuda(), [x, x2], [y, y2])

@@ -71,9 +71,10 @@ def test_adaptive_plan_rejects_what_the_decoder_cannot_take(E):
     sp = synth.random_int8_tensor(8, 320, 1.5, 8, 1280)
     b2 = E.encode_batch_adaptive([sp], n_threads=1)
     assert _try_plan(E, b2.tensors, b2.chunks, b2.blob.size) == -1
-    # exponent streams are not taken with per-chunk tables
+    # exponent streams need whole blocks too (their rows need not be)
     t = b.tensors.copy()
     t[0]["kind"] = oracle.KIND_BF16EXP
+    t[0]["chunk_symbols"] = 1024 + 64
     assert _try_plan(E, t, b.chunks, bb) == -1
     # output offset not a multiple of 16
     t = b.tensors.copy()

@@ -86,3 +86,21 @@ def test_adaptive_tables_pay_on_banded_codes():
     words_a, words_s = int(a.chunks[:, 2].sum()), int(s.chunks[:, 2].sum())
     assert abs(words_a - words_s) <= 0.005 * words_s
     assert a.blob.size > s.blob.size
+
+
+def test_exponent_streams_round_trip_with_per_chunk_tables():
+    """BF16 weights split into exponent and sign+mantissa bytes, the exponent
+    stream coded with per-chunk tables: the merge of the decoded exponents
+    gives back every original bit pattern, ragged tails included."""
+    a = synth.bf16_weights(64, 1024, sigma=0.02)[0]["bf16"]
+    b = synth.bf16_weights(64, 1024, sigma=2.0)[0]["bf16"]
+    w = np.concatenate([a, b, a[:70_001]])           # two regimes, then a ragged tail
+    e, sm = oracle.bf16_split(w)
+    spec = dict(kind=oracle.KIND_BF16EXP, rows=1, cols=w.size, symbols=e, chunk_symbols=16384)
+    c = oracle.encode_container_adaptive([spec])
+    got, st = oracle.decode_container_adaptive_split(c, sm)
+    assert (st == oracle.STATUS_OK).all()
+    np.testing.assert_array_equal(got, w)
+    # the chunks of the two regimes carry different tables
+    tabs = {bytes(c.blob[int(off):int(off) + 512]) for off in c.chunks[:, 3]}
+    assert len(tabs) >= 2
