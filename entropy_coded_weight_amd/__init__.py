@@ -48,6 +48,11 @@ COUNT_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("counts", "<u8"
 PACK_JOB = np.dtype([("scratch", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
                      ("reserved", "<u4"), ("n_words", "<u8"), ("offsets", "<u8")])
 # entq_encode_job (include/entq.h): device pointers as integers
+CHUNK_COUNT_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
+                            ("reserved", "<u4"), ("counts", "<u8")])
+PACK_ADAPTIVE_JOB = np.dtype([("scratch", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
+                              ("reserved", "<u4"), ("n_words", "<u8"), ("offsets", "<u8"),
+                              ("freq", "<u8")])
 ENCODE_JOB = np.dtype([("symbols", "<u8"), ("n_symbols", "<u8"), ("chunk_symbols", "<u4"),
                        ("reserved", "<u4"), ("freq", "<u8"), ("scratch", "<u8"),
                        ("scratch_bytes", "<u8"), ("n_words", "<u8")])
@@ -103,6 +108,11 @@ def lib():
             "entq_count_symbols_device_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_pack_device_batch": (c.c_int, [vp, c.c_int, vp, vp]),
             "entq_decode_gemm_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
+            "entq_count_chunks_device_batch": (c.c_int, [vp, c.c_int, vp]),
+            "entq_build_freq_chunks": (c.c_int, [vp, u64, vp, c.c_int]),
+            "entq_encode_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp]),
+            "entq_region_offsets_device_adaptive": (c.c_int, [vp, u64, u64, vp, vp, vp]),
+            "entq_pack_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -120,7 +130,9 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_encode_device_batch", "entq_decode_gemm", "entq_plan_adaptive",
             "entq_encode_tensor_adaptive", "entq_encode_bound_adaptive",
             "entq_count_symbols_device_batch", "entq_pack_device_batch",
-            "entq_decode_gemm_bf16_split"]
+            "entq_decode_gemm_bf16_split", "entq_count_chunks_device_batch",
+            "entq_build_freq_chunks", "entq_encode_device_adaptive_batch",
+            "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch"]
 
 
 def _str(status: int) -> str:
@@ -500,6 +512,61 @@ def region_offsets_device(n_words, offsets, end, base_offset: int = 0, stream=No
                                             _stream(stream)), "entq_region_offsets_device")
 
 
+def count_chunks_device_batch(jobs, stream=None):
+    """jobs: list of (symbols, chunk_symbols, counts) with device tensors;
+    counts int32 [ceil(n / chunk_symbols), 256] receives each chunk's byte
+    counts. One launch per 16 arrays."""
+    arr = np.zeros(len(jobs), CHUNK_COUNT_JOB)
+    for i, (sym, C, counts) in enumerate(jobs):
+        arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(counts))
+    _check(lib().entq_count_chunks_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                                _stream(stream)),
+           "entq_count_chunks_device_batch")
+
+
+def build_freq_chunks(counts: np.ndarray, n_threads: int | None = None) -> np.ndarray:
+    """Host: the table of each row of 256 counts (uint32 [k, 256])."""
+    counts = np.ascontiguousarray(counts, dtype=np.uint32).reshape(-1, 256)
+    freq = np.zeros(counts.shape, np.uint16)
+    _check(lib().entq_build_freq_chunks(_ptr(counts) if counts.size else None, counts.shape[0],
+                                        _ptr(freq) if counts.size else None,
+                                        n_threads or default_threads()),
+           "entq_build_freq_chunks")
+    return freq
+
+
+def encode_device_adaptive_batch(jobs, stream=None):
+    """encode_device_batch with per-chunk tables: jobs are (symbols,
+    chunk_symbols, freq, scratch, n_words) with freq a device uint16/int16
+    [n_chunks, 256]."""
+    arr = np.zeros(len(jobs), ENCODE_JOB)
+    for i, (sym, C, freq, scratch, nw) in enumerate(jobs):
+        arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(freq), _ptr(scratch),
+                  scratch.numel(), _ptr(nw))
+    _check(lib().entq_encode_device_adaptive_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                                   _stream(stream)),
+           "entq_encode_device_adaptive_batch")
+
+
+def region_offsets_device_adaptive(n_words, offsets, end, base_offset: int = 0, stream=None):
+    """region_offsets_device for regions headed by their table."""
+    _check(lib().entq_region_offsets_device_adaptive(_ptr(n_words) or None, n_words.numel(),
+                                                     int(base_offset), _ptr(offsets) or None,
+                                                     _ptr(end), _stream(stream)),
+           "entq_region_offsets_device_adaptive")
+
+
+def pack_device_adaptive_batch(jobs, blob, stream=None):
+    """pack_device_batch for regions headed by their table: jobs are
+    (scratch, n, chunk_symbols, n_words, offsets, freq)."""
+    arr = np.zeros(len(jobs), PACK_ADAPTIVE_JOB)
+    for i, (scratch, n, C, nw, offs, freq) in enumerate(jobs):
+        arr[i] = (_ptr(scratch), int(n), int(C), 0, _ptr(nw), _ptr(offs), _ptr(freq))
+    _check(lib().entq_pack_device_adaptive_batch(_ptr(arr) if len(jobs) else None, len(jobs),
+                                                 _ptr(blob), _stream(stream)),
+           "entq_pack_device_adaptive_batch")
+
+
 @dataclass
 class DeviceBatch:
     """Like Batch, with the blob left in device memory (a torch uint8 view)."""
@@ -610,3 +677,85 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         scale_off += rows
         k0 += k
     return DeviceBatch(blob[:end], tens, freqs, chunks)
+
+
+def encode_batch_device_adaptive(specs, stream=None, events=None) -> DeviceBatch:
+    """encode_batch_device with per-chunk tables (the container of
+    encode_batch_adaptive, built on the GPU): per-chunk byte counts on the
+    device, the tables on the host (entq_build_freq_chunks), then encoding,
+    the region layout and packing on the device, each step over all
+    tensors. The DeviceBatch's freq is None (pass it to plan() as such)."""
+    import torch
+    dev = specs[0]["symbols"].device if specs else torch.device("cuda")
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    T = len(specs)
+    shapes = []
+    for sp in specs:
+        sym = sp["symbols"]
+        rows, cols, C = int(sp["rows"]), int(sp["cols"]), int(sp["chunk_symbols"])
+        n = sym.numel()
+        assert n == rows * cols and sym.dtype == torch.uint8 and sym.is_contiguous()
+        shapes.append((rows, cols, C, n, -(-n // C)))
+    k_all = sum(sh[4] for sh in shapes)
+    k0s = np.concatenate([[0], np.cumsum([sh[4] for sh in shapes])]).astype(np.int64)
+    bound = sum(int(lib().entq_encode_bound_adaptive(sh[3], sh[2])) for sh in shapes)
+    scr = [int(lib().entq_encode_device_scratch_bytes(sh[3], sh[2])) for sh in shapes]
+    scr_off = np.concatenate([[0], np.cumsum(scr)]).astype(np.int64)
+    blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(max(int(scr_off[-1]), 16), dtype=torch.uint8, device=dev)
+    counts = torch.zeros((max(k_all, 1), 256), dtype=torch.int32, device=dev)
+    nw_d = torch.empty(max(k_all, 1), dtype=torch.int32, device=dev)
+    offs_d = torch.empty(max(k_all, 1), dtype=torch.int64, device=dev)
+    end_d = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def timed(name, fn):
+        if events is None:
+            return fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        events.append((name, a, b))
+
+    live = [t for t in range(T) if shapes[t][4]]
+    with torch.cuda.stream(s):
+        cjobs = [(specs[t]["symbols"], shapes[t][2], counts[k0s[t]:k0s[t + 1]]) for t in live]
+        if cjobs:
+            timed("count", lambda: count_chunks_device_batch(cjobs, s))
+        s.synchronize()
+        freqs = build_freq_chunks(counts[:k_all].cpu().numpy().view(np.uint32))
+        freq_d = torch.from_numpy(freqs.view(np.int16)).to(dev, non_blocking=False)
+        jobs = [(specs[t]["symbols"], shapes[t][2], freq_d[k0s[t]:k0s[t + 1]],
+                 scratch[scr_off[t]:scr_off[t + 1]], nw_d[k0s[t]:k0s[t + 1]]) for t in live]
+        if jobs:
+            timed("encode", lambda: encode_device_adaptive_batch(jobs, s))
+        if k_all:
+            timed("offsets", lambda: region_offsets_device_adaptive(
+                nw_d[:k_all], offs_d[:k_all], end_d, 0, s))
+        pjobs = [(scratch[scr_off[t]:scr_off[t + 1]], shapes[t][3], shapes[t][2],
+                  nw_d[k0s[t]:k0s[t + 1]], offs_d[k0s[t]:k0s[t + 1]], freq_d[k0s[t]:k0s[t + 1]])
+                 for t in live]
+        if pjobs:
+            timed("pack", lambda: pack_device_adaptive_batch(pjobs, blob, s))
+        s.synchronize()
+        nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
+        offs = offs_d[:k_all].cpu().numpy().view(np.uint64)
+        end = int(end_d.cpu().numpy()[0])
+    if (nw == 0xFFFFFFFF).any():
+        raise EntqError(-2, "entq_encode_device_adaptive_batch: a chunk could not be coded")
+    tens = np.zeros(T, TENSOR_DESC)
+    chunks = np.zeros(k_all, CHUNK_DESC)
+    out_off = scale_off = 0
+    for t, sp in enumerate(specs):
+        rows, cols, C, n, k = shapes[t]
+        ch = chunks[k0s[t]:k0s[t + 1]]
+        ch["tensor"] = t
+        ch["n_symbols"] = np.minimum(C, n - np.arange(k, dtype=np.int64) * C)
+        ch["n_words"] = nw[k0s[t]:k0s[t + 1]]
+        ch["byte_offset"] = offs[k0s[t]:k0s[t + 1]]
+        ch["elem_offset"] = np.arange(k, dtype=np.uint64) * C
+        tens[t] = (int(sp["kind"]), rows, cols, C, n, out_off, scale_off)
+        out_off += n
+        scale_off += rows
+    return DeviceBatch(blob[:end], tens, None, chunks)

@@ -163,6 +163,21 @@ entq_status entq_build_freq(const uint64_t counts[256], uint16_t freq[256]) {
     return ENTQ_OK;
 }
 
+entq_status entq_build_freq_chunks(const uint32_t *counts, uint64_t n_tables, uint16_t *freq,
+                                   int n_threads) {
+    if (n_tables == 0) return ENTQ_OK;
+    if (!counts || !freq) return ENTQ_EINVAL;
+    parallel_ranges(pick_threads(n_threads, n_tables / 64 + 1), n_tables,
+                    [&](int, uint64_t lo, uint64_t hi) {
+                        uint64_t c[256];
+                        for (uint64_t t = lo; t < hi; ++t) {
+                            for (int s = 0; s < 256; ++s) c[s] = counts[t * 256 + s];
+                            entq_build_freq(c, freq + t * 256);
+                        }
+                    });
+    return ENTQ_OK;
+}
+
 uint64_t entq_encode_bound(uint64_t n_symbols, uint32_t chunk_symbols) {
     if (chunk_symbols == 0) return 0;
     uint64_t k = (n_symbols + chunk_symbols - 1) / chunk_symbols;

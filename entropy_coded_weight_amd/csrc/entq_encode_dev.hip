@@ -223,6 +223,58 @@ __device__ bool build_entries(EncEntry *T, uint32_t *P, const uint16_t *freq) {
     return total == kProbScale && !over;
 }
 
+// The entries of one chunk's own table, built by one wave: lane l takes
+// symbols 4l .. 4l+3, a wave scan gives the cumulative starts. Returns
+// whether the table sums to 4096 with every f <= 4096.
+__device__ bool build_entries_wave(EncEntry *T, const uint16_t *__restrict__ freq, uint32_t lane) {
+    uint32_t f[4], pre[4], tot = 0;
+    for (int i = 0; i < 4; ++i) {
+        f[i] = freq[4u * lane + i];
+        pre[i] = tot;
+        tot += f[i];
+    }
+    uint32_t incl = tot;  // inclusive scan over lanes
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    const uint32_t start = incl - tot;
+    bool over = false;
+    for (int i = 0; i < 4; ++i) {
+        over |= f[i] > kProbScale;
+        T[4u * lane + i] = make_entry(f[i] > kProbScale ? 0u : f[i], start + pre[i]);
+    }
+    const uint32_t total = __shfl(incl, 63, 64);
+    const bool any_over = __ballot(over) != 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return total == kProbScale && !any_over;
+}
+
+// Chunks that carry their own tables: job.freq holds one table per chunk
+// (256 u16 each); each wave builds the entries of its chunk's table.
+__global__ __launch_bounds__(kEncThreads) void encode_chunks_own_tables(EncJobs jobs) {
+    __shared__ EncEntry TW[kEncWaves][256];
+    uint32_t j = 0;
+    while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
+    const EncJob &job = jobs.job[j];
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint64_t k = (uint64_t)(blockIdx.x - job.first_block) * kEncWaves + wave;
+    if (k >= job.n_chunks) return;
+    if (!build_entries_wave(TW[wave], job.freq + k * 256, lane)) {
+        if (lane == 0) job.n_words[k] = 0xFFFFFFFFu;
+        return;
+    }
+    const uint64_t e0 = k * job.chunk_symbols;
+    const uint32_t cn =
+        (uint32_t)((job.n - e0 < job.chunk_symbols) ? job.n - e0 : job.chunk_symbols);
+    const uint32_t nw = encode_chunk(TW[wave], job.symbols + e0, cn, job.chunk_symbols,
+                                     job.scratch + k * scratch_stride(job.chunk_symbols), lane);
+    if (lane == 0) job.n_words[k] = nw;
+}
+
 template <bool kInlineTable>
 __global__ __launch_bounds__(kEncThreads) void encode_chunks(EncJobs jobs, EncFreq inline_freq) {
     __shared__ EncEntry T[256];
@@ -253,15 +305,23 @@ __global__ __launch_bounds__(kEncThreads) void encode_chunks(EncJobs jobs, EncFr
 // of the chunk's word area), zeros up to the next 16-byte boundary. The
 // region is written one dword per thread and pass; when the words start at
 // an odd word index, each dword is funnelled from two source dwords.
+// With own_tables (one u16 table of 256 per chunk) the region starts with the
+// chunk's table, ENTQ_TABLE_BYTES, before the states.
 __device__ __forceinline__ void pack_one(const uint8_t *__restrict__ scratch,
                                          uint32_t chunk_symbols,
                                          const uint32_t *__restrict__ n_words,
                                          const uint64_t *__restrict__ offsets,
-                                         uint8_t *__restrict__ blob, uint64_t k) {
+                                         uint8_t *__restrict__ blob, uint64_t k,
+                                         const uint16_t *__restrict__ own_tables = nullptr) {
     const uint32_t nw = n_words[k];
     if (nw > chunk_symbols) return;  // a chunk the encoder rejected (frequency-0 symbol)
     const uint8_t *area = scratch + k * scratch_stride(chunk_symbols);
     uint32_t *dst = reinterpret_cast<uint32_t *>(blob + offsets[k]);
+    if (own_tables) {
+        const uint32_t *tab = reinterpret_cast<const uint32_t *>(own_tables + k * 256);
+        if (threadIdx.x < ENTQ_TABLE_BYTES / 4) dst[threadIdx.x] = tab[threadIdx.x];
+        dst += ENTQ_TABLE_BYTES / 4;
+    }
     if (threadIdx.x < 64) dst[threadIdx.x] = reinterpret_cast<const uint32_t *>(area)[threadIdx.x];
     const uint32_t *A = reinterpret_cast<const uint32_t *>(area + kStateBytes);  // word pairs
     uint32_t *D = dst + kStateBytes / 4;
@@ -306,6 +366,7 @@ struct PackJob {
     const uint8_t *scratch;
     const uint32_t *n_words;
     const uint64_t *offsets;
+    const uint16_t *own_tables;  // per-chunk tables, or null
     uint32_t chunk_symbols, first_block;
 };
 struct PackJobs {
@@ -318,7 +379,7 @@ __global__ __launch_bounds__(256) void pack_chunks_batch(PackJobs jobs, uint8_t 
     while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
     const PackJob &pj = jobs.job[j];
     pack_one(pj.scratch, pj.chunk_symbols, pj.n_words, pj.offsets, blob,
-             blockIdx.x - pj.first_block);
+             blockIdx.x - pj.first_block, pj.own_tables);
 }
 
 // Region offsets: offsets[k] = base + the region bytes of chunks 0..k-1
@@ -328,12 +389,17 @@ __global__ __launch_bounds__(256) void pack_chunks_batch(PackJobs jobs, uint8_t 
 // the 1024 run sums gives each run its start, the run is then written out.
 constexpr int kScanThreads = 1024;
 
-__device__ __forceinline__ uint64_t region_size(uint32_t nw) {
-    return nw > (uint32_t)kMaxChunkSymbols ? 0 : (((uint64_t)kStateBytes + 2ull * nw + 15u) & ~15ull);
+__device__ __forceinline__ uint64_t region_size(uint32_t nw, uint32_t header) {
+    return nw > (uint32_t)kMaxChunkSymbols
+               ? 0
+               : header + (((uint64_t)kStateBytes + 2ull * nw + 15u) & ~15ull);
 }
 
+// header: bytes before the states of every region (0, or ENTQ_TABLE_BYTES
+// for chunks that carry their own tables).
 __global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *__restrict__ n_words,
                                                                uint64_t n_chunks, uint64_t base,
+                                                               uint32_t header,
                                                                uint64_t *__restrict__ offsets,
                                                                uint64_t *__restrict__ end) {
     __shared__ uint64_t part[kScanThreads];
@@ -342,7 +408,7 @@ __global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *_
     const uint64_t lo = t * per < n_chunks ? t * per : n_chunks;
     const uint64_t hi = lo + per < n_chunks ? lo + per : n_chunks;
     uint64_t sum = 0;
-    for (uint64_t i = lo; i < hi; ++i) sum += region_size(n_words[i]);
+    for (uint64_t i = lo; i < hi; ++i) sum += region_size(n_words[i], header);
     part[t] = sum;
     __syncthreads();
     for (uint32_t d = 1; d < kScanThreads; d <<= 1) {
@@ -354,7 +420,7 @@ __global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *_
     uint64_t run = base + part[t] - sum;  // exclusive prefix of this run
     for (uint64_t i = lo; i < hi; ++i) {
         offsets[i] = run;
-        run += region_size(n_words[i]);
+        run += region_size(n_words[i], header);
     }
     if (t == kScanThreads - 1) *end = base + part[t];
 }
@@ -368,12 +434,12 @@ __global__ __launch_bounds__(kScanThreads) void region_offsets(const uint32_t *_
 constexpr int kCountThreads = 512;
 constexpr int kCountBytesPerLane = 64;
 
-// The histogram of one workgroup's share of a byte array: block bid of
-// nblocks takes lane rounds bid * kCountThreads + t, + nblocks *
-// kCountThreads, ...; block 0 also takes the last n % 64 bytes.
-__device__ __forceinline__ void count_share(uint32_t *H, const uint8_t *__restrict__ symbols,
-                                            uint64_t n, unsigned long long *__restrict__ counts,
-                                            uint64_t bid, uint64_t nblocks) {
+// The histogram of one workgroup's share of a byte array, left in H (bin b
+// = the sum of row b's 64 columns): block bid of nblocks takes lane rounds
+// bid * kCountThreads + t, + nblocks * kCountThreads, ...; block 0 also takes
+// the last n % 64 bytes.
+__device__ __forceinline__ void histogram(uint32_t *H, const uint8_t *__restrict__ symbols,
+                                          uint64_t n, uint64_t bid, uint64_t nblocks) {
     const uint32_t lane_off = (threadIdx.x & 63u) * 4u;  // byte offset of the lane's column
     for (uint32_t i = threadIdx.x; i < 256u * 64u / 4u; i += kCountThreads)
         reinterpret_cast<uint4 *>(H)[i] = make_uint4(0, 0, 0, 0);
@@ -405,10 +471,23 @@ __device__ __forceinline__ void count_share(uint32_t *H, const uint8_t *__restri
         if (tail < n) add_byte(symbols[tail]);
     }
     __syncthreads();
+}
+
+// Bin b of the histogram in H (thread b < 256).
+__device__ __forceinline__ uint64_t histogram_bin(const uint32_t *H, uint32_t b) {
+    uint64_t sum = 0;
+    for (uint32_t j = 0; j < 64; ++j)  // column order rotated by bin: no bank conflicts
+        sum += H[b * 64u + ((j + b) & 63u)];
+    return sum;
+}
+
+// A workgroup's share added into 64-bit counts.
+__device__ __forceinline__ void count_share(uint32_t *H, const uint8_t *__restrict__ symbols,
+                                            uint64_t n, unsigned long long *__restrict__ counts,
+                                            uint64_t bid, uint64_t nblocks) {
+    histogram(H, symbols, n, bid, nblocks);
     if (threadIdx.x < 256) {
-        uint64_t sum = 0;
-        for (uint32_t j = 0; j < 64; ++j)  // column order rotated by bin: no bank conflicts
-            sum += H[threadIdx.x * 64u + ((j + threadIdx.x) & 63u)];
+        const uint64_t sum = histogram_bin(H, threadIdx.x);
         if (sum) atomicAdd(&counts[threadIdx.x], (unsigned long long)sum);
     }
 }
@@ -439,6 +518,32 @@ __global__ __launch_bounds__(kCountThreads) void count_bytes_batch(CountJobs job
     while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
     const CountJob &cj = jobs.job[j];
     count_share(H, cj.symbols, cj.n, cj.counts, blockIdx.x - cj.first_block, cj.blocks);
+}
+
+// Counts of every chunk of several arrays in one launch, one workgroup per
+// chunk: job j's chunk k goes to counts[256 k ..] (32-bit: a chunk holds at
+// most 2^20 bytes).
+struct ChunkCountJob {
+    const uint8_t *symbols;
+    uint32_t *counts;
+    uint64_t n;
+    uint32_t chunk_symbols, first_block;
+};
+struct ChunkCountJobs {
+    ChunkCountJob job[kMaxEncJobs];
+    uint32_t n_jobs;
+};
+
+__global__ __launch_bounds__(kCountThreads) void count_chunks_batch(ChunkCountJobs jobs) {
+    __shared__ uint32_t H[256 * 64];
+    uint32_t j = 0;
+    while (j + 1 < jobs.n_jobs && jobs.job[j + 1].first_block <= blockIdx.x) ++j;
+    const ChunkCountJob &cj = jobs.job[j];
+    const uint64_t k = blockIdx.x - cj.first_block;
+    const uint64_t e0 = k * cj.chunk_symbols;
+    const uint64_t cn = (cj.n - e0 < cj.chunk_symbols) ? cj.n - e0 : cj.chunk_symbols;
+    histogram(H, cj.symbols + e0, cn, 0, 1);
+    if (threadIdx.x < 256) cj.counts[k * 256 + threadIdx.x] = (uint32_t)histogram_bin(H, threadIdx.x);
 }
 
 // Workgroups for counting n bytes: two per CU on 256 CUs at most, fewer for
@@ -536,7 +641,8 @@ entq_status entq_pack_device_batch(const entq_pack_job *jobs, int n_jobs, void *
         if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + k > 0x7FFFFFFFull)
             if (!flush()) return ENTQ_EHIP;
         batch.job[batch.n_jobs++] = {static_cast<const uint8_t *>(pj.d_scratch), pj.d_n_words,
-                                     pj.d_byte_offsets, pj.chunk_symbols, (uint32_t)blocks};
+                                     pj.d_byte_offsets, nullptr, pj.chunk_symbols,
+                                     (uint32_t)blocks};
         blocks += k;
     }
     return flush() ? ENTQ_OK : ENTQ_EHIP;
@@ -651,9 +757,139 @@ entq_status entq_region_offsets_device(const uint32_t *d_n_words, uint64_t n_chu
         return ENTQ_EALIGN;
     if (base_offset % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
     hipLaunchKernelGGL(entq::region_offsets, dim3(1), dim3(entq::kScanThreads), 0,
-                       (hipStream_t)stream, d_n_words, n_chunks, base_offset, d_byte_offsets,
-                       d_end_offset);
+                       (hipStream_t)stream, d_n_words, n_chunks, base_offset, 0u,
+                       d_byte_offsets, d_end_offset);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_region_offsets_device_adaptive(const uint32_t *d_n_words, uint64_t n_chunks,
+                                               uint64_t base_offset, uint64_t *d_byte_offsets,
+                                               uint64_t *d_end_offset, void *stream) {
+    if (!d_end_offset || (n_chunks && (!d_n_words || !d_byte_offsets))) return ENTQ_EINVAL;
+    if ((uintptr_t)d_n_words % 4 || (uintptr_t)d_byte_offsets % 8 || (uintptr_t)d_end_offset % 8)
+        return ENTQ_EALIGN;
+    if (base_offset % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
+    hipLaunchKernelGGL(entq::region_offsets, dim3(1), dim3(entq::kScanThreads), 0,
+                       (hipStream_t)stream, d_n_words, n_chunks, base_offset,
+                       (uint32_t)ENTQ_TABLE_BYTES, d_byte_offsets, d_end_offset);
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_count_chunks_device_batch(const entq_chunk_count_job *jobs, int n_jobs,
+                                           void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_chunk_count_job &cj = jobs[j];
+        const uint32_t C = cj.chunk_symbols;
+        if (C == 0 || C % entq::kLanes || C > entq::kMaxChunkSymbols) return ENTQ_EINVAL;
+        if (cj.n_symbols == 0) continue;
+        if (!cj.d_symbols || !cj.d_counts) return ENTQ_EINVAL;
+        if ((uintptr_t)cj.d_symbols % 16 || (uintptr_t)cj.d_counts % 4) return ENTQ_EALIGN;
+        if ((cj.n_symbols + C - 1) / C > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    }
+    entq::ChunkCountJobs batch = {};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::count_chunks_batch, dim3((unsigned)blocks),
+                           dim3(entq::kCountThreads), 0, (hipStream_t)stream, batch);
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_chunk_count_job &cj = jobs[j];
+        if (cj.n_symbols == 0) continue;
+        const uint64_t k = (cj.n_symbols + cj.chunk_symbols - 1) / cj.chunk_symbols;
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + k > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {cj.d_symbols, cj.d_counts, cj.n_symbols, cj.chunk_symbols,
+                                     (uint32_t)blocks};
+        blocks += k;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_encode_device_adaptive_batch(const entq_encode_job *jobs, int n_jobs,
+                                              void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_encode_job &jb = jobs[j];
+        const uint32_t C = jb.chunk_symbols;
+        if (C == 0 || C % entq::kLanes || C > entq::kMaxChunkSymbols) return ENTQ_EINVAL;
+        if (jb.n_symbols == 0) continue;
+        if (!jb.d_symbols || !jb.d_freq || !jb.d_scratch || !jb.d_n_words) return ENTQ_EINVAL;
+        if ((uintptr_t)jb.d_symbols % 16 || (uintptr_t)jb.d_scratch % 16 ||
+            (uintptr_t)jb.d_n_words % 4 || (uintptr_t)jb.d_freq % 2)
+            return ENTQ_EALIGN;
+        if (jb.scratch_bytes < entq_encode_device_scratch_bytes(jb.n_symbols, C))
+            return ENTQ_EWORKSPACE;
+        if ((jb.n_symbols + C - 1) / C > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    }
+    entq::EncJobs batch = {};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::encode_chunks_own_tables, dim3((unsigned)blocks),
+                           dim3(entq::kEncThreads), 0, (hipStream_t)stream, batch);
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_encode_job &jb = jobs[j];
+        if (jb.n_symbols == 0) continue;
+        const uint64_t k = (jb.n_symbols + jb.chunk_symbols - 1) / jb.chunk_symbols;
+        const uint64_t b = (k + entq::kEncWaves - 1) / entq::kEncWaves;
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + b > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {jb.d_symbols, static_cast<uint8_t *>(jb.d_scratch),
+                                     jb.d_n_words, jb.d_freq, jb.n_symbols, jb.chunk_symbols,
+                                     (uint32_t)k, (uint32_t)blocks, 0};
+        blocks += b;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_pack_device_adaptive_batch(const entq_pack_adaptive_job *jobs, int n_jobs,
+                                            void *d_blob, void *stream) {
+    if (n_jobs < 0 || (n_jobs && !jobs)) return ENTQ_EINVAL;
+    if (n_jobs && !d_blob) return ENTQ_EINVAL;
+    if ((uintptr_t)d_blob % ENTQ_REGION_ALIGN) return ENTQ_EALIGN;
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_pack_adaptive_job &pj = jobs[j];
+        const uint32_t C = pj.chunk_symbols;
+        if (C == 0 || C % entq::kLanes || C > entq::kMaxChunkSymbols) return ENTQ_EINVAL;
+        if (pj.n_symbols == 0) continue;
+        if (!pj.d_scratch || !pj.d_n_words || !pj.d_byte_offsets || !pj.d_freq)
+            return ENTQ_EINVAL;
+        if ((uintptr_t)pj.d_scratch % 16 || (uintptr_t)pj.d_n_words % 4 ||
+            (uintptr_t)pj.d_byte_offsets % 8 || (uintptr_t)pj.d_freq % 4)
+            return ENTQ_EALIGN;
+        if ((pj.n_symbols + C - 1) / C > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    }
+    entq::PackJobs batch = {};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> bool {
+        if (batch.n_jobs == 0) return true;
+        hipLaunchKernelGGL(entq::pack_chunks_batch, dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, batch, static_cast<uint8_t *>(d_blob));
+        batch = {};
+        blocks = 0;
+        return hipGetLastError() == hipSuccess;
+    };
+    for (int j = 0; j < n_jobs; ++j) {
+        const entq_pack_adaptive_job &pj = jobs[j];
+        if (pj.n_symbols == 0) continue;
+        const uint64_t k = (pj.n_symbols + pj.chunk_symbols - 1) / pj.chunk_symbols;
+        if (batch.n_jobs == (uint32_t)entq::kMaxEncJobs || blocks + k > 0x7FFFFFFFull)
+            if (!flush()) return ENTQ_EHIP;
+        batch.job[batch.n_jobs++] = {static_cast<const uint8_t *>(pj.d_scratch), pj.d_n_words,
+                                     pj.d_byte_offsets, pj.d_freq, pj.chunk_symbols,
+                                     (uint32_t)blocks};
+        blocks += k;
+    }
+    return flush() ? ENTQ_OK : ENTQ_EHIP;
 }
 
 }  // extern "C"

@@ -393,6 +393,66 @@ entq_status entq_region_offsets_device(const uint32_t *d_n_words, uint64_t n_chu
                                       uint64_t base_offset, uint64_t *d_byte_offsets,
                                       uint64_t *d_end_offset, void *stream);
 
+/* ---- On-device encoder with per-chunk tables (the regions of
+ * entq_plan_adaptive, byte for byte equal to entq_encode_tensor_adaptive's)
+ * [EntroLLM summary, "Significado y Afirmaciones"]:
+ *   1. entq_count_chunks_device_batch -> per-chunk counts (copy to host) ->
+ *      entq_build_freq_chunks -> per-chunk tables (copy to device)
+ *   2. entq_encode_device_adaptive_batch -> word counts
+ *   3. entq_region_offsets_device_adaptive -> offsets
+ *   4. entq_pack_device_adaptive_batch -> the regions, each headed by its
+ *      chunk's table ---- */
+
+/* Counts of every chunk of several device arrays, one launch per 16 arrays:
+ * chunk k of job j (bytes k * chunk_symbols .. of d_symbols, 16-byte
+ * aligned) writes its 256 counts to d_counts[256 k ..] (device u32, 4-byte
+ * aligned, ceil(n_symbols / chunk_symbols) rows). */
+typedef struct {
+    const uint8_t *d_symbols;
+    uint64_t n_symbols;
+    uint32_t chunk_symbols;    /* multiple of 64, at most 2^20 */
+    uint32_t reserved;
+    uint32_t *d_counts;
+} entq_chunk_count_job;
+
+entq_status entq_count_chunks_device_batch(const entq_chunk_count_job *jobs, int n_jobs,
+                                           void *stream);
+
+/* Host: entq_build_freq applied to each of n_tables rows of 256 counts
+ * (u32), written to freq[256 t ..]; n_threads <= 0 uses all cores. */
+entq_status entq_build_freq_chunks(const uint32_t *counts, uint64_t n_tables, uint16_t *freq,
+                                   int n_threads);
+
+/* entq_encode_device_batch with one table per chunk: job.d_freq holds
+ * ceil(n_symbols / chunk_symbols) tables of 256 u16 (each summing to 4096),
+ * the table of chunk k at d_freq[256 k]. A chunk whose table is invalid or
+ * lacks one of its symbols gets word count 0xFFFFFFFF. */
+entq_status entq_encode_device_adaptive_batch(const entq_encode_job *jobs, int n_jobs,
+                                              void *stream);
+
+/* entq_region_offsets_device for regions that start with their table:
+ * each takes ENTQ_TABLE_BYTES + entq_region_bytes(n_words) bytes (0 if
+ * rejected). */
+entq_status entq_region_offsets_device_adaptive(const uint32_t *d_n_words, uint64_t n_chunks,
+                                               uint64_t base_offset, uint64_t *d_byte_offsets,
+                                               uint64_t *d_end_offset, void *stream);
+
+/* entq_pack_device_batch for regions that start with their table: region k
+ * = the 512 bytes of d_freq[256 k ..] (device u16, 4-byte aligned), then
+ * the states and words as in a shared-table region. */
+typedef struct {
+    const void *d_scratch;
+    uint64_t n_symbols;
+    uint32_t chunk_symbols;
+    uint32_t reserved;
+    const uint32_t *d_n_words;
+    const uint64_t *d_byte_offsets;
+    const uint16_t *d_freq;
+} entq_pack_adaptive_job;
+
+entq_status entq_pack_device_adaptive_batch(const entq_pack_adaptive_job *jobs, int n_jobs,
+                                            void *d_blob, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -181,3 +181,87 @@ def test_batched_encode_marks_invalid_device_table(E):
     ok = nws[0].cpu().numpy().view(np.uint32)
     assert (ok != 0xFFFFFFFF).all() and (ok > 0).all()
     assert (nws[1].cpu().numpy().view(np.uint32) == 0xFFFFFFFF).all()
+
+
+# ---- per-chunk tables ------------------------------------------------------
+
+def test_per_chunk_counts_match_numpy(E):
+    import torch
+    rng = np.random.default_rng(61)
+    arrays = [rng.integers(0, 256, n, dtype=np.uint8) for n in (64, 4096 * 3 + 64, 65536 * 2 + 4160)]
+    arrays[1][:5000] = 7                                   # a skewed stretch
+    Cs = [64, 4096, 65536]
+    devs = [_dev(a) for a in arrays]
+    outs = [torch.full((-(-a.size // C), 256), -1, dtype=torch.int32, device="cuda")
+            for a, C in zip(arrays, Cs)]
+    E.count_chunks_device_batch([(d, C, o) for d, C, o in zip(devs, Cs, outs)])
+    torch.cuda.synchronize()
+    for a, C, o in zip(arrays, Cs, outs):
+        want = np.stack([np.bincount(a[e0:e0 + C], minlength=256) for e0 in range(0, a.size, C)])
+        np.testing.assert_array_equal(o.cpu().numpy(), want)
+
+
+def _check_adaptive_against_oracle(E, specs):
+    c = oracle.encode_container_adaptive(specs)
+    b = E.encode_batch_device_adaptive(_dev_specs(specs))
+    blob = b.blob.cpu().numpy()
+    assert blob.size == c.blob.size
+    assert np.array_equal(blob, c.blob)
+    assert np.array_equal(_device_chunks(b), _oracle_chunks(c))
+    assert b.freq is None
+    return b
+
+
+def test_per_chunk_tables_match_oracle(E):
+    specs = []
+    for seed, (r, c, C) in enumerate([(3, 7, 64), (1, 65, 64), (17, 129, 4096), (5, 4097, 4096),
+                                      (33, 1000, 65536), (2, 65536 + 64, 65536)]):
+        specs.append(synth.random_int8_tensor(r, c, 1.5 + seed, 70 + seed, C))
+    one = synth.random_int8_tensor(16, 64, 1.0, 80, 64)
+    one["symbols"] = np.full(one["symbols"].shape, 9, np.uint8)       # f = 4096 in every chunk
+    allb = synth.random_int8_tensor(64, 512, 1.0, 81, 4096)
+    allb["symbols"] = synth.random_bytes(64 * 512, 81).view(np.uint8)  # all 256 byte values
+    specs += [one, allb, synth.banded_int8_tensor(48, 2816, 4, 7, 2816 * 4)]
+    w = synth.bf16_weights(8, 4096)[0]
+    e, _ = oracle.bf16_split(w["bf16"])
+    specs.append(dict(kind=oracle.KIND_BF16EXP, rows=8, cols=4096, chunk_symbols=8192, symbols=e))
+    _say(f"{len(specs)} tensors with per-chunk tables, device encoder vs oracle")
+    _check_adaptive_against_oracle(E, specs)
+
+
+def test_per_chunk_tables_70b_layer_match_host_and_decode(E):
+    import torch
+    _say("70B-shaped layer 0 with per-chunk tables: device vs host encoder, then decode")
+    specs = synth.llama2_70b_layer(0)
+    host = E.encode_batch_adaptive(specs)
+    dev = E.encode_batch_device_adaptive(_dev_specs(specs))
+    assert dev.blob.numel() == host.blob.size
+    assert np.array_equal(dev.blob.cpu().numpy(), host.blob)
+    assert np.array_equal(dev.chunks, host.chunks)
+    p = E.plan(dev.tensors, None, dev.chunks, dev.blob.numel())
+    out = torch.zeros(dev.out_elems, dtype=torch.uint8, device="cuda")
+    status = torch.full((len(dev.chunks),), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, dev.blob, out, E.OUT_CODES, None, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    src = np.concatenate([np.ascontiguousarray(s["symbols"]).view(np.uint8).ravel()
+                          for s in specs])
+    assert np.array_equal(out.cpu().numpy(), src)
+
+
+def test_per_chunk_encode_marks_invalid_tables(E):
+    import torch
+    sym = np.zeros(4096 * 3, np.uint8)
+    sym[4096 + 10] = 5                       # chunk 1 holds byte 5
+    d = _dev(sym)
+    freq = np.zeros((3, 256), np.uint16)
+    freq[:, 0] = 4096                        # chunk 1's table lacks byte 5
+    freq[2, 0] = 4000                        # chunk 2's table sums to 4000
+    fd = torch.from_numpy(freq.view(np.int16)).cuda()
+    scratch = torch.empty(int(E.lib().entq_encode_device_scratch_bytes(sym.size, 4096)),
+                          dtype=torch.uint8, device="cuda")
+    nw = torch.zeros(3, dtype=torch.int32, device="cuda")
+    E.encode_device_adaptive_batch([(d, 4096, fd, scratch, nw)])
+    torch.cuda.synchronize()
+    got = nw.cpu().numpy().view(np.uint32)
+    assert got[0] == 0 and got[1] == 0xFFFFFFFF and got[2] == 0xFFFFFFFF

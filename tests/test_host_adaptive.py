@@ -80,3 +80,21 @@ def test_adaptive_plan_rejects_what_the_decoder_cannot_take(E):
     t = b.tensors.copy()
     t[0]["out_elem_offset"] = 8
     assert _try_plan(E, t, b.chunks, bb) == -1
+
+
+def test_build_freq_chunks_equals_the_oracle_rule(E):
+    rng = np.random.default_rng(44)
+    rows = [np.zeros(256, np.uint32)]                                  # an empty chunk
+    one = np.zeros(256, np.uint32); one[200] = 65536; rows.append(one)  # one symbol
+    rows.append(np.full(256, 256, np.uint32))                          # uniform
+    for i in range(300):
+        c = rng.integers(0, 2000, 256).astype(np.uint32)
+        c[rng.random(256) < 0.5 + 0.4 * (i % 2)] = 0
+        c[int(rng.integers(0, 256))] += int(rng.integers(0, 1 << 20))
+        rows.append(c)
+    counts = np.stack(rows)
+    for threads in (1, 5):
+        got = E.build_freq_chunks(counts, n_threads=threads)
+        for r, g in zip(counts, got):
+            want = np.zeros(256, np.uint16) if r.sum() == 0 else oracle.quantize_freqs(r.astype(np.uint64))
+            np.testing.assert_array_equal(g, want)
