@@ -366,6 +366,25 @@ def bench_encode(args):
     log(f"encode: {ms_per_step:.2f} ms/step wall, kernels per step (us): "
         + ", ".join(f"{k} {v:.0f}" for k, v in kind_us.items())
         + f"; encode {n_layer / kind_us['encode'] / 1e6:.3f} T sym/s, {enc_gbs:.0f} GB/s")
+    # the same layers with per-chunk tables (counts per chunk, tables on the host)
+    E.encode_batch_device_adaptive(layers[0], stream)
+    torch.cuda.synchronize()
+    ad_wall, ad_kinds, ad_comp = [], {}, []
+    for st in range(args.steps):
+        ev = []
+        t = time.perf_counter()
+        b = E.encode_batch_device_adaptive(layers[st % len(layers)], stream, events=ev)
+        ad_wall.append(time.perf_counter() - t)
+        ad_comp.append(int(b.blob.numel()))
+        for name, a_, z_ in ev:
+            ad_kinds.setdefault(name, []).append(a_.elapsed_time(z_) * 1e3)
+        del b
+    ad_kind_us = {k: float(np.sum(v)) / args.steps for k, v in ad_kinds.items()}
+    per_chunk = {"ms_per_step_wall": 1e3 * float(np.mean(ad_wall)),
+                 "kernel_us_per_step": ad_kind_us,
+                 "compressed_bytes_per_layer": float(np.mean(ad_comp))}
+    log(f"encode, per-chunk tables: {per_chunk['ms_per_step_wall']:.2f} ms/step wall, kernels "
+        "per step (us): " + ", ".join(f"{k} {v:.0f}" for k, v in ad_kind_us.items()))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = encode_cpu_baseline(host_layer0[1:3], layers[0][1:3], stream)
@@ -392,6 +411,7 @@ def bench_encode(args):
             "step_ms_wall_p10_p50_p90": [1e3 * float(np.percentile(wall, q)) for q in (10, 50, 90)],
             "note": "value is wall time per layer including the two host reads (counts; word "
                     "counts and offsets) and the host frequency tables",
+            "per_chunk_tables": per_chunk,
         },
         "roofline": {
             "bound": "hbm",
