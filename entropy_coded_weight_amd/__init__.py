@@ -113,6 +113,7 @@ def lib():
             "entq_encode_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_region_offsets_device_adaptive": (c.c_int, [vp, u64, u64, vp, vp, vp]),
             "entq_pack_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp, vp]),
+            "entq_build_freq_device": (c.c_int, [vp, c.c_uint32, u64, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -132,7 +133,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_count_symbols_device_batch", "entq_pack_device_batch",
             "entq_decode_gemm_bf16_split", "entq_count_chunks_device_batch",
             "entq_build_freq_chunks", "entq_encode_device_adaptive_batch",
-            "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch"]
+            "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
+            "entq_build_freq_device"]
 
 
 def _str(status: int) -> str:
@@ -535,6 +537,18 @@ def build_freq_chunks(counts: np.ndarray, n_threads: int | None = None) -> np.nd
     return freq
 
 
+def build_freq_device(counts, freq, stream=None):
+    """Tables from counts on the device: counts int32 or int64 [k, 256]
+    (device), freq int16/uint16 [k, 256] (device)."""
+    import torch
+    assert counts.dtype in (torch.int32, torch.int64) and counts.is_contiguous()
+    k = counts.numel() // 256
+    assert freq.numel() >= k * 256
+    _check(lib().entq_build_freq_device(_ptr(counts) or None, counts.element_size(), k,
+                                        _ptr(freq) or None, _stream(stream)),
+           "entq_build_freq_device")
+
+
 def encode_device_adaptive_batch(jobs, stream=None):
     """encode_device_batch with per-chunk tables: jobs are (symbols,
     chunk_symbols, freq, scratch, n_words) with freq a device uint16/int16
@@ -583,10 +597,10 @@ class DeviceBatch:
 
 def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
     """The device path of encode_batch: specs' ``symbols`` are device uint8
-    tensors (contiguous, 16-byte aligned). Counts, encoding, the region
-    layout and packing run on the GPU, each step over all tensors; the
-    host reads the counts once (to build the frequency tables) and the word
-    counts and offsets once at the end (for the chunk index). With
+    tensors (contiguous, 16-byte aligned). Counts, frequency tables,
+    encoding, the region layout and packing run on the GPU, each step over
+    all tensors; the host reads the word counts, offsets and tables once at
+    the end (for the chunk index). With
     ``events`` (a list), each kernel launch appends (name, start, end) HIP
     events recorded on the stream around it."""
     import torch
@@ -625,14 +639,9 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         cjobs = [(sp["symbols"], counts[t]) for t, sp in enumerate(specs) if shapes[t][3]]
         if cjobs:
             timed("count", lambda: count_symbols_device_batch(cjobs, s))
-        s.synchronize()
-        host_counts = counts.cpu().numpy().view(np.uint64)
-        freqs = np.zeros((max(T, 1), 256), np.uint16)
-        for t in range(T):
-            freqs[t] = build_freq(host_counts[t])
-            if shapes[t][3] == 0:
-                freqs[t, 0] = PROB_SCALE
-        freq_d = torch.from_numpy(freqs.view(np.int16)).to(dev, non_blocking=False)
+        freq_d = torch.zeros((max(T, 1), 256), dtype=torch.int16, device=dev)
+        if T:
+            timed("tables", lambda: build_freq_device(counts, freq_d, s))
         jobs, k0 = [], 0
         for t, sp in enumerate(specs):
             rows, cols, C, n, k = shapes[t]
@@ -642,7 +651,6 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
             k0 += k
         if jobs:
             timed("encode", lambda: encode_device_batch(jobs, s))
-        freqs = freqs[:T]
         if k_all:
             timed("offsets", lambda: region_offsets_device(nw_d[:k_all], offs_d[:k_all], end_d,
                                                            0, s))
@@ -659,6 +667,10 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
         offs = offs_d[:k_all].cpu().numpy().view(np.uint64)
         end = int(end_d.cpu().numpy()[0])
+        freqs = freq_d[:T].cpu().numpy().view(np.uint16).copy()
+    for t in range(T):
+        if shapes[t][3] == 0:
+            freqs[t, 0] = PROB_SCALE  # an empty tensor: any valid table
     if (nw == 0xFFFFFFFF).any():
         raise EntqError(-2, "entq_encode_device: a symbol has frequency 0")
     tens = np.zeros(T, TENSOR_DESC)
@@ -681,10 +693,11 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
 
 def encode_batch_device_adaptive(specs, stream=None, events=None) -> DeviceBatch:
     """encode_batch_device with per-chunk tables (the container of
-    encode_batch_adaptive, built on the GPU): per-chunk byte counts on the
-    device, the tables on the host (entq_build_freq_chunks), then encoding,
-    the region layout and packing on the device, each step over all
-    tensors. The DeviceBatch's freq is None (pass it to plan() as such)."""
+    encode_batch_adaptive, built on the GPU): per-chunk byte counts, their
+    tables (entq_build_freq_device), encoding, the region layout and packing,
+    each step over all tensors, with no host round trip before the final
+    read of the chunk index. The DeviceBatch's freq is None (pass it to
+    plan() as such)."""
     import torch
     dev = specs[0]["symbols"].device if specs else torch.device("cuda")
     s = torch.cuda.current_stream(dev) if stream is None else stream
@@ -723,9 +736,9 @@ def encode_batch_device_adaptive(specs, stream=None, events=None) -> DeviceBatch
         cjobs = [(specs[t]["symbols"], shapes[t][2], counts[k0s[t]:k0s[t + 1]]) for t in live]
         if cjobs:
             timed("count", lambda: count_chunks_device_batch(cjobs, s))
-        s.synchronize()
-        freqs = build_freq_chunks(counts[:k_all].cpu().numpy().view(np.uint32))
-        freq_d = torch.from_numpy(freqs.view(np.int16)).to(dev, non_blocking=False)
+        freq_d = torch.zeros((max(k_all, 1), 256), dtype=torch.int16, device=dev)
+        if k_all:
+            timed("tables", lambda: build_freq_device(counts[:k_all], freq_d, s))
         jobs = [(specs[t]["symbols"], shapes[t][2], freq_d[k0s[t]:k0s[t + 1]],
                  scratch[scr_off[t]:scr_off[t + 1]], nw_d[k0s[t]:k0s[t + 1]]) for t in live]
         if jobs:

@@ -546,6 +546,107 @@ __global__ __launch_bounds__(kCountThreads) void count_chunks_batch(ChunkCountJo
     if (threadIdx.x < 256) cj.counts[k * 256 + threadIdx.x] = (uint32_t)histogram_bin(H, threadIdx.x);
 }
 
+// ---- tables from counts on the device --------------------------------------
+//
+// The table rule of entq_build_freq, one wave per table (lane l holds bytes
+// 4l .. 4l+3): nearest share of 4096 (halves up), at least 1 for a present
+// byte; a surplus is taken from the largest shares, smallest byte first on
+// ties, and a shortfall given to the most frequent byte (smallest on ties);
+// one present byte gets 4096, none gives an all-zero table. Taking one unit
+// at a time from the current largest share is done in one pass: every share
+// is capped at the smallest level L whose cap costs at most the surplus K,
+// and the K - cost(L) units left come off the smallest bytes standing at L.
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum32(uint32_t v) {
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+template <typename CountT>
+__device__ void build_table_wave(const CountT *__restrict__ counts, uint16_t *__restrict__ freq,
+                                 uint32_t lane) {
+    uint64_t c[4];
+    uint64_t n_loc = 0;
+    uint32_t p_loc = 0;
+    for (int i = 0; i < 4; ++i) {
+        c[i] = counts[4u * lane + i];
+        n_loc += c[i];
+        p_loc += c[i] ? 1u : 0u;
+    }
+    const uint64_t N = wave_sum64(n_loc);
+    const uint32_t present = wave_sum32(p_loc);
+    uint32_t q[4] = {0, 0, 0, 0};
+    if (present == 1) {
+        for (int i = 0; i < 4; ++i) q[i] = c[i] ? kProbScale : 0u;
+    } else if (present > 1) {
+        uint32_t s_loc = 0;
+        for (int i = 0; i < 4; ++i) {
+            if (c[i]) {
+                const uint64_t v = (2ull * kProbScale * c[i] + N) / (2ull * N);
+                q[i] = v < 1 ? 1u : (uint32_t)v;
+            }
+            s_loc += q[i];
+        }
+        const uint32_t sum = wave_sum32(s_loc);
+        if (sum > kProbScale) {
+            const uint32_t K = sum - kProbScale;
+            auto cost = [&](uint32_t L) {
+                uint32_t d = 0;
+                for (int i = 0; i < 4; ++i) d += q[i] > L ? q[i] - L : 0u;
+                return wave_sum32(d);
+            };
+            uint32_t lo = 1, hi = kProbScale;  // smallest L with cost(L) <= K
+            while (lo < hi) {
+                const uint32_t mid = (lo + hi) / 2;
+                if (cost(mid) <= K) hi = mid;
+                else lo = mid + 1;
+            }
+            const uint32_t L = lo;
+            const uint32_t r = K - cost(L);
+            uint32_t at_loc = 0;
+            for (int i = 0; i < 4; ++i) at_loc += q[i] >= L ? 1u : 0u;
+            uint32_t incl = at_loc;  // bytes at level L up to this lane
+            for (uint32_t d = 1; d < 64; d <<= 1) {
+                const uint32_t v = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += v;
+            }
+            uint32_t rank = incl - at_loc;
+            for (int i = 0; i < 4; ++i) {
+                if (q[i] >= L) {
+                    q[i] = (rank < r) ? L - 1 : L;
+                    ++rank;
+                }
+            }
+        } else if (sum < kProbScale) {
+            // most frequent byte, smallest on ties
+            uint64_t best = c[0];
+            uint32_t arg = 4u * lane;
+            for (int i = 1; i < 4; ++i)
+                if (c[i] > best) { best = c[i]; arg = 4u * lane + i; }
+            for (int d = 32; d >= 1; d >>= 1) {
+                const uint64_t ob = __shfl_xor(best, d, 64);
+                const uint32_t oa = __shfl_xor(arg, d, 64);
+                if (ob > best || (ob == best && oa < arg)) { best = ob; arg = oa; }
+            }
+            if ((arg >> 2) == lane) q[arg & 3u] += kProbScale - sum;
+        }
+    }
+    for (int i = 0; i < 4; ++i) freq[4u * lane + i] = (uint16_t)q[i];
+}
+
+template <typename CountT>
+__global__ __launch_bounds__(256) void build_tables(const CountT *__restrict__ counts,
+                                                    uint64_t n_tables, uint16_t *__restrict__ freq) {
+    const uint64_t t = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tables) return;
+    build_table_wave(counts + t * 256, freq + t * 256, threadIdx.x & 63);
+}
+
 // Workgroups for counting n bytes: two per CU on 256 CUs at most, fewer for
 // small inputs (at least 16 lane rounds per thread); a lane column counts at
 // most n / (64 blocks) bytes, more blocks keep that below 2^32.
@@ -772,6 +873,25 @@ entq_status entq_region_offsets_device_adaptive(const uint32_t *d_n_words, uint6
     hipLaunchKernelGGL(entq::region_offsets, dim3(1), dim3(entq::kScanThreads), 0,
                        (hipStream_t)stream, d_n_words, n_chunks, base_offset,
                        (uint32_t)ENTQ_TABLE_BYTES, d_byte_offsets, d_end_offset);
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+entq_status entq_build_freq_device(const void *d_counts, uint32_t count_bytes, uint64_t n_tables,
+                                   uint16_t *d_freq, void *stream) {
+    if (count_bytes != 4 && count_bytes != 8) return ENTQ_EINVAL;
+    if (n_tables == 0) return ENTQ_OK;
+    if (!d_counts || !d_freq) return ENTQ_EINVAL;
+    if ((uintptr_t)d_counts % count_bytes || (uintptr_t)d_freq % 2) return ENTQ_EALIGN;
+    const uint64_t blocks = (n_tables + 3) / 4;
+    if (blocks > 0x7FFFFFFFull) return ENTQ_EINVAL;
+    if (count_bytes == 4)
+        hipLaunchKernelGGL(entq::build_tables<uint32_t>, dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, static_cast<const uint32_t *>(d_counts), n_tables,
+                           d_freq);
+    else
+        hipLaunchKernelGGL(entq::build_tables<uint64_t>, dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, static_cast<const uint64_t *>(d_counts), n_tables,
+                           d_freq);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
 }
 

@@ -291,15 +291,15 @@ entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_e
  * "Float8@2bits: Entropy Coding Enables Data-Free Model Compression",
  * technical summary §2 "Codificación de Pesos"]; these calls encode the
  * library's own format on the GPU. A tensor is encoded in three enqueued
- * steps, with the frequency table and the region offsets settled on the
- * host between them:
- *   1. entq_count_symbols_device -> counts (copy to host) -> entq_build_freq
+ * steps:
+ *   1. entq_count_symbols_device -> counts -> entq_build_freq_device (or a
+ *      copy to the host and entq_build_freq there)
  *   2. entq_encode_device -> per-chunk word counts; region k takes
  *      entq_region_bytes(n_words[k]) bytes at a 16-byte-aligned offset, laid
  *      out on the device by entq_region_offsets_device (or on the host)
  *   3. entq_pack_device -> the regions in the caller's blob
- * Only the counts of step 1 need to reach the host before step 2; the word
- * counts and offsets are read back once, after step 3, for the chunk index.
+ * Nothing needs to reach the host before step 3; the word counts and
+ * offsets are read back once, after it, for the chunk index.
  * All buffers are caller-owned device memory; all work is enqueued on
  * `stream` and nothing synchronises. */
 
@@ -396,8 +396,8 @@ entq_status entq_region_offsets_device(const uint32_t *d_n_words, uint64_t n_chu
 /* ---- On-device encoder with per-chunk tables (the regions of
  * entq_plan_adaptive, byte for byte equal to entq_encode_tensor_adaptive's)
  * [EntroLLM summary, "Significado y Afirmaciones"]:
- *   1. entq_count_chunks_device_batch -> per-chunk counts (copy to host) ->
- *      entq_build_freq_chunks -> per-chunk tables (copy to device)
+ *   1. entq_count_chunks_device_batch -> per-chunk counts ->
+ *      entq_build_freq_device (or on the host, entq_build_freq_chunks)
  *   2. entq_encode_device_adaptive_batch -> word counts
  *   3. entq_region_offsets_device_adaptive -> offsets
  *   4. entq_pack_device_adaptive_batch -> the regions, each headed by its
@@ -422,6 +422,14 @@ entq_status entq_count_chunks_device_batch(const entq_chunk_count_job *jobs, int
  * (u32), written to freq[256 t ..]; n_threads <= 0 uses all cores. */
 entq_status entq_build_freq_chunks(const uint32_t *counts, uint64_t n_tables, uint16_t *freq,
                                    int n_threads);
+
+/* entq_build_freq on the device: n_tables rows of 256 counts (device, u32
+ * when count_bytes is 4, u64 when 8; aligned to their size) to tables
+ * d_freq[256 t ..] (device u16), one wavefront per table, same results as
+ * the host call for totals below 2^48. Lets the counts -> tables -> encode
+ * sequence run without a host round trip. */
+entq_status entq_build_freq_device(const void *d_counts, uint32_t count_bytes, uint64_t n_tables,
+                                   uint16_t *d_freq, void *stream);
 
 /* entq_encode_device_batch with one table per chunk: job.d_freq holds
  * ceil(n_symbols / chunk_symbols) tables of 256 u16 (each summing to 4096),

@@ -265,3 +265,28 @@ def test_per_chunk_encode_marks_invalid_tables(E):
     torch.cuda.synchronize()
     got = nw.cpu().numpy().view(np.uint32)
     assert got[0] == 0 and got[1] == 0xFFFFFFFF and got[2] == 0xFFFFFFFF
+
+
+def test_device_tables_equal_the_oracle_rule(E):
+    """entq_build_freq_device on u32 and u64 counts: the oracle's table for
+    every row, trimming, shortfall, one-byte and empty rows included."""
+    import torch
+    rng = np.random.default_rng(62)
+    rows = [np.zeros(256, np.int64), np.eye(256, dtype=np.int64)[200] * 65536,
+            np.full(256, 256, np.int64), np.arange(256, dtype=np.int64)]
+    for i in range(4000):
+        c = rng.integers(0, [2, 50, 5000, 1 << 20][i % 4], 256)
+        c[rng.random(256) < rng.random()] = 0
+        if i % 3 == 0:
+            c[int(rng.integers(0, 256))] += int(rng.integers(1, 1 << 30))
+        rows.append(c)
+    counts = np.stack(rows)
+    want = np.stack([oracle.quantize_freqs(r.astype(np.uint64)) if r.sum()
+                     else np.zeros(256, np.uint16) for r in counts])
+    for dt, rows_ok in ((torch.int64, slice(None)), (torch.int32, counts.max(axis=1) < 2**31)):
+        sel = counts[rows_ok]
+        cd = torch.from_numpy(sel.astype(np.int64 if dt == torch.int64 else np.int32)).cuda()
+        fd = torch.full((sel.shape[0], 256), -1, dtype=torch.int16, device="cuda")
+        E.build_freq_device(cd, fd)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(fd.cpu().numpy().view(np.uint16), want[rows_ok])
