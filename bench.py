@@ -310,7 +310,7 @@ ENCODE_METRIC = "encoded symbols/s for 70B-shaped layer encode on the GPU (count
 def bench_encode(args):
     """One step = the on-device encoder over one 70B-shaped layer (855.6 M
     int8 codes, 7 tensors, 65,536-symbol chunks), resident in HBM: byte
-    counts, frequency tables (host), 64-lane rANS encode, region layout and
+    counts, frequency tables, 64-lane rANS encode, region layout and
     packing, ending with the chunk index on the host. The steps cycle over
     --encode-layers layers. The roofline entry is the encode kernel's:
     algorithmic bytes = symbols read + final states and words written."""
@@ -409,8 +409,9 @@ def bench_encode(args):
             "kernel_us_per_step": kind_us,
             "encode_launch_us_p10_p50_p90": [float(np.percentile(enc_us, q)) for q in (10, 50, 90)],
             "step_ms_wall_p10_p50_p90": [1e3 * float(np.percentile(wall, q)) for q in (10, 50, 90)],
-            "note": "value is wall time per layer including the two host reads (counts; word "
-                    "counts and offsets) and the host frequency tables",
+            "note": "value is wall time per layer including the final host read of the word "
+                    "counts, offsets and tables; counts, tables, encode, offsets and packing all "
+                    "run on the GPU",
             "per_chunk_tables": per_chunk,
         },
         "roofline": {
