@@ -99,7 +99,8 @@ def lib():
             "entq_pack_device": (c.c_int, [vp, u64, c.c_uint32, vp, vp, vp, vp]),
             "entq_region_offsets_device": (c.c_int, [vp, u64, u64, vp, vp, vp]),
             "entq_encode_device_batch": (c.c_int, [vp, c.c_int, vp]),
-            "entq_decode_gemm": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
+            "entq_decode_gemm": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp, vp]),
+            "entq_decode_gemm_workspace_bytes": (u64, [vp, c.c_int]),
             "entq_plan_adaptive": (c.c_int, [vp, c.c_int, vp, i64, u64, vp, c.c_size_t, vp,
                                              c.POINTER(vp)]),
             "entq_encode_tensor_adaptive": (c.c_int, [vp, u64, c.c_uint32, c.c_uint32, u64, vp,
@@ -107,7 +108,8 @@ def lib():
             "entq_encode_bound_adaptive": (u64, [u64, c.c_uint32]),
             "entq_count_symbols_device_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_pack_device_batch": (c.c_int, [vp, c.c_int, vp, vp]),
-            "entq_decode_gemm_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
+            "entq_decode_gemm_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp,
+                                                      vp]),
             "entq_count_chunks_device_batch": (c.c_int, [vp, c.c_int, vp]),
             "entq_build_freq_chunks": (c.c_int, [vp, u64, vp, c.c_int]),
             "entq_encode_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp]),
@@ -134,7 +136,7 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_decode_gemm_bf16_split", "entq_count_chunks_device_batch",
             "entq_build_freq_chunks", "entq_encode_device_adaptive_batch",
             "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
-            "entq_build_freq_device"]
+            "entq_build_freq_device", "entq_decode_gemm_workspace_bytes"]
 
 
 def _str(status: int) -> str:
@@ -268,25 +270,53 @@ def _gemm_io(p: Plan, xs, ys):
     return io, m
 
 
-def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
+def _gemm_workspace(p: Plan, m: int, workspace):
+    """The packed-activation workspace for m rows: None when m <= 16 (no
+    gain there) unless given; "none" forces the unpacked reads."""
+    import torch
+    if isinstance(workspace, str) and workspace == "none":
+        return None, 0
+    if workspace is None:
+        if m <= 16:
+            return None, 0
+        n = int(lib().entq_decode_gemm_workspace_bytes(p.handle, int(m)))
+        raw = torch.empty(n + 256, dtype=torch.uint8, device=p.workspace.device)
+        shift = (-raw.data_ptr()) % 256
+        workspace = raw[shift:shift + n]
+        return workspace, n
+    return workspace, workspace.numel()
+
+
+def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None,
+                workspace=None):
     """Y_t = X_t . W_t^T for every tensor t of the plan, W_t the bf16 weights
     the bf16 decode would write, without writing them: xs[t] is a device
     bfloat16 tensor [m, ldx >= cols] (m <= 64, the same m for all), ys[t] a
-    device float32 tensor [m, ldy >= rows]."""
+    device float32 tensor [m, ldy >= rows]. workspace: a device uint8 tensor
+    (256-byte aligned, entq_decode_gemm_workspace_bytes long) for the packed
+    activations, None to allocate one when m > 16, or "none"."""
     io, m = _gemm_io(p, xs, ys)
+    ws, wsb = _gemm_workspace(p, m, workspace)
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)  # allocated here, used on another stream
     st = lib().entq_decode_gemm(p.handle, _ptr(compressed), _ptr(scales) or None,
                                 _ptr(io) if len(xs) else None, int(m),
+                                _ptr(ws) if ws is not None else None, int(wsb),
                                 _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm")
 
 
 def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=None,
-                           stream=None):
+                           stream=None, workspace=None):
     """decode_gemm for BF16 weights given as a coded exponent stream plus raw
     sign+mantissa bytes (as decode_bf16_split takes them)."""
     io, m = _gemm_io(p, xs, ys)
+    ws, wsb = _gemm_workspace(p, m, workspace)
+    if ws is not None and workspace is None and stream is not None:
+        ws.record_stream(stream)
     st = lib().entq_decode_gemm_bf16_split(p.handle, _ptr(exp_stream), _ptr(signmant),
                                            _ptr(io) if len(xs) else None, int(m),
+                                           _ptr(ws) if ws is not None else None, int(wsb),
                                            _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm_bf16_split")
 

@@ -37,7 +37,7 @@ constexpr uint32_t kGemmM = 16;      // activation rows of one MFMA tile
 constexpr int kGemmMaxGroups = 4;    // up to 64 activation rows per launch
 
 struct GemmTensor {
-    const uint16_t *x;   // bf16 activations
+    const uint16_t *x;   // bf16 activations (row-major, ldx), or their packed copy
     float *y;
     uint64_t ldx, ldy;   // row strides in elements
     uint32_t chunk_base; // first DevChunk of the tensor
@@ -60,8 +60,11 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // MT: groups of 16 activation rows. SPLIT: the weights are BF16 rebuilt from
-// a coded exponent stream and raw sign+mantissa bytes (no scales).
-template <int MT, bool SPLIT>
+// a coded exponent stream and raw sign+mantissa bytes (no scales). PACKED:
+// x is the packed copy written by pack_activations (below), so each wave's
+// activation fragments of a block are one contiguous run of MT x 512 bytes
+// instead of 16 rows x 32 bytes per group.
+template <int MT, bool SPLIT, bool PACKED>
 __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restrict__ tables,
                                                         const DevChunk *__restrict__ chunks,
                                                         const uint8_t *__restrict__ blob,
@@ -135,7 +138,10 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
 #pragma unroll
             for (int g = 0; g < MT; ++g) {
                 a[g] = make_uint2(0, 0);
-                if (16u * g + a_row < args.m)
+                if (PACKED)  // rows past m are zeros in the packed copy
+                    a[g] = *reinterpret_cast<const uint2 *>(
+                        gt.x + (((uint64_t)kb * kWaves + wave) * MT + g) * 256u + 4u * lane);
+                else if (16u * g + a_row < args.m)
                     a[g] = *reinterpret_cast<const uint2 *>(xa + g * group_stride +
                                                             (uint64_t)kb * kBlockSyms);
             }
@@ -197,57 +203,129 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     wait_vm<0>();  // no global->LDS load may outlive the workgroup
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool PACKED>
 void launch_groups(int groups_m, dim3 grid, hipStream_t st, const entq_plan_t *plan,
                    const uint8_t *blob, const float *scales, const uint8_t *signmant,
                    int32_t *status, const GemmArgs &args) {
     const dim3 block(kThreads);
     if (groups_m == 1)
-        hipLaunchKernelGGL((decode_gemm<1, SPLIT>), grid, block, 0, st, plan->d_tables,
+        hipLaunchKernelGGL((decode_gemm<1, SPLIT, PACKED>), grid, block, 0, st, plan->d_tables,
                            plan->d_chunks, blob, scales, signmant, status, args);
     else if (groups_m == 2)
-        hipLaunchKernelGGL((decode_gemm<2, SPLIT>), grid, block, 0, st, plan->d_tables,
+        hipLaunchKernelGGL((decode_gemm<2, SPLIT, PACKED>), grid, block, 0, st, plan->d_tables,
                            plan->d_chunks, blob, scales, signmant, status, args);
     else if (groups_m == 3)
-        hipLaunchKernelGGL((decode_gemm<3, SPLIT>), grid, block, 0, st, plan->d_tables,
+        hipLaunchKernelGGL((decode_gemm<3, SPLIT, PACKED>), grid, block, 0, st, plan->d_tables,
                            plan->d_chunks, blob, scales, signmant, status, args);
     else
-        hipLaunchKernelGGL((decode_gemm<4, SPLIT>), grid, block, 0, st, plan->d_tables,
+        hipLaunchKernelGGL((decode_gemm<4, SPLIT, PACKED>), grid, block, 0, st, plan->d_tables,
                            plan->d_chunks, blob, scales, signmant, status, args);
+}
+
+// The packed copy of one tensor's activations: for block kb (256 columns),
+// wave w, group g and lane l, the 8 bytes the wave's A operand takes, at
+// element ((kb * 16 + w) * MT + g) * 256 + 4 l: row 16 g + (l mod 16),
+// columns 256 kb + 16 w + 4 (l / 16) .. +3, zeros for rows m and beyond.
+// One thread per 8 bytes, consecutive threads reading consecutive columns.
+struct PackTensor {
+    const uint16_t *x;
+    uint16_t *xp;
+    uint64_t ldx;
+    uint32_t cols, first_block;
+};
+struct PackArgs {
+    PackTensor t[kGemmMaxTensors];
+    uint32_t n_tensors, m, groups;
+};
+
+__global__ __launch_bounds__(256) void pack_activations(PackArgs args) {
+    uint32_t ti = 0;
+    while (ti + 1 < args.n_tensors && args.t[ti + 1].first_block <= blockIdx.x) ++ti;
+    const PackTensor &pt = args.t[ti];
+    const uint64_t i = (uint64_t)(blockIdx.x - pt.first_block) * 256 + threadIdx.x;
+    const uint32_t quads = pt.cols / 4;
+    const uint64_t r = i / quads;               // activation row
+    if (r >= 16ull * args.groups) return;
+    const uint32_t c4 = (uint32_t)(i % quads);  // column quad
+    uint2 v = make_uint2(0, 0);
+    if (r < args.m) v = *reinterpret_cast<const uint2 *>(pt.x + r * pt.ldx + 4ull * c4);
+    const uint32_t kb = c4 / 64, q = c4 % 64;
+    const uint32_t w = q / 4, lane = (q % 4) * 16 + (uint32_t)(r % 16), g = (uint32_t)(r / 16);
+    *reinterpret_cast<uint2 *>(pt.xp + (((uint64_t)kb * kWaves + w) * args.groups + g) * 256u +
+                               4u * lane) = v;
 }
 
 }  // namespace
 
+// Bytes of one tensor's packed activations (16-row groups, 256-byte aligned).
+uint64_t packed_bytes(uint32_t cols, int groups_m) {
+    return ((uint64_t)16 * groups_m * cols * 2 + 255) & ~(uint64_t)255;
+}
+
+uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m) {
+    const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
+    uint64_t total = 0;
+    for (int t = 0; t < plan->n_tensors; ++t)
+        if (plan->host_tensors[t].n_symbols)
+            total += packed_bytes(plan->host_tensors[t].cols, groups_m);
+    return total;
+}
+
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
-                       const uint8_t *signmant, const entq_gemm_io *io, int m, int32_t *status,
-                       void *stream) {
+                       const uint8_t *signmant, const entq_gemm_io *io, int m,
+                       uint8_t *workspace, int32_t *status, void *stream) {
     GemmArgs args = {};
     args.m = (uint32_t)m;
-    uint64_t blocks = 0;
+    PackArgs pack = {};
+    pack.m = (uint32_t)m;
+    uint64_t blocks = 0, pack_blocks = 0, ws_off = 0;
     const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
+    pack.groups = (uint32_t)groups_m;
+    const hipStream_t st = (hipStream_t)stream;
     auto flush = [&]() -> int {
         if (args.n_tensors == 0) return ENTQ_OK;
         const uint8_t *b = static_cast<const uint8_t *>(blob);
-        if (signmant)
-            launch_groups<true>(groups_m, dim3((unsigned)blocks), (hipStream_t)stream, plan, b,
-                                scales, signmant, status, args);
-        else
-            launch_groups<false>(groups_m, dim3((unsigned)blocks), (hipStream_t)stream, plan, b,
-                                 scales, signmant, status, args);
+        const dim3 grid((unsigned)blocks);
+        if (workspace) {
+            hipLaunchKernelGGL(pack_activations, dim3((unsigned)pack_blocks), dim3(256), 0, st,
+                               pack);
+            if (signmant)
+                launch_groups<true, true>(groups_m, grid, st, plan, b, scales, signmant, status,
+                                          args);
+            else
+                launch_groups<false, true>(groups_m, grid, st, plan, b, scales, signmant, status,
+                                           args);
+        } else if (signmant) {
+            launch_groups<true, false>(groups_m, grid, st, plan, b, scales, signmant, status, args);
+        } else {
+            launch_groups<false, false>(groups_m, grid, st, plan, b, scales, signmant, status,
+                                        args);
+        }
         args.n_tensors = 0;
+        pack.n_tensors = 0;
         blocks = 0;
+        pack_blocks = 0;
         return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
     };
     for (int t = 0; t < plan->n_tensors; ++t) {
         const HostTensor &h = plan->host_tensors[t];
         if (h.n_symbols == 0) continue;
         const uint64_t groups = ((uint64_t)h.n_chunks + kWaves - 1) / kWaves;
-        if (args.n_tensors == (uint32_t)kGemmMaxTensors || blocks + groups > 0x7FFFFFFFull) {
-            const int st = flush();
-            if (st != ENTQ_OK) return st;
+        const uint64_t pb = ((uint64_t)16 * groups_m * (h.cols / 4) + 255) / 256;
+        if (args.n_tensors == (uint32_t)kGemmMaxTensors || blocks + groups > 0x7FFFFFFFull ||
+            pack_blocks + pb > 0x7FFFFFFFull) {
+            const int r = flush();
+            if (r != ENTQ_OK) return r;
         }
         GemmTensor &g = args.t[args.n_tensors++];
         g.x = static_cast<const uint16_t *>(io[t].d_x);
+        if (workspace) {
+            uint16_t *xp = reinterpret_cast<uint16_t *>(workspace + ws_off);
+            pack.t[pack.n_tensors++] = {g.x, xp, io[t].ldx, h.cols, (uint32_t)pack_blocks};
+            pack_blocks += pb;
+            ws_off += packed_bytes(h.cols, groups_m);
+            g.x = xp;
+        }
         g.y = io[t].d_y;
         g.ldx = io[t].ldx;
         g.ldy = io[t].ldy;
@@ -291,30 +369,51 @@ entq_status check_gemm_args(const entq_plan_t *plan, const entq_gemm_io *io, int
     return ENTQ_OK;
 }
 
+// An optional workspace for the packed activations: null, or 256-byte
+// aligned and at least entq_decode_gemm_workspace_bytes.
+entq_status check_workspace(const entq_plan_t *plan, int m, void *ws, uint64_t bytes) {
+    if (!ws) return ENTQ_OK;
+    if ((uintptr_t)ws % 256) return ENTQ_EALIGN;
+    return bytes < entq::gemm_workspace_bytes(plan, m) ? ENTQ_EWORKSPACE : ENTQ_OK;
+}
+
 }  // namespace
+
+uint64_t entq_decode_gemm_workspace_bytes(const entq_plan_t *plan, int m) {
+    if (!plan || m < 1 || m > (int)entq::kGemmM * entq::kGemmMaxGroups) return 0;
+    return entq::gemm_workspace_bytes(plan, m);
+}
 
 entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
+                             void *d_workspace, uint64_t workspace_bytes,
                              int32_t *d_chunk_status, void *stream) {
-    const entq_status st = check_gemm_args(plan, io, m, false);
+    entq_status st = check_gemm_args(plan, io, m, false);
     if (st != ENTQ_OK) return st;
     if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
     if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    st = check_workspace(plan, m, d_workspace, workspace_bytes);
+    if (st != ENTQ_OK) return st;
     return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, nullptr, io, m,
+                                                 static_cast<uint8_t *>(d_workspace),
                                                  d_chunk_status, stream);
 }
 
 entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                         const uint8_t *d_signmant, const entq_gemm_io *io,
-                                        int m, int32_t *d_chunk_status, void *stream) {
-    const entq_status st = check_gemm_args(plan, io, m, true);
+                                        int m, void *d_workspace, uint64_t workspace_bytes,
+                                        int32_t *d_chunk_status, void *stream) {
+    entq_status st = check_gemm_args(plan, io, m, true);
     if (st != ENTQ_OK) return st;
     if (plan->n_chunks && (!d_exp_stream || !d_signmant)) return ENTQ_EINVAL;
     if ((uintptr_t)d_signmant % 16) return ENTQ_EALIGN;
     for (int t = 0; t < plan->n_tensors; ++t)
         if (plan->host_tensors[t].n_symbols && plan->host_tensors[t].out_elem_offset % 16)
             return ENTQ_EALIGN;
+    st = check_workspace(plan, m, d_workspace, workspace_bytes);
+    if (st != ENTQ_OK) return st;
     return (entq_status)entq::launch_decode_gemm(plan, d_exp_stream, nullptr, d_signmant, io, m,
+                                                 static_cast<uint8_t *>(d_workspace),
                                                  d_chunk_status, stream);
 }
 

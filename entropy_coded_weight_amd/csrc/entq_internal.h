@@ -112,9 +112,11 @@ int launch_decode_adaptive(const entq_plan_t *plan, int mode, const void *blob, 
                            const float *scales, const uint8_t *signmant, int32_t *status,
                            void *stream);
 // Fused decode + product with activations (entq_decode_gemm.hip).
+// workspace: null, or room for the packed activations (gemm_workspace_bytes).
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
                        const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
-                       int32_t *status, void *stream);
+                       uint8_t *workspace, int32_t *status, void *stream);
+uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m);
 // Workgroups of the decode kernels that fit on the current device at once
 // (compute units x workgroups per compute unit); 0 if HIP cannot tell.
 int64_t resident_workgroups();

@@ -261,7 +261,16 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * exponent streams: entq_decode_gemm_bf16_split),
  * cols a multiple of 256, chunk_symbols a multiple of cols (every chunk
  * holds whole rows). d_chunk_status as in entq_decode. Enqueued on stream;
- * the summation order is fixed (results are reproducible run to run). */
+ * the summation order is fixed (results are reproducible run to run).
+ *
+ * d_workspace: NULL, or device memory (256-byte aligned, at least
+ * entq_decode_gemm_workspace_bytes(plan, m) bytes, else ENTQ_EALIGN /
+ * ENTQ_EWORKSPACE) into which the call first copies each tensor's
+ * activations in the order the kernel's waves read them, so that every wave
+ * reads one contiguous run per 256 columns instead of 16 rows of 32 bytes.
+ * The results are the same bit for bit either way; with more than 16
+ * activation rows the workspace makes the call several times faster. The
+ * workspace must not be used by other work while the call runs. */
 typedef struct {
     const void *d_x;
     uint64_t ldx;
@@ -269,8 +278,14 @@ typedef struct {
     uint64_t ldy;
 } entq_gemm_io;
 
+/* Bytes of workspace entq_decode_gemm and entq_decode_gemm_bf16_split take
+ * for this plan and m (0 for invalid arguments): for each non-empty tensor,
+ * 2 bytes x 16 ceil(m / 16) rows x cols, rounded up to 256. */
+uint64_t entq_decode_gemm_workspace_bytes(const entq_plan_t *plan, int m);
+
 entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
+                             void *d_workspace, uint64_t workspace_bytes,
                              int32_t *d_chunk_status, void *stream);
 
 /* The same product for BF16 weights stored as a coded exponent stream plus
@@ -282,7 +297,8 @@ entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
  * entq_decode_gemm. */
 entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
                                         const uint8_t *d_signmant, const entq_gemm_io *io,
-                                        int m, int32_t *d_chunk_status, void *stream);
+                                        int m, void *d_workspace, uint64_t workspace_bytes,
+                                        int32_t *d_chunk_status, void *stream);
 
 /* ---- On-device encoder (one wavefront per chunk; same regions as the
  * host encoder, byte for byte) ----

@@ -56,7 +56,7 @@ def _setup(E, specs):
     return b, p, blob, scales
 
 
-def _run(E, p, blob, scales, xs_host, specs, pad_x=0, pad_y=0):
+def _run(E, p, blob, scales, xs_host, specs, pad_x=0, pad_y=0, workspace=None):
     """xs_host: list of float32 arrays [m, cols] (values already bf16)."""
     import torch
     xs, ys = [], []
@@ -68,7 +68,7 @@ def _run(E, p, blob, scales, xs_host, specs, pad_x=0, pad_y=0):
         ys.append(torch.full((m, sp["rows"] + pad_y), float("nan"), dtype=torch.float32,
                              device="cuda"))
     status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
-    E.decode_gemm(p, blob, scales, [x[:, :] for x in xs], ys, status)
+    E.decode_gemm(p, blob, scales, [x[:, :] for x in xs], ys, status, workspace=workspace)
     torch.cuda.synchronize()
     assert (status.cpu().numpy() == 0).all()
     return [y.cpu().numpy() for y in ys]
@@ -127,6 +127,44 @@ def test_random_activations_within_the_accumulation_bound(E):
             assert (np.abs(got - ref) <= bound + 1e-30).all(), (t, m)
             if pad_y:
                 assert np.isnan(ys[t][:, sp["rows"]:]).all()  # nothing written past the rows
+
+
+def test_packed_activations_give_the_same_bits(E):
+    """With a workspace the activations are first copied into the waves'
+    read order; the products are the same bit for bit, padded strides and
+    partial 16-row groups included."""
+    import torch
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    rng = np.random.default_rng(9)
+    for m, pad_x in ((1, 0), (16, 4), (17, 0), (40, 12), (64, 0)):
+        _say(f"packed vs unpacked activations, m={m}")
+        xs = [rng.standard_normal((m, sp["cols"])).astype(np.float32) for sp in specs]
+        n = int(E.lib().entq_decode_gemm_workspace_bytes(p.handle, m))
+        groups = -(-m // 16)
+        assert n == sum(-(-32 * groups * sp["cols"] // 256) * 256 for sp in specs)
+        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # stale bytes
+        plain = _run(E, p, blob, scales, xs, specs, pad_x, workspace="none")
+        packed = _run(E, p, blob, scales, xs, specs, pad_x, workspace=ws)
+        for t in range(len(specs)):
+            assert np.array_equal(plain[t].view(np.uint32), packed[t].view(np.uint32)), (t, m)
+
+
+def test_workspace_size_and_alignment_are_checked(E):
+    import torch
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    m = 33
+    xs = [torch.zeros(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+    ys = [torch.zeros(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+    n = int(E.lib().entq_decode_gemm_workspace_bytes(p.handle, m))
+    raw = torch.empty(n + 512, dtype=torch.uint8, device="cuda")
+    base = (-raw.data_ptr()) % 256
+    with pytest.raises(E.EntqError):
+        E.decode_gemm(p, blob, scales, xs, ys, workspace=raw[base:base + n - 256])  # short
+    with pytest.raises(E.EntqError):
+        E.decode_gemm(p, blob, scales, xs, ys, workspace=raw[base + 16:base + 16 + n])  # 16 off
+    assert int(E.lib().entq_decode_gemm_workspace_bytes(p.handle, 65)) == 0
 
 
 def test_results_are_reproducible(E):
