@@ -202,3 +202,19 @@ def test_workspace_bytes_grows_with_inputs(E):
     b = E.lib().entq_plan_workspace_bytes(7, 13056)
     assert 0 < a < b
     assert b >= 7 * 4096 * 8 + 13056 * 48
+
+
+def test_missing_library_fails_loudly():
+    """No CPU fallback: without the built library every call raises."""
+    import subprocess
+    import sys
+    code = ("import entropy_coded_weight_amd as E\n"
+            "E.LIB_PATH = '/nonexistent/libentq.so'\n"
+            "E._lib = None\n"
+            "try:\n"
+            "    E.build_freq(__import__('numpy').ones(256, 'uint64'))\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and "raised" in r.stdout and "no CPU fallback" in r.stdout
