@@ -51,8 +51,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=80,
                     help="layers in the model (80 is the workload; fewer only for quick checks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tensors", type=int, default=5,
-                    help="tensors of layer 0 the oracle decodes for the CPU baseline")
+    ap.add_argument("--cpu-sample-tensors", type=int, default=7,
+                    help="tensors of layer 0 the oracle decodes for the CPU baseline "
+                         "(7: the whole layer, about 7 s on one core)")
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead", "adaptive"),
                     default="decode",
