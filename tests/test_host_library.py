@@ -218,3 +218,36 @@ def test_missing_library_fails_loudly():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0 and "raised" in r.stdout and "no CPU fallback" in r.stdout
+
+
+def test_device_calls_validate_before_launching(E):
+    """Argument checks of the device-encoder and fused-product entry points
+    return their codes before any HIP call (fake device addresses)."""
+    L = E.lib()
+    fake = 1 << 20                                   # 256-byte aligned, never touched
+    # per-chunk counts: chunk size not a multiple of 64, then a misaligned array
+    job = np.zeros(1, E.CHUNK_COUNT_JOB)
+    job[0] = (fake, 4096, 100, 0, fake)
+    assert L.entq_count_chunks_device_batch(job.ctypes.data, 1, None) == -1
+    job[0] = (fake + 8, 4096, 64, 0, fake)
+    assert L.entq_count_chunks_device_batch(job.ctypes.data, 1, None) == -4
+    assert L.entq_count_chunks_device_batch(None, -1, None) == -1
+    # device tables: only 4- and 8-byte counts
+    assert L.entq_build_freq_device(fake, 3, 1, fake, None) == -1
+    assert L.entq_build_freq_device(fake + 4, 8, 1, fake, None) == -4
+    assert L.entq_build_freq_device(None, 4, 0, None, None) == 0  # nothing to do
+    # per-chunk encode: missing tables, then a too-small scratch
+    enc = np.zeros(1, E.ENCODE_JOB)
+    enc[0] = (fake, 8192, 4096, 0, 0, fake, 1 << 30, fake)
+    assert L.entq_encode_device_adaptive_batch(enc.ctypes.data, 1, None) == -1
+    enc[0] = (fake, 8192, 4096, 0, fake, fake, 16, fake)
+    assert L.entq_encode_device_adaptive_batch(enc.ctypes.data, 1, None) == -5
+    # regions headed by tables: misaligned offsets, misaligned tables
+    assert L.entq_region_offsets_device_adaptive(fake, 4, 8, fake, fake, None) == -4
+    pack = np.zeros(1, E.PACK_ADAPTIVE_JOB)
+    pack[0] = (fake, 8192, 4096, 0, fake, fake, fake + 2)
+    assert L.entq_pack_device_adaptive_batch(pack.ctypes.data, 1, fake, None) == -4
+    pack[0] = (fake, 8192, 4096, 0, fake, fake, 0)
+    assert L.entq_pack_device_adaptive_batch(pack.ctypes.data, 1, fake, None) == -1
+    # fused product: workspace size of no plan
+    assert L.entq_decode_gemm_workspace_bytes(None, 16) == 0
