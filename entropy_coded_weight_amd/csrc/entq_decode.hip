@@ -144,7 +144,10 @@ struct alignas(16) WaveStage {
     uint8_t sm[MODE == kModeSplit ? 2 : 1][MODE == kModeSplit ? kBlockSyms : 16];
 };
 
-template <int MODE>
+// PRIO: progress-based wave priority (below); off for launches with one
+// chunk per workgroup, where the waves do not compete and its per-block
+// bookkeeping only lengthens each wave's chain.
+template <int MODE, bool PRIO>
 __global__ __launch_bounds__(kThreads) void decode_stream(
     const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
     const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
@@ -173,11 +176,12 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     // workgroup on a CU, and the younger waves of a workgroup, then finish
     // long after the rest, with the CU half idle.)
     uint32_t my_blocks = 0;
-    for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
-        my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
+    if (PRIO)
+        for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
+            my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
     const uint32_t quarter = my_blocks / 4 ? my_blocks / 4 : 1;
     uint32_t done = 0, prio_at = quarter, prio = 3;
-    __builtin_amdgcn_s_setprio(3);
+    if (PRIO) __builtin_amdgcn_s_setprio(3);
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         const uint8_t *region = blob + ch.byte_offset;
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
 
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
-            if (++done == prio_at) {
+            if (PRIO && ++done == prio_at) {
                 prio_at += quarter;
                 --prio;
                 if (prio == 2) __builtin_amdgcn_s_setprio(2);
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
 template <int MODE>
 __host__ int64_t stream_occupancy() {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_stream<MODE>, kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_stream<MODE, true>, kThreads, 0) !=
         hipSuccess)
         return 0;
     return blocks;
@@ -298,8 +302,14 @@ int launch_mode(const entq_plan_t *plan, bool stream, int64_t first, int64_t cou
     if (count <= 0) return ENTQ_OK;
     if (first + count > 0x7FFFFFFF) return ENTQ_EINVAL;
     const dim3 grid((unsigned)count), block(kThreads);
-    if (stream)
-        hipLaunchKernelGGL(decode_stream<MODE>, grid, block, 0, s, plan->d_tables,
+    const bool prio = (MODE == kModeBf16 ? plan->max_task_chunks_rows
+                                         : plan->max_task_chunks_blocks) > 1;
+    if (stream && prio)
+        hipLaunchKernelGGL((decode_stream<MODE, true>), grid, block, 0, s, plan->d_tables,
+                           plan->d_tensors, plan->d_chunks, plan->d_tasks, (uint32_t)first, blob,
+                           out, scales, signmant, status);
+    else if (stream)
+        hipLaunchKernelGGL((decode_stream<MODE, false>), grid, block, 0, s, plan->d_tables,
                            plan->d_tensors, plan->d_chunks, plan->d_tasks, (uint32_t)first, blob,
                            out, scales, signmant, status);
     else

@@ -87,6 +87,10 @@ struct entq_plan_s {
     // n_tasks_blocks) only chunk sizes; the rest neither.
     int64_t n_tasks_rows;
     int64_t n_tasks_blocks;
+    // The most chunks any task of [0, n_tasks_rows) / [0, n_tasks_blocks)
+    // holds (1: a latency-bound launch, one chunk per workgroup).
+    uint32_t max_task_chunks_rows;
+    uint32_t max_task_chunks_blocks;
     uint64_t blob_bytes;
     uint64_t out_elems;
     uint64_t scale_rows;

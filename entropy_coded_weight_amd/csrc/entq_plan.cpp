@@ -308,6 +308,12 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     p->n_tasks = n_tasks;
     p->n_tasks_rows = group_end[0];
     p->n_tasks_blocks = group_end[1];
+    p->max_task_chunks_rows = p->max_task_chunks_blocks = 0;
+    for (int64_t k = 0; k < group_end[1]; ++k) {
+        const uint32_t c = task_list[k].n_chunks;
+        if (k < group_end[0]) p->max_task_chunks_rows = std::max(p->max_task_chunks_rows, c);
+        p->max_task_chunks_blocks = std::max(p->max_task_chunks_blocks, c);
+    }
     p->blob_bytes = blob_bytes;
     p->out_elems = out_elems;
     p->scale_rows = scale_rows;
