@@ -363,3 +363,41 @@ def test_nan_and_inf_scales_both_kernels(E, cols):
         specs.append(dict(name=f"k{kind}", kind=kind, rows=rows, cols=cols, chunk_symbols=512,
                           symbols=sym, scales=sc))
     check_codes_and_bf16(E, specs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_batches_of_shapes_chunk_sizes_and_kinds(E, seed):
+    """Batches of 1-5 tensors with random rows, row lengths (block-aligned or
+    not), chunk sizes (multiples of 64 up to 2^16), kinds and spreads, so both
+    kernels get a share: codes and bf16 equal the oracle's."""
+    rng = np.random.default_rng(1000 + seed)
+    specs = []
+    for i in range(int(rng.integers(1, 6))):
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.choice([64, 192, 256, 320, 512, 768, 1000, 2048, 4096, 4160]))
+        C = int(rng.choice([64, 256, 512, 768, 4096, 16384, 65536]))
+        if rng.random() < 0.3:
+            sp = synth.e4m3_matrix(rows=rows, cols=cols)[0]
+            sp["chunk_symbols"] = C
+        else:
+            sp = synth.random_int8_tensor(rows, cols, float(rng.uniform(0.3, 6.0)),
+                                          100 * seed + i, C)
+        specs.append(sp)
+    _say(f"random batch {seed}: " + ", ".join(f"{s['rows']}x{s['cols']}/C{s['chunk_symbols']}"
+                                             for s in specs))
+    check_codes_and_bf16(E, specs)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_exponent_streams(E, seed):
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 300_000))
+    C = int(rng.choice([64, 256, 4096, 65536]))
+    w = synth.bf16_weights(1, n, sigma=float(rng.choice([0.02, 1.0, 300.0])))[0]["bf16"]
+    e, sm = oracle.bf16_split(w)
+    c = oracle.encode_container([dict(kind=oracle.KIND_BF16EXP, rows=1, cols=n, symbols=e,
+                                      chunk_symbols=C)])
+    _say(f"random exponent stream {seed}: {n} weights, C{C}")
+    got, gst = gpu_decode(E, c, None, split_sm=sm)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, w)
