@@ -81,7 +81,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the decode has no cross-GPU step: each GPU decodes the chunks of its own shard", file=sys.stderr)
         sys.exit(2)
     if args.path == "encode":
