@@ -55,14 +55,16 @@ def parse():
                     help="tensors of layer 0 the oracle decodes for the CPU baseline "
                          "(7: the whole layer, about 7 s on one core)")
     ap.add_argument("--threads", type=int, default=0)
-    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead", "adaptive"),
+    ap.add_argument("--path", choices=("decode", "encode", "overlap", "fused", "lmhead", "adaptive",
+                             "workloads"),
                     default="decode",
                     help="decode: the layer-by-layer decode (the headline line); encode: the "
                          "on-device encoder over 70B-shaped layers; overlap: decode of layer "
                          "l+1 overlapped with layer l's projection GEMMs; fused: decode and "
                          "product with m activation rows in one kernel vs decode + GEMM; lmhead: "
                          "the 32,000 x 8,192 output projection decoded on its own; adaptive: "
-                         "per-chunk tables against shared tables")
+                         "per-chunk tables against shared tables; workloads: the smaller "
+                         "workloads (and one 70B-shaped layer) each decoded alone")
     ap.add_argument("--tokens", type=str, default="",
                     help="activation rows per GEMM, comma-separated; the first value is the "
                          "line's (overlap default 2048,256,16; fused default 16,4,1,32,64)")
@@ -94,6 +96,8 @@ def main():
         return bench_lm_head(args)
     if args.path == "adaptive":
         return bench_adaptive(args)
+    if args.path == "workloads":
+        return bench_workloads(args)
     import torch
 
     import entropy_coded_weight_amd as E
@@ -1164,6 +1168,163 @@ def adaptive_cpu_baseline(E, sample, layer0, out, stream, torch):
     return {"value": n / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0, first 3 tensors ({n} params): single-threaded C oracle "
                       "per-chunk-table decode + dequant + RNE bf16"}
+
+
+WORKLOADS_METRIC = "decoded params/s per workload, each decoded alone with caches flushed"
+
+
+def bench_workloads(args):
+    """The smaller workloads, each decoded alone: 256 x 256 Laplace int8
+    codes (4,096-symbol chunks; codes and bf16), the e4m3 4096 x 4096 matrix
+    (codes and bf16), one LLaMA-2-13B block (7 int8 tensors, bf16), the
+    8192 x 8192 BF16 matrix from its coded exponents + raw sign/mantissa
+    bytes, and one 70B-shaped layer for comparison. Each timed launch follows
+    a 512 MB read that evicts the last-level cache; median of the per-launch
+    HIP events. Lossless outputs (codes, the BF16 matrix) are compared with
+    their sources; the bf16 outputs of the two small workloads with the
+    oracle (the CPU-baseline leg)."""
+    import torch
+
+    import entropy_coded_weight_amd as E
+    import synth
+
+    E.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    nthreads = args.threads or synth.default_threads()
+    # Before each timed launch, a read of 512 MB of clean data evicts the
+    # last-level cache (256 MB) without leaving dirty lines whose write-back
+    # would land inside the timed launch.
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    reps = max(args.steps, 20)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        times = []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sum)
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            z.record(stream)
+            z.synchronize()
+            times.append(a.elapsed_time(z) * 1e3)
+        return float(np.median(times)), float(np.percentile(times, 10)), float(np.percentile(times, 90))
+
+    rows_out, checks, kept = [], {}, {}
+
+    def coded(name, specs, outs):
+        b = E.encode_batch(specs, n_threads=nthreads)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+        blob = torch.from_numpy(b.blob).to(dev)
+        sc = torch.from_numpy(np.concatenate([np.asarray(s["scales"], np.float32)
+                                              for s in specs])).to(dev)
+        n = b.out_elems
+        for kind in outs:
+            if kind == "codes":
+                out = torch.empty(n, dtype=torch.uint8, device=dev)
+                med, p10, p90 = timed(lambda: E.decode(p, blob, out, E.OUT_CODES, None, None, stream))
+                src = np.concatenate([np.asarray(s["symbols"]).view(np.uint8).ravel() for s in specs])
+                checks[f"{name} codes equal the source"] = bool(np.array_equal(out.cpu().numpy(), src))
+                written = n
+            else:
+                out = torch.empty(n, dtype=torch.int16, device=dev)
+                med, p10, p90 = timed(lambda: E.decode(p, blob, out, E.OUT_BF16, sc, None, stream))
+                kept[name] = (specs, b, out.cpu().numpy().view(np.uint16))
+                written = 2 * n
+            alg = b.blob.size + (4 * sc.numel() if kind == "bf16" else 0) + written
+            rows_out.append({"workload": name, "output": kind, "params": n,
+                             "chunks": int(p.n_chunks), "bits_per_param": 8.0 * b.blob.size / n,
+                             "us_median": med, "us_p10": p10, "us_p90": p90,
+                             "params_per_s": n / (med / 1e6), "alg_gbs": alg / (med / 1e6) / 1e9})
+            log(f"{name} -> {kind}: {med:.1f} us (p10 {p10:.1f}, p90 {p90:.1f}), "
+                f"{rows_out[-1]['alg_gbs']:.0f} GB/s")
+
+    coded("laplace int8 256x256", synth.tiny_int8_laplace(), ("codes", "bf16"))
+    coded("e4m3 4096x4096", synth.e4m3_matrix(), ("codes", "bf16"))
+    coded("llama2-13b block", synth.llama2_13b_block(), ("bf16",))
+
+    w = synth.bf16_weights()[0]
+    e, sm = E.bf16_split(w["bf16"], n_threads=nthreads)
+    b = E.encode_batch([dict(kind=E.KIND_BF16EXP, rows=w["rows"], cols=w["cols"],
+                             chunk_symbols=w["chunk_symbols"], symbols=e)], n_threads=nthreads)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob, smd = torch.from_numpy(b.blob).to(dev), torch.from_numpy(sm).to(dev)
+    n = w["rows"] * w["cols"]
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    med, p10, p90 = timed(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))
+    checks["bf16 8192x8192 equals the source weights"] = bool(
+        np.array_equal(out.cpu().numpy().view(np.uint16), w["bf16"]))
+    rows_out.append({"workload": "bf16 8192x8192 exponent stream + sign/mantissa", "output": "bf16",
+                     "params": n, "chunks": int(p.n_chunks),
+                     "bits_per_param": 8.0 * (b.blob.size + n) / n,
+                     "us_median": med, "us_p10": p10, "us_p90": p90,
+                     "params_per_s": n / (med / 1e6),
+                     "alg_gbs": (b.blob.size + n + 2 * n) / (med / 1e6) / 1e9})
+    log(f"bf16 8192x8192 split: {med:.1f} us, {rows_out[-1]['alg_gbs']:.0f} GB/s")
+    del blob, smd, out
+
+    coded("llama2-70b layer 0", synth.llama2_70b_layer(0, nthreads=nthreads), ("bf16",))
+    del flush
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t = time.perf_counter()
+        n_s = 0
+        for name in ("laplace int8 256x256", "e4m3 4096x4096"):
+            specs, bb, gpu = kept[name]
+            sp = specs[0]
+            desc = np.stack([bb.chunks["n_symbols"], bb.chunks["n_words"], bb.chunks["byte_offset"],
+                             bb.chunks["elem_offset"]], axis=1).astype(np.uint64)
+            sym, st = oracle.decode_tensor(bb.blob, desc, bb.freq[0], sp["rows"] * sp["cols"])
+            bits = oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"])
+            checks[f"{name} bf16 equals the oracle"] = bool((st == 0).all() and np.array_equal(bits, gpu))
+            n_s += sp["rows"] * sp["cols"]
+        dt = time.perf_counter() - t
+        cpu = {"value": n_s / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole 256x256 Laplace and e4m3 4096x4096 workloads: single-threaded "
+                         "C oracle decode + dequant + RNE bf16"}
+        log(f"cpu oracle: {n_s} params in {dt:.2f}s")
+    for k, ok in checks.items():
+        log(f"check: {k}: {ok}")
+    if not all(checks.values()):
+        raise SystemExit("a workload's output differs from its source or from the oracle")
+    main_row = next(r for r in rows_out if r["workload"] == "llama2-13b block")
+    rec = {
+        "metric": WORKLOADS_METRIC,
+        "value": main_row["params_per_s"],
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": args.warmup,
+        "ms_per_step": main_row["us_median"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f32->bf16",
+        "data": "synthetic (seeded codes and weights of the stated distributions; no trained weights)",
+        "config": {
+            "workload": "llama2-13b block (7 int8 tensors, 317,194,240 params) -> bf16; the other "
+                        "workloads in 'workloads'",
+            "workloads": rows_out,
+            "timing": "per launch, after a 512 MB read that evicts the last-level cache; median",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": main_row["alg_gbs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": main_row["alg_gbs"] / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

@@ -135,14 +135,19 @@ __global__ __launch_bounds__(kThreads) void decode_simple(
 // decode_stream
 // ---------------------------------------------------------------------------
 
-// Per-wave staging and (split mode) sign+mantissa buffers. A decoded step
-// stores, per lane, the high half of its slot-table entry (symbol << 8), so
-// the symbol is byte 1 of a 16-bit slot.
-template <int MODE>
+// Per-wave staging: a decoded step stores, per lane, the high half of its
+// slot-table entry (symbol << 8), so the symbol is byte 1 of a 16-bit slot.
 struct alignas(16) WaveStage {
     uint16_t stage[kBlockSyms];
-    uint8_t sm[MODE == kModeSplit ? 2 : 1][MODE == kModeSplit ? kBlockSyms : 16];
 };
+
+// Split mode: blocks of sign+mantissa bytes in flight per wave.
+constexpr uint32_t kSmAhead = 4;
+
+// Sign+mantissa bytes that lane k merges into its 4 outputs of a block.
+__device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t lane) {
+    return *reinterpret_cast<const uint32_t *>(sm_block + 4u * lane);
+}
 
 // PRIO: progress-based wave priority (below); off for launches with one
 // chunk per workgroup, where the waves do not compete and its per-block
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
     __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
-    __shared__ WaveStage<MODE> STG[kWaves];
+    __shared__ WaveStage STG[kWaves];
 
     const DevTask task = tasks[task0 + blockIdx.x];
     const bool e4m3 = tensors[task.tensor].kind == ENTQ_SYM_E4M3;
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
-    WaveStage<MODE> &G = STG[wave];
+    WaveStage &G = STG[wave];
     // the task's chunks in rounds of equal width: every round keeps the same
     // number of waves busy
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
@@ -189,10 +194,17 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
         Stream s;
         ring_open(s, region + kStateBytes, lds_addr(RING[wave]), ch.n_words, lane);
-        // first block's sign+mantissa bytes (a partial block reads them from
-        // global memory instead)
-        if (MODE == kModeSplit && n >= kBlockSyms && lane < kBlockSyms / 16)
-            dma16(signmant + ch.out_elem + 16u * lane, lds_addr(G.sm[0]));
+        const uint8_t *sm_g = signmant + ch.out_elem;
+        const uint32_t full_blocks = n / kBlockSyms;
+        // split mode: the sign+mantissa bytes of block b are loaded into
+        // register smr[b % kSmAhead] kSmAhead blocks ahead of their use (the
+        // block loop is unrolled kSmAhead times, so the registers are never
+        // copied: a copy would wait for the load in flight)
+        uint32_t smr[kSmAhead] = {};
+        if (MODE == kModeSplit)
+#pragma unroll
+            for (uint32_t j = 0; j < kSmAhead; ++j)
+                if (j < full_blocks) smr[j] = load_sm4(sm_g + j * kBlockSyms, lane);
         // vmcnt(0) as a real instruction, so that the compiler also knows the
         // state load has completed and places no wait of its own in the loop
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
@@ -203,10 +215,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         uint32_t col = ch.col0;  // a multiple of kBlockSyms on this path
         uint16_t *o16 = static_cast<uint16_t *>(out) + ch.out_elem;
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
-        const uint8_t *sm_g = signmant + ch.out_elem;
 
-        const uint32_t full_blocks = n / kBlockSyms;
-        for (uint32_t b = 0; b < full_blocks; ++b) {
+        auto block = [&](uint32_t b, uint32_t &sm_reg) __attribute__((always_inline)) {
             if (PRIO && ++done == prio_at) {
                 prio_at += quarter;
                 --prio;
@@ -237,18 +247,31 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 o16 += kBlockSyms;
                 col += kBlockSyms;
             } else {
-                wait_vm<0>();  // this block's sign+mantissa bytes
-                const uint32_t sm4 = *reinterpret_cast<const uint32_t *>(G.sm[b & 1] + 4u * lane);
                 // per 16-bit half: exponent << 8 | sign+mantissa
-                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
-                                           merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
-                // next block's sign+mantissa bytes, if that block is full
+                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm_reg, 0x07010500u)),
+                                           merge2(__builtin_amdgcn_perm(d.y, sm_reg, 0x07030502u)));
+                // block b + kSmAhead's bytes into the register just consumed
+                // (past the last full block: this block's again, unused). The
+                // load is unconditional and kept after the merge, so that the
+                // register is reused in place: a copy would wait for it.
+                __builtin_amdgcn_sched_barrier(0);
+                sm_reg = load_sm4(sm_g + (b + kSmAhead < full_blocks ? kSmAhead * kBlockSyms : 0u),
+                                  lane);
                 sm_g += kBlockSyms;
-                if (b + 1 < full_blocks && lane < kBlockSyms / 16)
-                    dma16(sm_g + 16u * lane, lds_addr(G.sm[(b + 1) & 1]));
                 reinterpret_cast<uint2 *>(o16)[lane] = w;
                 o16 += kBlockSyms;
             }
+        };
+        uint32_t b = 0;
+        if (MODE == kModeSplit) {
+            for (; b + kSmAhead <= full_blocks; b += kSmAhead)
+#pragma unroll
+                for (uint32_t j = 0; j < kSmAhead; ++j) block(b + j, smr[j]);
+#pragma unroll
+            for (uint32_t j = 0; j < kSmAhead; ++j)
+                if (b + j < full_blocks) block(b + j, smr[j]);
+        } else {
+            for (; b < full_blocks; ++b) block(b, smr[0]);
         }
         // the last, partial block: one symbol per lane and step, element-wise output
         const uint32_t rest = n - full_blocks * kBlockSyms;
