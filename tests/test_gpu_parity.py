@@ -346,6 +346,40 @@ def test_split_stream_ragged_and_high_entropy(E):
     np.testing.assert_array_equal(got, words)
 
 
+def test_split_block_counts_around_the_prefetch_depth(E):
+    """bf16 split on the streaming path, chunks of 0 to 9 full blocks
+    (256 symbols) with and without a partial block, and multi-chunk tensors
+    whose chunks hold 1 to 9 blocks: the sign+mantissa bytes run several
+    blocks ahead of the decode, so every count below and around that depth
+    and every remainder of the unrolled block loop is covered."""
+    _say("split block counts around the prefetch depth")
+    specs, parts = [], []
+    seed = 0
+    for k in range(10):
+        for r in (0, 48):
+            if k == 0 and r == 0:
+                continue
+            parts.append((256 * k + r, 65536))
+    for blocks in range(1, 10):
+        parts.append((7 * 256 * blocks + 160, 256 * blocks))
+    for n, C in parts:
+        seed += 1
+        w = synth.bf16_weights(1, n, sigma=float([0.02, 1.0, 300.0][seed % 3]))[0]["bf16"]
+        specs.append((w, C))
+    words = np.concatenate([w for w, _ in specs])
+    e_all, sm = oracle.bf16_split(words)
+    tens, at = [], 0
+    for w, C in specs:
+        tens.append(dict(kind=oracle.KIND_BF16EXP, rows=1, cols=w.size,
+                         symbols=e_all[at:at + w.size], chunk_symbols=C))
+        at += w.size
+    c = oracle.encode_container(tens)
+    assert [t["out_elem_offset"] for t in c.tensors] == list(np.cumsum([0] + [w.size for w, _ in specs])[:-1])
+    got, gst = gpu_decode(E, c, None, split_sm=sm)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, words)
+
+
 @pytest.mark.parametrize("cols", [320, 512])
 def test_nan_and_inf_scales_both_kernels(E, cols):
     """Non-finite scales and e4m3 NaN codes: cols=320 runs the simple
