@@ -158,9 +158,9 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     // block-aligned, then the rest (the launcher picks a kernel per group)
     auto group_of = [&](int t) {
         const entq_tensor_desc &td = tensors[t];
-        // the streaming kernel writes 4 outputs per lane and streams the
-        // sign+mantissa bytes 16 at a time: chunk sizes must be whole blocks
-        // and outputs 16-aligned
+        // the streaming kernel writes 4 outputs and reads 4 sign+mantissa
+        // bytes per lane and block (vector accesses): chunk sizes must be
+        // whole blocks and outputs 16-aligned
         if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return 2;
         return (td.cols % entq::kBlockSyms) ? 1 : 0;
     };
