@@ -59,6 +59,14 @@ struct GemmArgs {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Split mode: blocks of sign+mantissa bytes in flight per wave.
+constexpr uint32_t kSmAhead = 4;
+
+// Sign+mantissa bytes that lane k merges into its 4 columns of a block.
+__device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t lane) {
+    return *reinterpret_cast<const uint32_t *>(sm_block + 4u * lane);
+}
+
 // MT: groups of 16 activation rows. SPLIT: the weights are BF16 rebuilt from
 // a coded exponent stream and raw sign+mantissa bytes (no scales). PACKED:
 // x is the packed copy written by pack_activations (below), so each wave's
@@ -119,21 +127,30 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
     for (uint32_t r = 0; r < rows_per_chunk; ++r) {
         const bool live = r < my_rows;  // uniform per wave
         const float scale = (live && !SPLIT) ? scales[ch.scale_row + r] : 0.f;
-        // sign+mantissa bytes of this lane's four columns of each block
-        const uint8_t *sm_row = signmant + ch.out_elem + (uint64_t)r * cols + 4u * lane;
+        // sign+mantissa bytes of this lane's four columns of each block of
+        // the row: block kb's are loaded into register smr[kb % kSmAhead]
+        // kSmAhead blocks ahead of their use (the block loop is unrolled
+        // kSmAhead times so that the registers are never copied: a copy
+        // would wait for the load in flight)
+        // (a wave past its rows reads the buffer's first row instead, unused:
+        // every wave issues the same loads, so that the compiler's wait
+        // counts stay exact)
+        const uint8_t *sm_row = signmant + (live ? ch.out_elem + (uint64_t)r * cols : 0);
+        uint32_t smr[kSmAhead] = {};
+        if (SPLIT)
+#pragma unroll
+            for (uint32_t j = 0; j < kSmAhead; ++j)
+                if (j < blocks_per_row) smr[j] = load_sm4(sm_row + j * kBlockSyms, lane);
         float4_t acc[MT];
 #pragma unroll
         for (int g = 0; g < MT; ++g) acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
-        for (uint32_t kb = 0; kb < blocks_per_row; ++kb) {
+        auto block = [&](uint32_t kb, uint32_t &sm_reg) __attribute__((always_inline)) {
             const uint32_t buf = kb & 1;
             uint16_t *row_tile = TILE[buf][wave];
             if (live) {
                 if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
             }
-            // this block's activation slices and sign+mantissa bytes (in flight
-            // while the block decodes)
-            uint32_t sm4 = 0;
-            if (SPLIT && live) sm4 = *reinterpret_cast<const uint32_t *>(sm_row + kb * kBlockSyms);
+            // this block's activation slices (in flight while the block decodes)
             uint2 a[MT];
 #pragma unroll
             for (int g = 0; g < MT; ++g) {
@@ -141,7 +158,13 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                 if (PACKED)  // rows past m are zeros in the packed copy
                     a[g] = *reinterpret_cast<const uint2 *>(
                         gt.x + (((uint64_t)kb * kWaves + wave) * MT + g) * 256u + 4u * lane);
-                else if (16u * g + a_row < args.m)
+                else if (SPLIT) {  // unconditional (row 0 past m, then zeroed)
+                    const bool in_m = 16u * g + a_row < args.m;
+                    const uint2 v = *reinterpret_cast<const uint2 *>(
+                        (in_m ? xa + g * group_stride : xa - (uint64_t)a_row * gt.ldx) +
+                        (uint64_t)kb * kBlockSyms);
+                    a[g] = in_m ? v : make_uint2(0, 0);
+                } else if (16u * g + a_row < args.m)
                     a[g] = *reinterpret_cast<const uint2 *>(xa + g * group_stride +
                                                             (uint64_t)kb * kBlockSyms);
             }
@@ -153,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                 const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
                 uint2 w;
                 if (SPLIT)  // per 16-bit half: exponent << 8 | sign+mantissa
-                    w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
-                                   merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
+                    w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm_reg, 0x07010500u)),
+                                   merge2(__builtin_amdgcn_perm(d.y, sm_reg, 0x07030502u)));
                 else if (gt.e4m3)
                     w = make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale));
                 else
@@ -163,6 +186,16 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
             } else {
                 *reinterpret_cast<uint2 *>(row_tile + 4u * lane) = make_uint2(0, 0);
             }
+            if (SPLIT) {
+                // block kb + kSmAhead's bytes into the register just consumed
+                // (past the row's end: this block's again, unused), by every
+                // wave and after the merge, so that the register is reused in
+                // place
+                __builtin_amdgcn_sched_barrier(0);
+                sm_reg = load_sm4(sm_row + (kb + kSmAhead < blocks_per_row ? kb + kSmAhead : kb) *
+                                               kBlockSyms,
+                                  lane);
+            }
             __syncthreads();  // the tile of this block is complete
             const uint2 bw = *reinterpret_cast<const uint2 *>(&TILE[buf][0][0] + b_off);
 #pragma unroll
@@ -170,6 +203,17 @@ __global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restr
                 acc[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                     __builtin_bit_cast(short4_t, a[g]), __builtin_bit_cast(short4_t, bw), acc[g],
                     0, 0, 0);
+        };
+        uint32_t kb = 0;
+        if (SPLIT) {
+            for (; kb + kSmAhead <= blocks_per_row; kb += kSmAhead)
+#pragma unroll
+                for (uint32_t j = 0; j < kSmAhead; ++j) block(kb + j, smr[j]);
+#pragma unroll
+            for (uint32_t j = 0; j < kSmAhead; ++j)
+                if (kb + j < blocks_per_row) block(kb + j, smr[j]);
+        } else {
+            for (; kb < blocks_per_row; ++kb) block(kb, smr[0]);
         }
         // end of a weight row: add the 16 waves' partial sums, fixed order,
         // one group of activation rows at a time

@@ -250,12 +250,17 @@ def _run_split(E, p, blob, sm, x, rows):
     return y.cpu().numpy()
 
 
-def test_bf16_split_one_hot_returns_the_source_weights(E):
-    rows, cols = 72, 768                 # 3 blocks per row; 4-row chunks, the last one short
-    p, blob, sm, w = _bf16_setup(E, rows, cols, cols * 4)
+@pytest.mark.parametrize("rows,blocks,chunk_rows,ms", [
+    (72, 3, 4, (1, 16, 33)),   # 3 blocks per row; 18 chunks: a partial second workgroup
+    (40, 5, 3, (16,)),         # 5 and 7 blocks per row: the sign+mantissa prefetch's
+    (35, 7, 2, (7, 64)),       # unrolled loop plus a remainder; the last chunk short
+])
+def test_bf16_split_one_hot_returns_the_source_weights(E, rows, blocks, chunk_rows, ms):
+    cols = 256 * blocks
+    p, blob, sm, w = _bf16_setup(E, rows, cols, cols * chunk_rows)
     rng = np.random.default_rng(11)
-    for m in (1, 16, 33):
-        _say(f"bf16 split one-hot, m={m}")
+    for m in ms:
+        _say(f"bf16 split one-hot, {rows}x{cols}, {chunk_rows}-row chunks, m={m}")
         c = rng.choice(cols, m, replace=False)
         x = np.zeros((m, cols), np.float32)
         x[np.arange(m), c] = 1.0
