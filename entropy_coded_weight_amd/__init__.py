@@ -625,6 +625,39 @@ class DeviceBatch:
         return int((t["out_elem_offset"] + t["n_symbols"]).max()) if t.size else 0
 
 
+def _encode_meta(dev, k_all: int, n_freq: int):
+    """One zeroed device buffer holding the encoder's per-chunk word counts
+    (int32), region offsets (int64), the blob's end (int64) and n_freq
+    frequency tables (int16 x 256), so that the host reads them back in one
+    copy. Returns (buffer, nw, offs, end, freq, layout)."""
+    import torch
+    k = max(k_all, 1)
+
+    def up(v):  # every part starts 256-byte aligned, like an allocation of its own
+        return -(-v // 256) * 256
+    o_offs = up(4 * k)
+    o_end = up(o_offs + 8 * k)
+    o_freq = up(o_end + 8)
+    total = o_freq + 512 * max(n_freq, 1)
+    meta = torch.zeros(total, dtype=torch.uint8, device=dev)
+    nw = meta[:4 * k].view(torch.int32)
+    offs = meta[o_offs:o_offs + 8 * k].view(torch.int64)
+    end = meta[o_end:o_end + 8].view(torch.int64)
+    freq = meta[o_freq:].view(torch.int16).view(max(n_freq, 1), 256)
+    return meta, nw, offs, end, freq, (k, o_offs, o_end, o_freq)
+
+
+def _read_meta(meta, layout, k_all: int, n_freq: int):
+    """The host copy of an _encode_meta buffer: (nw u32, offs u64, end, freq u16)."""
+    k, o_offs, o_end, o_freq = layout
+    h = meta.cpu().numpy()
+    nw = h[:4 * k].view(np.uint32)[:k_all]
+    offs = h[o_offs:o_offs + 8 * k].view(np.uint64)[:k_all]
+    end = int(h[o_end:o_end + 8].view(np.int64)[0])
+    freq = h[o_freq:].view(np.uint16).reshape(max(n_freq, 1), 256)[:n_freq].copy()
+    return nw, offs, end, freq
+
+
 def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
     """The device path of encode_batch: specs' ``symbols`` are device uint8
     tensors (contiguous, 16-byte aligned). Counts, frequency tables,
@@ -651,9 +684,7 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
     blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(int(scr_off[-1]), 16), dtype=torch.uint8, device=dev)
     counts = torch.zeros((max(T, 1), 256), dtype=torch.int64, device=dev)
-    nw_d = torch.empty(max(k_all, 1), dtype=torch.int32, device=dev)
-    offs_d = torch.empty(max(k_all, 1), dtype=torch.int64, device=dev)
-    end_d = torch.zeros(1, dtype=torch.int64, device=dev)
+    meta, nw_d, offs_d, end_d, freq_d, layout = _encode_meta(dev, k_all, T)
 
     def timed(name, fn):
         if events is None:
@@ -669,7 +700,6 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         cjobs = [(sp["symbols"], counts[t]) for t, sp in enumerate(specs) if shapes[t][3]]
         if cjobs:
             timed("count", lambda: count_symbols_device_batch(cjobs, s))
-        freq_d = torch.zeros((max(T, 1), 256), dtype=torch.int16, device=dev)
         if T:
             timed("tables", lambda: build_freq_device(counts, freq_d, s))
         jobs, k0 = [], 0
@@ -694,10 +724,7 @@ def encode_batch_device(specs, stream=None, events=None) -> DeviceBatch:
         if pjobs:
             timed("pack", lambda: pack_device_batch(pjobs, blob, s))
         s.synchronize()
-        nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
-        offs = offs_d[:k_all].cpu().numpy().view(np.uint64)
-        end = int(end_d.cpu().numpy()[0])
-        freqs = freq_d[:T].cpu().numpy().view(np.uint16).copy()
+        nw, offs, end, freqs = _read_meta(meta, layout, k_all, T)
     for t in range(T):
         if shapes[t][3] == 0:
             freqs[t, 0] = PROB_SCALE  # an empty tensor: any valid table
@@ -747,9 +774,7 @@ def encode_batch_device_adaptive(specs, stream=None, events=None) -> DeviceBatch
     blob = torch.empty(max(bound, 16), dtype=torch.uint8, device=dev)
     scratch = torch.empty(max(int(scr_off[-1]), 16), dtype=torch.uint8, device=dev)
     counts = torch.zeros((max(k_all, 1), 256), dtype=torch.int32, device=dev)
-    nw_d = torch.empty(max(k_all, 1), dtype=torch.int32, device=dev)
-    offs_d = torch.empty(max(k_all, 1), dtype=torch.int64, device=dev)
-    end_d = torch.zeros(1, dtype=torch.int64, device=dev)
+    meta, nw_d, offs_d, end_d, _, layout = _encode_meta(dev, k_all, 0)
 
     def timed(name, fn):
         if events is None:
@@ -782,9 +807,7 @@ def encode_batch_device_adaptive(specs, stream=None, events=None) -> DeviceBatch
         if pjobs:
             timed("pack", lambda: pack_device_adaptive_batch(pjobs, blob, s))
         s.synchronize()
-        nw = nw_d[:k_all].cpu().numpy().view(np.uint32)
-        offs = offs_d[:k_all].cpu().numpy().view(np.uint64)
-        end = int(end_d.cpu().numpy()[0])
+        nw, offs, end, _ = _read_meta(meta, layout, k_all, 0)
     if (nw == 0xFFFFFFFF).any():
         raise EntqError(-2, "entq_encode_device_adaptive_batch: a chunk could not be coded")
     tens = np.zeros(T, TENSOR_DESC)
