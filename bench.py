@@ -1181,8 +1181,8 @@ def bench_workloads(args):
     bytes, and one 70B-shaped layer for comparison. Each timed launch follows
     a 512 MB read that evicts the last-level cache; median of the per-launch
     HIP events. Lossless outputs (codes, the BF16 matrix) are compared with
-    their sources; the bf16 outputs of the two small workloads with the
-    oracle (the CPU-baseline leg)."""
+    their sources; every bf16 output but the 70B layer's with the oracle
+    (the CPU-baseline leg)."""
     import torch
 
     import entropy_coded_weight_amd as E
@@ -1257,8 +1257,9 @@ def bench_workloads(args):
     n = w["rows"] * w["cols"]
     out = torch.empty(n, dtype=torch.int16, device=dev)
     med, p10, p90 = timed(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))
-    checks["bf16 8192x8192 equals the source weights"] = bool(
-        np.array_equal(out.cpu().numpy().view(np.uint16), w["bf16"]))
+    split_bits = out.cpu().numpy().view(np.uint16)
+    checks["bf16 8192x8192 equals the source weights"] = bool(np.array_equal(split_bits, w["bf16"]))
+    kept["bf16 split"] = (b, sm, split_bits, n)
     rows_out.append({"workload": "bf16 8192x8192 exponent stream + sign/mantissa", "output": "bf16",
                      "params": n, "chunks": int(p.n_chunks),
                      "bits_per_param": 8.0 * (b.blob.size + n) / n,
@@ -1276,19 +1277,32 @@ def bench_workloads(args):
         import oracle
         t = time.perf_counter()
         n_s = 0
-        for name in ("laplace int8 256x256", "e4m3 4096x4096"):
+        for name in ("laplace int8 256x256", "e4m3 4096x4096", "llama2-13b block"):
             specs, bb, gpu = kept[name]
-            sp = specs[0]
-            desc = np.stack([bb.chunks["n_symbols"], bb.chunks["n_words"], bb.chunks["byte_offset"],
-                             bb.chunks["elem_offset"]], axis=1).astype(np.uint64)
-            sym, st = oracle.decode_tensor(bb.blob, desc, bb.freq[0], sp["rows"] * sp["cols"])
-            bits = oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"])
-            checks[f"{name} bf16 equals the oracle"] = bool((st == 0).all() and np.array_equal(bits, gpu))
-            n_s += sp["rows"] * sp["cols"]
+            ok, at = True, 0
+            for ti, sp in enumerate(specs):
+                ch = bb.chunks[bb.chunks["tensor"] == ti]
+                desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"],
+                                 ch["elem_offset"]], axis=1).astype(np.uint64)
+                nt = sp["rows"] * sp["cols"]
+                sym, st = oracle.decode_tensor(bb.blob, desc, bb.freq[ti], nt)
+                bits = oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"])
+                ok = ok and bool((st == 0).all() and np.array_equal(bits, gpu[at:at + nt]))
+                at += nt
+            checks[f"{name} bf16 equals the oracle"] = ok
+            n_s += at
+        bb, sm_h, gpu, nw_ = kept["bf16 split"]
+        desc = np.stack([bb.chunks["n_symbols"], bb.chunks["n_words"], bb.chunks["byte_offset"],
+                         bb.chunks["elem_offset"]], axis=1).astype(np.uint64)
+        sym, st = oracle.decode_tensor(bb.blob, desc, bb.freq[0], nw_)
+        checks["bf16 8192x8192 equals the oracle"] = bool(
+            (st == 0).all() and np.array_equal(oracle.bf16_merge(sym, sm_h), gpu))
+        n_s += nw_
         dt = time.perf_counter() - t
         cpu = {"value": n_s / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-               "sample": "the whole 256x256 Laplace and e4m3 4096x4096 workloads: single-threaded "
-                         "C oracle decode + dequant + RNE bf16"}
+               "sample": "the whole 256x256 Laplace, e4m3 4096x4096, LLaMA-2-13B block and BF16 "
+                         "8192x8192 workloads: single-threaded C oracle decode + dequant + RNE "
+                         "bf16 (+ sign/mantissa merge)"}
         log(f"cpu oracle: {n_s} params in {dt:.2f}s")
     for k, ok in checks.items():
         log(f"check: {k}: {ok}")
