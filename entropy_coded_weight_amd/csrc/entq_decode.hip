@@ -175,17 +175,18 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     // number of waves busy
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
     const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
-    // Wave priority by progress: a wave drops one level each time it has
-    // done a quarter of its blocks, so waves that are behind win issue
-    // arbitration. (The default favours the oldest waves: the younger
-    // workgroup on a CU, and the younger waves of a workgroup, then finish
-    // long after the rest, with the CU half idle.)
+    // Wave priority by progress: a wave drops one level once it has done
+    // half of its blocks, again at three quarters and at seven eighths (half
+    // of what is left each time), so waves that are behind win issue
+    // arbitration near the end. (The default favours the oldest waves: the
+    // younger workgroup on a CU, and the younger waves of a workgroup, then
+    // finish long after the rest, with the CU half idle. Drops every quarter
+    // of the blocks, or from the first eighth on, left a longer tail.)
     uint32_t my_blocks = 0;
     if (PRIO)
         for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
             my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
-    const uint32_t quarter = my_blocks / 4 ? my_blocks / 4 : 1;
-    uint32_t done = 0, prio_at = quarter, prio = 3;
+    uint32_t done = 0, prio_at = my_blocks / 2 ? my_blocks / 2 : 1, prio = 3;
     if (PRIO) __builtin_amdgcn_s_setprio(3);
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
 
         auto block = [&](uint32_t b, uint32_t &sm_reg) __attribute__((always_inline)) {
             if (PRIO && ++done == prio_at) {
-                prio_at += quarter;
+                prio_at += (my_blocks - prio_at) / 2 ? (my_blocks - prio_at) / 2 : 1;
                 --prio;
                 if (prio == 2) __builtin_amdgcn_s_setprio(2);
                 else if (prio == 1) __builtin_amdgcn_s_setprio(1);
