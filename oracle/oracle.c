@@ -95,14 +95,18 @@ uint16_t orc_bf16_from_f32_bits(uint32_t u)
  * 3 mantissa bits, no infinities, NaN only at S.1111.111.
  *   E = 0        : subnormal, value = m * 2^-9
  *   otherwise    : value = (1 + m/8) * 2^(E-7)
- * A NaN code carries no payload; it decodes to the default NaN. */
+ * A NaN code is widened as IEEE 754-2008 §6.2.3 widens a NaN into a wider
+ * format: it stays a NaN with its sign, and its trailing significand (the
+ * 3 mantissa bits, all ones, the first of them the quiet bit) becomes the
+ * leading bits of the fp32 trailing significand:
+ *   S.1111.111 -> S << 31 | 0x7F800000 | 7 << 20  (0x7FF00000 / 0xFFF00000). */
 uint32_t orc_e4m3_to_f32_bits(uint8_t c)
 {
     uint32_t sign = c >> 7;
     uint32_t E = (c >> 3) & 15u;
     uint32_t m = c & 7u;
     if (E == 15u && m == 7u)
-        return ORC_DEFAULT_NAN;
+        return (sign << 31) | 0x7F800000u | (m << 20);
     double v;
     if (E == 0u)
         v = ldexp((double)m, -9);

@@ -67,15 +67,17 @@ def test_bf16_nan_follows_ieee_narrowing():
 
 
 def test_e4m3_decode_all_256_codes_match_torch():
+    # every pattern, the two NaN codes included: torch's CPU cast widens a
+    # NaN code keeping its sign and putting its mantissa bits at the top of
+    # the fp32 payload, as IEEE 754-2008 6.2.3 widens a NaN
     mine = oracle.e4m3_table().view(np.float32)
     ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
     nan_ref = np.isnan(ref)
     assert np.array_equal(np.isnan(mine), nan_ref)
     assert nan_ref.sum() == 2 and nan_ref[0x7F] and nan_ref[0xFF]
-    np.testing.assert_array_equal(mine[~nan_ref].view(np.uint32), ref[~nan_ref].view(np.uint32))
-    # NaN codes carry no payload: both decode to the default NaN
+    np.testing.assert_array_equal(mine.view(np.uint32), ref.view(np.uint32))
     bits = oracle.e4m3_table()
-    assert bits[0x7F] == 0xFFC00000 and bits[0xFF] == 0xFFC00000
+    assert bits[0x7F] >> 31 == 0 and bits[0xFF] >> 31 == 1  # sign kept
     # a few values by the format definition: 448 max, 2^-9 min subnormal, -0
     assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and bits[0x80] == 0x80000000
 
@@ -106,9 +108,20 @@ def test_dequant_matches_torch_fp32_product_then_bf16(kind):
     np.testing.assert_array_equal(got, want)
 
 
-def test_dequant_of_nan_code_is_the_default_nan():
-    assert oracle.dequant_bf16(0x7F, oracle.KIND_E4M3, 0.5) == 0xFFC0
-    assert oracle.dequant_bf16(0xFF, oracle.KIND_E4M3, -0.5) == 0xFFC0
+def test_dequant_of_nan_code_composes_the_pinned_steps():
+    # value: torch's widening of the NaN code; product: the host's IEEE
+    # multiply (a NaN operand comes out as itself, quieted); bf16: the IEEE
+    # narrowing (sign and top payload kept, quiet bit set)
+    codes = torch.tensor([0x7F, 0xFF], dtype=torch.uint8).view(torch.float8_e4m3fn)
+    v = codes.float().numpy().view(np.uint32)
+    for scale in (0.5, -0.5, 3.0e38, 0.0, 1e-40, float("inf"), float("-inf")):
+        sb = int(np.array([scale], np.float32).view(np.uint32)[0])
+        for c, vb in zip((0x7F, 0xFF), v):
+            p = int(_np_mul_bits([int(vb)], [sb])[0])
+            want = (p >> 16) | 0x0040
+            assert oracle.dequant_bf16(c, oracle.KIND_E4M3, scale) == want, (hex(c), scale)
+    assert oracle.dequant_bf16(0x7F, oracle.KIND_E4M3, 0.5) >> 15 == 0
+    assert oracle.dequant_bf16(0xFF, oracle.KIND_E4M3, 0.5) >> 15 == 1
 
 
 def _np_mul_bits(a_bits, b_bits):
