@@ -227,6 +227,10 @@ class Plan:
         self.out_elems, self.scale_rows = int(oe.value), int(sr.value)
 
     @property
+    def device(self):
+        return self.workspace.device
+
+    @property
     def handle(self):
         return self._h
 
@@ -246,26 +250,89 @@ def plan(tensors, freq_tables, chunk_index, blob_bytes, device="cuda", stream=No
     return Plan(tensors, freq_tables, chunk_index, blob_bytes, device, stream)
 
 
+EINVAL = -1
+
+
+def _device_buffer(p: Plan, name: str, t, min_elems: int, elem_size: int | None = None,
+                   dtypes=None):
+    """Checks one device buffer argument against the plan before a launch:
+    the kernels dereference raw pointers, so a buffer that is too small, of
+    the wrong element size or on another device must be refused here."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise EntqError(EINVAL, f"{name}: a torch tensor on {p.device} is required")
+    if t.device != p.device:
+        raise EntqError(EINVAL, f"{name} is on {t.device}, the plan on {p.device}")
+    if not t.is_contiguous():
+        raise EntqError(EINVAL, f"{name} is not contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise EntqError(EINVAL, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise EntqError(EINVAL, f"{name} has {t.element_size()}-byte elements, expected "
+                                f"{elem_size}")
+    if t.numel() < min_elems:
+        raise EntqError(EINVAL, f"{name} holds {t.numel()} elements, the plan needs {min_elems}")
+
+
+def _status_buffer(p: Plan, chunk_status):
+    import torch
+    if chunk_status is not None:
+        _device_buffer(p, "chunk_status", chunk_status, p.n_chunks, dtypes=(torch.int32,))
+
+
+def _blob_buffer(p: Plan, name: str, t):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise EntqError(EINVAL, f"{name}: a torch tensor on {p.device} is required")
+    _device_buffer(p, name, t, -(-p.blob_bytes // t.element_size()))
+
+
 def decode(p: Plan, compressed, out, out_kind: int, scales=None, chunk_status=None,
            stream=None):
     """Enqueue the decode of every chunk of ``p`` on ``stream``. All buffers
-    are device tensors: compressed (uint8, the blob), out (uint8 for
-    OUT_CODES, bf16/int16/uint16 for OUT_BF16), scales (float32),
-    chunk_status (int32 [n_chunks]) or None."""
+    are device tensors on the plan's device: compressed (the blob, at least
+    blob_bytes), out (1-byte elements for OUT_CODES, 2-byte bf16/int16/uint16
+    for OUT_BF16, at least out_elems), scales (float32, at least scale_rows;
+    OUT_BF16 only), chunk_status (int32 [n_chunks]) or None."""
+    import torch
+    if out_kind not in (OUT_CODES, OUT_BF16):
+        raise EntqError(EINVAL, f"out_kind {out_kind}")
+    _blob_buffer(p, "compressed", compressed)
+    _device_buffer(p, "out", out, p.out_elems, elem_size=1 if out_kind == OUT_CODES else 2)
+    if out_kind == OUT_BF16:
+        if scales is None:
+            raise EntqError(EINVAL, "scales are required for OUT_BF16")
+        _device_buffer(p, "scales", scales, p.scale_rows, dtypes=(torch.float32,))
+    else:
+        scales = None
+    _status_buffer(p, chunk_status)
     st = lib().entq_decode(p.handle, _ptr(compressed), _ptr(out), int(out_kind),
                            _ptr(scales) or None, _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode")
 
 
 def _gemm_io(p: Plan, xs, ys):
+    """io[] of the fused calls; every activation and result matrix is checked
+    against its tensor's shape (x: bf16 [m, >= cols], y: float32 [m, >=
+    rows], rows unit-stride, on the plan's device)."""
     import torch
-    assert len(xs) == len(ys) == p.n_tensors
+    if not (len(xs) == len(ys) == p.n_tensors):
+        raise EntqError(EINVAL, f"{len(xs)} activation and {len(ys)} result matrices for "
+                                f"{p.n_tensors} tensors")
     m = xs[0].shape[0] if xs else 0
     io = np.zeros(len(xs), GEMM_IO)
     for t, (x, y) in enumerate(zip(xs, ys)):
-        assert x.dtype == torch.bfloat16 and y.dtype == torch.float32
-        assert x.dim() == 2 and y.dim() == 2 and x.shape[0] == m and y.shape[0] == m
-        assert x.stride(1) == 1 and y.stride(1) == 1
+        rows, cols = int(p.tensors[t]["rows"]), int(p.tensors[t]["cols"])
+        for name, a, dt, width in (("x", x, torch.bfloat16, cols), ("y", y, torch.float32, rows)):
+            if not isinstance(a, torch.Tensor) or a.device != p.device:
+                raise EntqError(EINVAL, f"{name}[{t}] must be a tensor on {p.device}")
+            if a.dtype != dt or a.dim() != 2 or a.shape[0] != m or a.stride(1) != 1:
+                raise EntqError(EINVAL, f"{name}[{t}]: {a.dtype} {tuple(a.shape)} stride "
+                                        f"{tuple(a.stride())}; expected {dt} [{m}, >= {width}] "
+                                        "with unit-stride rows")
+            if a.shape[1] < width:
+                raise EntqError(EINVAL, f"{name}[{t}] has {a.shape[1]} columns, tensor {t} "
+                                        f"needs {width}")
         io[t] = (_ptr(x), x.stride(0), _ptr(y), y.stride(0))
     return io, m
 
@@ -284,6 +351,8 @@ def _gemm_workspace(p: Plan, m: int, workspace):
         shift = (-raw.data_ptr()) % 256
         workspace = raw[shift:shift + n]
         return workspace, n
+    need = int(lib().entq_decode_gemm_workspace_bytes(p.handle, int(m))) if p.handle.value else 0
+    _device_buffer(p, "workspace", workspace, need, elem_size=1)
     return workspace, workspace.numel()
 
 
@@ -295,7 +364,11 @@ def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=N
     device float32 tensor [m, ldy >= rows]. workspace: a device uint8 tensor
     (256-byte aligned, entq_decode_gemm_workspace_bytes long) for the packed
     activations, None to allocate one when m > 16, or "none"."""
+    import torch
     io, m = _gemm_io(p, xs, ys)
+    _blob_buffer(p, "compressed", compressed)
+    _device_buffer(p, "scales", scales, p.scale_rows, dtypes=(torch.float32,))
+    _status_buffer(p, chunk_status)
     ws, wsb = _gemm_workspace(p, m, workspace)
     if ws is not None and workspace is None and stream is not None:
         ws.record_stream(stream)  # allocated here, used on another stream
@@ -311,6 +384,9 @@ def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=N
     """decode_gemm for BF16 weights given as a coded exponent stream plus raw
     sign+mantissa bytes (as decode_bf16_split takes them)."""
     io, m = _gemm_io(p, xs, ys)
+    _blob_buffer(p, "exp_stream", exp_stream)
+    _device_buffer(p, "signmant", signmant, p.out_elems, elem_size=1)
+    _status_buffer(p, chunk_status)
     ws, wsb = _gemm_workspace(p, m, workspace)
     if ws is not None and workspace is None and stream is not None:
         ws.record_stream(stream)
@@ -322,6 +398,13 @@ def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=N
 
 
 def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):
+    """Exponent stream (the blob) + raw sign/mantissa bytes (1-byte elements,
+    at least out_elems) -> bf16 words in out (2-byte elements, at least
+    out_elems); all on the plan's device."""
+    _blob_buffer(p, "exp_stream", exp_stream)
+    _device_buffer(p, "signmant", signmant, p.out_elems, elem_size=1)
+    _device_buffer(p, "out", out, p.out_elems, elem_size=2)
+    _status_buffer(p, chunk_status)
     st = lib().entq_decode_bf16_split(p.handle, _ptr(exp_stream), _ptr(signmant), _ptr(out),
                                       _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_bf16_split")
