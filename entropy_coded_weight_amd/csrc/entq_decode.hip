@@ -90,7 +90,7 @@ __device__ __forceinline__ void simple_chunk(const uint2 *T, const DevTensor &td
                 static_cast<uint8_t *>(out)[o] = (uint8_t)sym;
             } else if (MODE == kModeBf16) {
                 const float v = (td.kind == ENTQ_SYM_E4M3)
-                                    ? __builtin_amdgcn_cvt_f32_fp8((int)sym, 0)
+                                    ? e4m3_value(sym)
                                     : (float)(int8_t)sym;
                 static_cast<uint16_t *>(out)[o] = bf16_bits(mul_value_scale(v, scales[row]));
             } else {
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
                 if (MODE == kModeCodes) {
                     o8[i] = (uint8_t)sym;
                 } else if (MODE == kModeBf16) {
-                    const float v = e4m3 ? __builtin_amdgcn_cvt_f32_fp8((int)sym, 0)
+                    const float v = e4m3 ? e4m3_value(sym)
                                          : (float)(int8_t)sym;
                     o16[i] = bf16_bits(mul_value_scale(v, scale));
                 } else {

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
                     const uint32_t sm = sm_g[i];
                     o16[i] = (uint16_t)(((sm & 0x80u) << 8) | (sym << 7) | (sm & 0x7Fu));
                 } else {
-                    const float v = e4m3 ? __builtin_amdgcn_cvt_f32_fp8((int)sym, 0)
+                    const float v = e4m3 ? e4m3_value(sym)
                                          : (float)(int8_t)sym;
                     o16[i] = bf16_bits(mul_value_scale(v, scale));
                 }

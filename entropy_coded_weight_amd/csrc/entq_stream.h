@@ -204,6 +204,27 @@ __device__ __forceinline__ void stream_step(uint32_t &x, uint32_t &pos, const ui
     pos += (uint32_t)__popcll(mask);
 }
 
+// The value of an e4m3 NaN code (S.1111.111) is the NaN that keeps the
+// code's sign and puts its mantissa bits at the top of the fp32 payload:
+// S << 31 | 0x7FF00000 (a NaN widened into a wider format, IEEE 754-2008
+// §6.2.3). The conversion instruction returns one fixed NaN for both codes,
+// so the NaN codes are patched. Element-wise form, code in bits 0..7:
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+    const float v = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+    return ((code & 0x7Fu) == 0x7Fu) ? __uint_as_float(((code & 0x80u) << 24) | 0x7FF00000u) : v;
+}
+
+// Two bf16 results r of the codes in bytes 1 and 3 of d: the half whose
+// code is a NaN code becomes that NaN's bf16, S << 15 | 0x7FF0, whatever
+// the scale (the code's NaN wins over a NaN scale, and a NaN stays a NaN
+// through the product and the rounding).
+__device__ __forceinline__ uint32_t e4m3_nan_patch2(uint32_t d, uint32_t r) {
+    // bit 15 / 31 set iff the code's low 7 bits are all ones
+    const uint32_t hit = ((d & 0x7F007F00u) + 0x01000100u) & 0x80008000u;
+    const uint32_t sel = (hit >> 15) * 0xFFFFu;
+    return (r & ~sel) | (((d & 0x80008000u) | 0x7FF07FF0u) & sel);
+}
+
 // bf16 of (value of a code byte) * scale, two per dword; d holds two staged
 // 16-bit slots, the code bytes in bytes 1 and 3.
 template <bool E4M3>
@@ -216,7 +237,8 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t d, float scale) {
         v0 = (float)((int32_t)(d << 16) >> 24);
         v1 = (float)((int32_t)d >> 24);
     }
-    return bf16x2_bits(mul_value_uscale(v0, scale), mul_value_uscale(v1, scale));
+    const uint32_t r = bf16x2_bits(mul_value_uscale(v0, scale), mul_value_uscale(v1, scale));
+    return E4M3 ? e4m3_nan_patch2(d, r) : r;
 }
 
 // sign << 15 | exponent << 7 | mantissa for two elements: q holds, per

@@ -36,8 +36,10 @@
  *   ENTQ_OUT_CODES  uint8  out[i] = the decoded code byte;
  *   ENTQ_OUT_BF16   uint16 out[i] = RNE_bf16( fl32( value(code) * scale[row] ) )
  *                   where value is the two's-complement integer (INT8) or
- *                   the OCP e4m3 ("E4M3FN") value (E4M3; both NaN codes have
- *                   the default NaN 0xFFC00000 as value), the product is one
+ *                   the OCP e4m3 ("E4M3FN") value (E4M3; a NaN code
+ *                   S.1111.111 has the NaN S << 31 | 0x7FF00000 as value:
+ *                   sign kept, mantissa bits at the top of the payload, as
+ *                   IEEE 754-2008 §6.2.3 widens a NaN), the product is one
  *                   IEEE single multiply rounded to nearest even (a NaN
  *                   operand comes out quieted with its payload, the code's
  *                   before the scale's; 0 * inf gives 0xFFC00000), and
