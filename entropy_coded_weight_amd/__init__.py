@@ -116,6 +116,7 @@ def lib():
             "entq_region_offsets_device_adaptive": (c.c_int, [vp, u64, u64, vp, vp, vp]),
             "entq_pack_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp, vp]),
             "entq_build_freq_device": (c.c_int, [vp, c.c_uint32, u64, vp, vp]),
+            "entq_decode_gemm_static": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -136,7 +137,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_decode_gemm_bf16_split", "entq_count_chunks_device_batch",
             "entq_build_freq_chunks", "entq_encode_device_adaptive_batch",
             "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
-            "entq_build_freq_device", "entq_decode_gemm_workspace_bytes"]
+            "entq_build_freq_device", "entq_decode_gemm_workspace_bytes",
+            "entq_decode_gemm_static"]
 
 
 def _str(status: int) -> str:
@@ -250,7 +252,9 @@ def plan(tensors, freq_tables, chunk_index, blob_bytes, device="cuda", stream=No
     return Plan(tensors, freq_tables, chunk_index, blob_bytes, device, stream)
 
 
-EINVAL = -1
+EINVAL, EWORKSPACE, ETOOLARGE = -1, -5, -9
+# bytes of the static device scratch behind decode_gemm_static (include/entq.h)
+GEMM_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 def _device_buffer(p: Plan, name: str, t, min_elems: int, elem_size: int | None = None,
@@ -377,6 +381,23 @@ def decode_gemm(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=N
                                 _ptr(ws) if ws is not None else None, int(wsb),
                                 _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm")
+
+
+def decode_gemm_static(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None):
+    """decode_gemm with the packed activations in the library's static
+    device scratch (entq_decode_gemm_static): no workspace, no allocation,
+    results bit for bit those of decode_gemm. Raises EntqError(ETOOLARGE)
+    when the packed activations would exceed GEMM_STATIC_SCRATCH_BYTES.
+    Calls on one GPU share the scratch: overlapping calls race."""
+    import torch
+    io, m = _gemm_io(p, xs, ys)
+    _blob_buffer(p, "compressed", compressed)
+    _device_buffer(p, "scales", scales, p.scale_rows, dtypes=(torch.float32,))
+    _status_buffer(p, chunk_status)
+    st = lib().entq_decode_gemm_static(p.handle, _ptr(compressed), _ptr(scales) or None,
+                                       _ptr(io) if len(xs) else None, int(m),
+                                       _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_gemm_static")
 
 
 def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=None,

@@ -25,6 +25,8 @@
 // (fixed order) and written out.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "entq.h"
 #include "entq_internal.h"
 #include "entq_stream.h"
@@ -388,6 +390,45 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
 
 }  // namespace entq
 
+// ---------------------------------------------------------------------------
+// entq_decode_gemm_static: the packed activations in a file-scope device array
+// ---------------------------------------------------------------------------
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops). Each GPU holds its own copy of the array
+// from the library's first use on it until the process ends. Host code never
+// uses the array's name as an address: the device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and kept.
+
+static __device__ __align__(256) uint8_t scratch[ENTQ_GEMM_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that runs `stream`.
+entq_status static_scratch(void *stream, uint8_t **out) {
+    int dev = 0, cur = 0;
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return ENTQ_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return ENTQ_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        if (hipGetDevice(&cur) != hipSuccess) return ENTQ_EHIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return ENTQ_EHIP;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return ENTQ_EHIP;
+        if (e != hipSuccess || !ptr || (uintptr_t)ptr % 256) return ENTQ_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return ENTQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 namespace {
@@ -440,6 +481,23 @@ entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
     if (st != ENTQ_OK) return st;
     return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, nullptr, io, m,
                                                  static_cast<uint8_t *>(d_workspace),
+                                                 d_chunk_status, stream);
+}
+
+entq_status entq_decode_gemm_static(const entq_plan_t *plan, const void *d_compressed,
+                                    const float *d_scales, const entq_gemm_io *io, int m,
+                                    int32_t *d_chunk_status, void *stream) {
+    entq_status st = check_gemm_args(plan, io, m, false);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    if (entq::gemm_workspace_bytes(plan, m) > ENTQ_GEMM_STATIC_SCRATCH_BYTES) return ENTQ_ETOOLARGE;
+    uint8_t *ptr = nullptr;
+    st = static_scratch(stream, &ptr);
+    if (st != ENTQ_OK) return st;
+    // the pack kernel writes every byte the product reads (zeros for rows
+    // past m), so the previous call's contents need no clearing
+    return (entq_status)entq::launch_decode_gemm(plan, d_compressed, d_scales, nullptr, io, m, ptr,
                                                  d_chunk_status, stream);
 }
 

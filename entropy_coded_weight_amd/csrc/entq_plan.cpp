@@ -66,6 +66,7 @@ const char *entq_status_str(entq_status s) {
     case ENTQ_EHIP: return "HIP call failed";
     case ENTQ_ENOMEM: return "out of host memory";
     case ENTQ_ESYMBOL: return "a coded symbol has frequency 0";
+    case ENTQ_ETOOLARGE: return "request exceeds the library's static scratch";
     }
     return "unknown status";
 }

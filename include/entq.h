@@ -84,7 +84,8 @@ typedef enum {
     ENTQ_EWORKSPACE = -5,   /* workspace too small                          */
     ENTQ_EHIP = -6,         /* a HIP call or kernel launch failed           */
     ENTQ_ENOMEM = -7,       /* host allocation failed                       */
-    ENTQ_ESYMBOL = -8       /* encoder: a symbol has frequency 0            */
+    ENTQ_ESYMBOL = -8,      /* encoder: a symbol has frequency 0            */
+    ENTQ_ETOOLARGE = -9     /* beyond the library's static scratch          */
 } entq_status;
 
 typedef enum { ENTQ_SYM_INT8 = 0, ENTQ_SYM_E4M3 = 1, ENTQ_SYM_BF16EXP = 2 } entq_symkind;
@@ -289,6 +290,26 @@ entq_status entq_decode_gemm(const entq_plan_t *plan, const void *d_compressed,
                              const float *d_scales, const entq_gemm_io *io, int m,
                              void *d_workspace, uint64_t workspace_bytes,
                              int32_t *d_chunk_status, void *stream);
+
+/* entq_decode_gemm with the packed activations in the library's own static
+ * device scratch instead of a caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). It allocates nothing: the
+ * scratch is a file-scope device array of ENTQ_GEMM_STATIC_SCRATCH_BYTES
+ * that each GPU holds from the library's first use on it until the process
+ * ends. Arguments and results as entq_decode_gemm (Int8 / E4M3 plans); the
+ * results are bit for bit those of entq_decode_gemm. Returns ENTQ_ETOOLARGE
+ * when entq_decode_gemm_workspace_bytes(plan, m) exceeds the scratch (16
+ * MiB: every 70B-shaped layer at m <= 64), ENTQ_EHIP if the scratch's
+ * address cannot be looked up on the stream's device. Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race and must be ordered by
+ * the caller. */
+#define ENTQ_GEMM_STATIC_SCRATCH_BYTES (16u << 20)
+
+entq_status entq_decode_gemm_static(const entq_plan_t *plan, const void *d_compressed,
+                                    const float *d_scales, const entq_gemm_io *io, int m,
+                                    int32_t *d_chunk_status, void *stream);
 
 /* The same product for BF16 weights stored as a coded exponent stream plus
  * raw sign+mantissa bytes [DFloat11 write-up, "Formato DFloat11"]: W_t is
