@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=80,
                     help="layers in the model (80 is the workload; fewer only for quick checks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the untimed pass that compares every layer's GPU output with the "
+                         "oracle (all host threads)")
     ap.add_argument("--cpu-sample-tensors", type=int, default=7,
                     help="tensors of layer 0 the oracle decodes for the CPU baseline "
                          "(7: the whole layer, about 7 s on one core)")
@@ -111,6 +114,7 @@ def main():
     # ---------------------------------------------------------------- setup
     t0 = time.time()
     plans, blobs, scales = [], [], []
+    host_layers = []  # per layer: the compressed batch and the scales, for the parity pass
     params_per_layer = 0
     layer_blob_bytes = []
     cpu_sample = None
@@ -125,6 +129,8 @@ def main():
         scales.append(sc)
         layer_blob_bytes.append(int(b.blob.size))
         params_per_layer = b.out_elems
+        if not args.no_parity:
+            host_layers.append((b, [(s["kind"], s["rows"], s["cols"], s["scales"]) for s in specs]))
         if layer == 0 and not args.no_cpu_baseline:
             cpu_sample = (specs[:args.cpu_sample_tensors], b)
         if layer % 10 == 0 or layer == args.layers - 1:
@@ -195,6 +201,19 @@ def main():
     if cpu_sample is not None:
         cpu = cpu_baseline(cpu_sample, plans[0], blobs[0], scales[0], out, stream)
 
+    # ------------------------------------------- parity of every layer (untimed)
+    parity = None
+    if not args.no_parity:
+        parity = parity_pass(plans, blobs, scales, host_layers, out, stream)
+        if cpu is not None:
+            cpu["all_threads"] = {
+                "value": parity["oracle_params_per_s"], "unit": "params/s",
+                "threads": parity["oracle_threads"],
+                "sample": f"all {args.layers} layers ({parity['elements_compared']} params): the "
+                          "same single-threaded oracle functions over disjoint row-aligned chunk "
+                          "ranges, one range per thread at a time; time of the parity pass's "
+                          "oracle phases"}
+
     rec = {
         "metric": METRIC,
         "value": value,
@@ -231,8 +250,92 @@ def main():
             "traffic": measured_traffic(),
         },
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(rec), flush=True)
+    if parity is not None and parity["layers_bit_exact"] != parity["layers"]:
+        raise SystemExit("GPU output differs from the oracle on "
+                         f"{parity['layers'] - parity['layers_bit_exact']} layers")
+
+
+def host_cpu():
+    """(os.cpu_count(), CPU model string from /proc/cpuinfo)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def parity_pass(plans, blobs, scales, host_layers, out, stream):
+    """Decodes every layer again, in the timed launch configuration plus a
+    per-chunk status buffer, copies the bf16 output to the host and has the
+    oracle (decode + dequant of the same compressed bytes, fanned out over
+    the host's threads) compare every element. Returns the record."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    import entropy_coded_weight_amd as E
+    from oracle import fanout
+
+    threads = fanout.default_threads()
+    pinned = torch.empty(out.numel(), dtype=torch.int16, pin_memory=True)
+    host_out = pinned.numpy().view(np.uint16)
+    n_layers = len(host_layers)
+    exact = mismatches = bad = status_bad = elems = 0
+    first_bad = None
+    oracle_s = 0.0
+    t_all = time.perf_counter()
+    with ThreadPoolExecutor(threads) as pool, ThreadPoolExecutor(8) as drivers:
+        for layer, (b, tens) in enumerate(host_layers):
+            status = torch.full((b.chunks.size,), -7, dtype=torch.int32, device=out.device)
+            E.decode(plans[layer], blobs[layer], out, E.OUT_BF16, scales[layer], status, stream)
+            pinned.copy_(out, non_blocking=True)
+            st = status.cpu().numpy()  # waits for the decode and the copy
+            t0 = time.perf_counter()
+            jobs = []
+            for t, (kind, rows, cols, sc) in enumerate(tens):
+                ch = b.chunks[b.chunks["tensor"] == t]
+                ch = ch[np.argsort(ch["elem_offset"])]
+                desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"],
+                                 ch["elem_offset"]], axis=1).astype(np.uint64)
+                o = int(b.tensors[t]["out_elem_offset"])
+                jobs.append(drivers.submit(fanout.tensor_bf16, b.blob, desc, b.freq[t], kind,
+                                           rows, cols, sc, threads,
+                                           host_out[o:o + rows * cols], None, False, pool))
+            res = [j.result() for j in jobs]
+            oracle_s += time.perf_counter() - t0
+            lm = sum(r.mismatches for _, r in res)
+            lb = sum(r.bad_chunks for _, r in res)
+            ls = int(np.count_nonzero(st != 0))
+            mismatches += lm
+            bad += lb
+            status_bad += ls
+            elems += int(b.out_elems)
+            if lm == 0 and lb == 0 and ls == 0:
+                exact += 1
+            elif first_bad is None:
+                first_bad = layer
+            if layer % 10 == 0 or layer == n_layers - 1:
+                log(f"parity: layer {layer} {'bit-exact' if lm == lb == ls == 0 else 'DIFFERS'} "
+                    f"({exact}/{layer + 1} so far, {time.perf_counter() - t_all:.1f}s)")
+    wall = time.perf_counter() - t_all
+    cores, model = host_cpu()
+    log(f"parity: {exact}/{n_layers} layers bit-exact, {elems} elements, oracle {oracle_s:.1f}s "
+        f"on {threads} threads ({elems / oracle_s / 1e6:.0f} M params/s)")
+    return {"layers": n_layers, "layers_bit_exact": exact, "elements_compared": elems,
+            "mismatches": mismatches, "bad_chunks": bad, "status_nonzero": status_bad,
+            "first_differing_layer": first_bad, "oracle_threads": threads,
+            "oracle_s": oracle_s, "wall_s": wall, "oracle_params_per_s": elems / oracle_s,
+            "host_cores": cores, "cpu_model": model,
+            "what": "every bf16 output of every layer, decoded on the GPU in the timed launch "
+                    "configuration with a status buffer, equals the oracle's decode + dequant of "
+                    "the same compressed bytes; every chunk status is 0"}
 
 
 def d2d_copy_gbs(buf):
@@ -304,9 +407,11 @@ def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
         f"matches GPU: {ok}")
     if not ok:
         raise SystemExit("GPU output differs from the oracle on the CPU-baseline sample")
+    cores, model = host_cpu()
     return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0, first {len(specs)} tensors ({n_sample} params): single-threaded "
-                      "C oracle rANS decode + fp32 dequant + RNE bf16 from the same compressed bytes"}
+                      "C oracle rANS decode + fp32 dequant + RNE bf16 from the same compressed bytes",
+            "host_cores": cores, "cpu_model": model}
 
 
 ENCODE_METRIC = "encoded symbols/s for 70B-shaped layer encode on the GPU (counts, rANS encode, layout, pack)"
