@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle_rows
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -119,9 +120,9 @@ def test_other_calls_reject_adaptive_plans(E):
         E.decode_bf16_split(p, blob, sm, out)
 
 
-def test_llama2_70b_layer_sampled_chunks(E):
+def test_llama2_70b_layer_every_chunk(E):
     import torch
-    _say("70B-shaped layer 0 with per-chunk tables (library host encoder)")
+    _say("70B-shaped layer 0 with per-chunk tables (library host encoder), every element")
     specs = synth.llama2_70b_layer(0)
     b = E.encode_batch_adaptive(specs)
     p = E.plan(b.tensors, None, b.chunks, b.blob.size)
@@ -130,21 +131,12 @@ def test_llama2_70b_layer_sampled_chunks(E):
     total = sum(s["rows"] * s["cols"] for s in specs)
     got, gst = _decode(E, p, blob, total, E.OUT_BF16, scales)
     assert (gst == 0).all()
-    rng = np.random.default_rng(10)
-    picks = sorted(set([0, len(b.chunks) - 1] + [int(v) for v in rng.integers(0, len(b.chunks), 14)]))
-    for k in picks:
-        ch = b.chunks[k]
-        t, n, e0 = int(ch["tensor"]), int(ch["n_symbols"]), int(ch["elem_offset"])
-        sym, st = oracle.decode_adaptive_chunk(b.blob, int(ch["byte_offset"]), n, int(ch["n_words"]))
-        assert st == 0
-        sp = specs[t]
+    for t, sp in enumerate(specs):
         o = int(b.tensors[t]["out_elem_offset"])
-        cols = sp["cols"]
-        r0, r1 = e0 // cols, (e0 + n - 1) // cols       # the rows the chunk touches
-        full = np.zeros((r1 - r0 + 1) * cols, np.uint8)
-        full[e0 - r0 * cols:e0 - r0 * cols + n] = sym
-        want = oracle.dequant_tensor(full, r1 - r0 + 1, cols, sp["kind"], sp["scales"][r0:r1 + 1])
-        np.testing.assert_array_equal(got[o + e0:o + e0 + n], want[e0 - r0 * cols:e0 - r0 * cols + n])
+        n = sp["rows"] * sp["cols"]
+        want = oracle_rows.tensor_from_oracle(b.blob, b.chunks[b.chunks["tensor"] == t], None,
+                                              sp, adaptive=True)
+        np.testing.assert_array_equal(got[o:o + n], want.ravel(), err_msg=sp["name"])
 
 
 def test_exponent_streams_with_per_chunk_tables(E):

@@ -1,7 +1,8 @@
 """GPU parity of a single large tensor decoded on its own: the LLaMA-2-70B
 output projection (32,000 x 8,192 int8 codes), through the bf16 decode and
 through the fused decode + product (logits for 16 activation rows).
-Expected values: the oracle, row by row from the chunks that hold them."""
+Expected values: the oracle's decode + dequant of every element, and the
+fp64 product with those weights for every output row."""
 import numpy as np
 import pytest
 
@@ -36,13 +37,9 @@ def _container(E, chunk_symbols):
     return specs, b, p, torch.from_numpy(b.blob).cuda(), torch.from_numpy(specs[0]["scales"]).cuda()
 
 
-def _rows(rng, n):
-    return sorted(set([0, 1, n - 1] + [int(v) for v in rng.integers(0, n, 9)]))
-
-
 def test_lm_head_bf16_decode(E):
     import torch
-    _say("LM head 32000 x 8192, 65,536-symbol chunks, bf16 decode")
+    _say("LM head 32000 x 8192, 65,536-symbol chunks, bf16 decode, every element")
     specs, b, p, blob, scales = _container(E, 65536)
     sp = specs[0]
     out = torch.empty(sp["rows"] * sp["cols"], dtype=torch.int16, device="cuda")
@@ -50,16 +47,14 @@ def test_lm_head_bf16_decode(E):
     E.decode(p, blob, out, E.OUT_BF16, scales, status)
     torch.cuda.synchronize()
     assert (status.cpu().numpy() == 0).all()
-    got = out.view(sp["rows"], sp["cols"])
-    rows = _rows(np.random.default_rng(8), sp["rows"])
-    want = oracle_rows.rows_from_oracle(b.blob, b.chunks, b.freq[0], sp, rows)
-    for r in rows:
-        assert np.array_equal(got[r].cpu().numpy().view(np.uint16), want[r]), r
+    got = out.cpu().numpy().view(np.uint16).reshape(sp["rows"], sp["cols"])
+    want = oracle_rows.tensor_from_oracle(b.blob, b.chunks, b.freq[0], sp)
+    np.testing.assert_array_equal(got, want)
 
 
 def test_lm_head_fused_logits(E):
     import torch
-    _say("LM head, row-aligned 32,768-symbol chunks, fused logits for 16 rows")
+    _say("LM head, row-aligned 32,768-symbol chunks, fused logits for 16 rows, every row")
     specs, b, p, blob, scales = _container(E, 32768)
     sp = specs[0]
     rng = np.random.default_rng(9)
@@ -71,10 +66,5 @@ def test_lm_head_fused_logits(E):
     torch.cuda.synchronize()
     got = y.cpu().numpy()
     assert not np.isnan(got).any()
-    rows = _rows(rng, sp["rows"])
-    W = oracle_rows.rows_from_oracle(b.blob, b.chunks, b.freq[0], sp, rows)
-    for r in rows:
-        w = _f32(W[r]).astype(np.float64)
-        ref = x.astype(np.float64) @ w
-        bound = sp["cols"] * 2.0 ** -24 * (np.abs(x.astype(np.float64)) @ np.abs(w))
-        assert (np.abs(got[:, r] - ref) <= bound).all(), r
+    W = oracle_rows.tensor_from_oracle(b.blob, b.chunks, b.freq[0], sp)
+    assert oracle_rows.check_product(got, x, W) == sp["rows"]
