@@ -149,11 +149,73 @@ __device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t l
     return *reinterpret_cast<const uint32_t *>(sm_block + 4u * lane);
 }
 
-// PRIO: progress-based wave priority (below); off for launches with one
+// Progress-based wave priority: a wave drops one level once it has done
+// half of its blocks, again at three quarters and at seven eighths (half of
+// what is left each time), so waves that are behind win issue arbitration
+// near the end. (The default favours the oldest waves: the younger
+// workgroup on a CU, and the younger waves of a workgroup, then finish long
+// after the rest, with the CU half idle. Drops every quarter of the blocks,
+// or from the first eighth on, left a longer tail.)
+struct Prio {
+    uint32_t my_blocks, done, at, level;
+    __device__ __forceinline__ void start(uint32_t blocks) {
+        my_blocks = blocks;
+        done = 0;
+        at = blocks / 2 ? blocks / 2 : 1;
+        level = 3;
+        __builtin_amdgcn_s_setprio(3);
+    }
+    __device__ __forceinline__ void tick() {
+        if (__builtin_expect(++done == at, 0)) {
+            at += (my_blocks - at) / 2 ? (my_blocks - at) / 2 : 1;
+            --level;
+            if (level == 2) __builtin_amdgcn_s_setprio(2);
+            else if (level == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
+    }
+};
+
+// The full blocks of one chunk to bf16. The e4m3 / int8 choice is made once
+// per chunk (a template argument), and rows are counted down in blocks: the
+// next row's scale is loaded once the last block of a row is converted, if
+// that row has a block in this chunk (no scale past the chunk's last row is
+// read). (Moving a block's conversion and store into the LDS-read shadows of
+// the next block's first step made the layer decode 15 % slower.)
+template <bool E4M3, bool PRIO>
+__device__ __forceinline__ void blocks_bf16(Stream &s, uint32_t &x, const uint2 *T,
+                                            uint16_t *stage, uint32_t lane, uint32_t full_blocks,
+                                            uint32_t cols, uint32_t &col,
+                                            const float *&scale_row, float &scale,
+                                            uint16_t *&o16, Prio &pr) {
+    // blocks of the current row still to convert (col is a multiple of the block)
+    uint32_t row_left = (cols - col) / kBlockSyms;
+    const uint32_t row_blocks = cols / kBlockSyms;
+    for (uint32_t b = 0; b < full_blocks; ++b) {
+        if (PRIO) pr.tick();
+        if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
+#pragma unroll
+        for (uint32_t t = 0; t < kBlockSteps; ++t)
+            stream_step<false>(x, s.pos, T, stage + 64u * t, lane, true);
+        // lane k: symbols 4k .. 4k+3 of the block (bytes 1, 3, 5, 7)
+        const uint2 d = *reinterpret_cast<const uint2 *>(stage + 4u * lane);
+        reinterpret_cast<uint2 *>(o16)[lane] =
+            make_uint2(dequant2<E4M3>(d.x, scale), dequant2<E4M3>(d.y, scale));
+        o16 += kBlockSyms;
+        if (__builtin_expect(--row_left == 0, 0) && b + 1 < full_blocks) {  // b ends a row
+            row_left = row_blocks;
+            ++scale_row;
+            scale = *scale_row;
+        }
+    }
+    col = cols - row_left * kBlockSyms;
+}
+
+// PRIO: progress-based wave priority (Prio); off for launches with one
 // chunk per workgroup, where the waves do not compete and its per-block
 // bookkeeping only lengthens each wave's chain.
 template <int MODE, bool PRIO>
-__global__ __launch_bounds__(kThreads) void decode_stream(
+__global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_stream(
     const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
     const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks, uint32_t task0,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
@@ -175,19 +237,13 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
     // number of waves busy
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
     const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
-    // Wave priority by progress: a wave drops one level once it has done
-    // half of its blocks, again at three quarters and at seven eighths (half
-    // of what is left each time), so waves that are behind win issue
-    // arbitration near the end. (The default favours the oldest waves: the
-    // younger workgroup on a CU, and the younger waves of a workgroup, then
-    // finish long after the rest, with the CU half idle. Drops every quarter
-    // of the blocks, or from the first eighth on, left a longer tail.)
-    uint32_t my_blocks = 0;
-    if (PRIO)
+    Prio pr = {};
+    if (PRIO) {
+        uint32_t my_blocks = 0;
         for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
             my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
-    uint32_t done = 0, prio_at = my_blocks / 2 ? my_blocks / 2 : 1, prio = 3;
-    if (PRIO) __builtin_amdgcn_s_setprio(3);
+        pr.start(my_blocks);
+    }
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         const uint8_t *region = blob + ch.byte_offset;
@@ -218,13 +274,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
         uint8_t *o8 = static_cast<uint8_t *>(out) + ch.out_elem;
 
         auto block = [&](uint32_t b, uint32_t &sm_reg) __attribute__((always_inline)) {
-            if (PRIO && ++done == prio_at) {
-                prio_at += (my_blocks - prio_at) / 2 ? (my_blocks - prio_at) / 2 : 1;
-                --prio;
-                if (prio == 2) __builtin_amdgcn_s_setprio(2);
-                else if (prio == 1) __builtin_amdgcn_s_setprio(1);
-                else __builtin_amdgcn_s_setprio(0);
-            }
+            if (PRIO) pr.tick();
             if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
@@ -234,19 +284,6 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
             if (MODE == kModeCodes) {
                 reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
                 o8 += kBlockSyms;
-            } else if (MODE == kModeBf16) {
-                // the previous block ended a row: this one starts the next
-                // (only rows that get outputs have their scale read)
-                if (col == cols) {
-                    col = 0;
-                    ++scale_row;
-                    scale = *scale_row;
-                }
-                const uint2 w = e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
-                                     : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
-                reinterpret_cast<uint2 *>(o16)[lane] = w;
-                o16 += kBlockSyms;
-                col += kBlockSyms;
             } else {
                 // per 16-bit half: exponent << 8 | sign+mantissa
                 const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm_reg, 0x07010500u)),
@@ -264,7 +301,14 @@ __global__ __launch_bounds__(kThreads) void decode_stream(
             }
         };
         uint32_t b = 0;
-        if (MODE == kModeSplit) {
+        if (MODE == kModeBf16) {
+            if (e4m3)
+                blocks_bf16<true, PRIO>(s, x, T, G.stage, lane, full_blocks, cols, col, scale_row,
+                                        scale, o16, pr);
+            else
+                blocks_bf16<false, PRIO>(s, x, T, G.stage, lane, full_blocks, cols, col,
+                                         scale_row, scale, o16, pr);
+        } else if (MODE == kModeSplit) {
             for (; b + kSmAhead <= full_blocks; b += kSmAhead)
 #pragma unroll
                 for (uint32_t j = 0; j < kSmAhead; ++j) block(b + j, smr[j]);

@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t l
 // activation fragments of a block are one contiguous run of MT x 512 bytes
 // instead of 16 rows x 32 bytes per group.
 template <int MT, bool SPLIT, bool PACKED>
-__global__ __launch_bounds__(kThreads) void decode_gemm(const SlotEntry *__restrict__ tables,
+__global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_gemm(const SlotEntry *__restrict__ tables,
                                                         const DevChunk *__restrict__ chunks,
                                                         const uint8_t *__restrict__ blob,
                                                         const float *__restrict__ scales,

@@ -24,6 +24,15 @@ constexpr uint32_t kMaxChunkSymbols = 1u << 20;
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 
+// Scalar registers a wave of a kWaves-wave kernel may use so that two of its
+// workgroups (8 waves per SIMD) are resident on a CU at once. Measured on
+// MI355X with workgroups of 16 waves: 80 scalar registers in total (VCC and
+// the other reserved ones included) still let two workgroups start
+// together, 83 or more let only one start, whatever the LDS size -- and the
+// second workgroup then waits until waves of the first exit. The compiler's
+// own occupancy estimate does not see this, so the kernels cap the count.
+#define ENTQ_TWO_WORKGROUPS_SGPRS __attribute__((amdgpu_num_sgpr(80)))
+
 // The streaming kernel works in blocks of kBlockSteps steps (256 symbols
 // per chunk); a tensor can use it when its chunk size is a multiple of the
 // block, and, for bf16 output, when a block never crosses a row.
