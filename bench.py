@@ -75,8 +75,9 @@ def parse():
                     help="resident layers of source codes the encode steps cycle through")
     ap.add_argument("--split-chunk-rows", type=int, default=1,
                     help="fused: rows per chunk of the lone BF16 8192 x 8192 split case")
-    ap.add_argument("--row-chunk-max", type=int, default=32768,
-                    help="fused: a chunk holds as many whole rows as fit in this many symbols")
+    ap.add_argument("--row-chunk-max", type=int, default=8192,
+                    help="fused: a chunk holds as many whole rows as fit in this many symbols "
+                         "(at least one; 8192: one row of every 70B-shaped tensor per chunk)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain fp32 negate (read N MiB, write N MiB) before timing, as a "
                          "known-size reference for hardware byte counters")
@@ -712,16 +713,18 @@ def oracle_tensor_sample(blob, chunks, freq, spec, n_chunks):
     return bits, time.perf_counter() - t, n
 
 
-def compressed_layers_row_aligned(args, E, synth, dev, torch):
-    """The 80 layers encoded on the device with chunks of whole rows (8 rows
-    of 8192 columns, 2 rows of 28672), as the fused kernel needs."""
+def compressed_layers_row_aligned(args, E, synth, dev, torch, row_chunk_max=None):
+    """The 80 layers encoded on the device with chunks of whole rows, as many
+    as fit in row_chunk_max symbols (at least one), as the fused kernel
+    needs."""
     nthreads = args.threads or synth.default_threads()
+    rcm = row_chunk_max or args.row_chunk_max
     t0 = time.time()
     layers, out_elems, tens, meta0 = [], 0, None, None
     for layer in range(args.layers):
         specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
         for sp in specs:
-            sp["chunk_symbols"] = sp["cols"] * max(1, args.row_chunk_max // sp["cols"])
+            sp["chunk_symbols"] = sp["cols"] * max(1, rcm // sp["cols"])
         ds = [dict(sp, symbols=torch.from_numpy(
             np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()).to(dev)) for sp in specs]
         b = E.encode_batch_device(ds)
@@ -733,7 +736,8 @@ def compressed_layers_row_aligned(args, E, synth, dev, torch):
             meta0 = (b.chunks, b.freq, [dict(sp, symbols=None) for sp in specs])
         del ds, b
         if layer % 10 == 0 or layer == args.layers - 1:
-            log(f"layer {layer} encoded on the device, row-aligned chunks ({time.time() - t0:.1f}s)")
+            log(f"layer {layer} encoded on the device, row-aligned chunks of at most {rcm} "
+                f"symbols ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return layers, out_elems, tens, meta0
@@ -744,8 +748,11 @@ def bench_fused(args):
     Y = X . W^T (q,k,v,gate,up from X [m, 8192], o from an [m, 8192] and down
     from an [m, 28672] activation, synthetic bf16) for m activation rows.
     Fused: one entq_decode_gemm launch per layer (fp32 Y, the bf16 weights
-    never written). Unfused: entq_decode into a bf16 layer buffer, then seven
-    torch.mm (bf16 Y). HIP events around every launch on the one stream."""
+    never written) on a container of one-row chunks (--row-chunk-max).
+    Unfused: entq_decode into a bf16 layer buffer, then seven torch.mm (bf16
+    Y), on the container the decode runs fastest on (whole rows in chunks of
+    at most 65,536 symbols, as the layer-decode line's). HIP events around
+    every launch on the one stream."""
     import torch
 
     import entropy_coded_weight_amd as E
@@ -755,6 +762,7 @@ def bench_fused(args):
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     layers, out_elems, tens, meta0 = compressed_layers_row_aligned(args, E, synth, dev, torch)
+    dec_layers = compressed_layers_row_aligned(args, E, synth, dev, torch, 65536)[0]
     names = [n for n, _, _ in synth.LLAMA2_70B_LAYER]
     views = [(names[t], int(tens["rows"][t]), int(tens["cols"][t]), int(tens["out_elem_offset"][t]))
              for t in range(len(tens))]
@@ -781,7 +789,7 @@ def bench_fused(args):
 
         def unfused(ev=None):
             W = buf.view(torch.bfloat16)
-            for li, (p_, blob, sc_) in enumerate(layers):
+            for li, (p_, blob, sc_) in enumerate(dec_layers):
                 if ev is not None:
                     ev[li][0].record(stream)
                 E.decode(p_, blob, buf, E.OUT_BF16, sc_, None, stream)
@@ -791,7 +799,7 @@ def bench_fused(args):
                     ev[li][1].record(stream)
 
         def decode_only(ev=None):
-            for li, (p_, blob, sc_) in enumerate(layers):
+            for li, (p_, blob, sc_) in enumerate(dec_layers):
                 if ev is not None:
                     ev[li][0].record(stream)
                 E.decode(p_, blob, buf, E.OUT_BF16, sc_, None, stream)
@@ -846,7 +854,11 @@ def bench_fused(args):
             "layers": args.layers,
             "params_per_layer": out_elems,
             "compressed_bytes_per_layer": blob_mean,
-            "chunking": f"whole rows, at most {args.row_chunk_max} symbols per chunk",
+            "chunking": f"fused: whole rows, at most {args.row_chunk_max} symbols per chunk "
+                        "(at least one row); unfused and decode only: whole rows, at most "
+                        "65,536 symbols per chunk",
+            "unfused_compressed_bytes_per_layer": float(np.mean([l[1].numel()
+                                                                 for l in dec_layers])),
             "results": results,
             "bf16_split_8192x8192": split,
         },
@@ -965,7 +977,7 @@ def bench_lm_head(args):
     encoded in 32,768-symbol chunks (8,000 chunks, whole rows): the line's
     value is that bf16 decode; 65,536 and 16,384 are timed beside it. Also
     logits for m activation rows, fused (entq_decode_gemm) against decode +
-    torch.mm, on the 32,768 container."""
+    torch.mm, on the one-row (8,192-symbol) and the 32,768 containers."""
     import torch
 
     import entropy_coded_weight_amd as E
@@ -977,7 +989,7 @@ def bench_lm_head(args):
     stream = torch.cuda.current_stream()
     nthreads = args.threads or synth.default_threads()
     conts = {}
-    for C in (32768, 65536, 16384):
+    for C in (32768, 65536, 16384, 8192):
         specs = synth.llama2_70b_lm_head(nthreads=nthreads, chunk_symbols=C)
         ds = [dict(sp, symbols=torch.from_numpy(
             np.ascontiguousarray(sp["symbols"]).view(np.uint8).ravel()).to(dev)) for sp in specs]
@@ -1016,7 +1028,6 @@ def bench_lm_head(args):
                   "alg_gbs": alg / (us / 1e6) / 1e9}
         log(f"lm head decode, {C}-symbol chunks ({nch}): {us:.1f} us, "
             f"{dec[C]['alg_gbs']:.0f} GB/s")
-    p, blob, sc, nbytes, nch = conts[32768]
     W = out.view(torch.bfloat16)
     logits = []
     gen = torch.Generator().manual_seed(0)
@@ -1024,15 +1035,19 @@ def bench_lm_head(args):
         X = (torch.randn(m, cols, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         Y = torch.empty(m, rows, dtype=torch.float32, device=dev)
         Yb = torch.empty(m, rows, dtype=torch.bfloat16, device=dev)
+        for C in (8192, 32768):
+            p, blob, sc, nbytes, nch = conts[C]
 
-        def unfused():
-            E.decode(p, blob, out, E.OUT_BF16, sc, None, stream)
-            torch.mm(X, W.view(rows, cols).t(), out=Yb)
+            def unfused():
+                E.decode(p, blob, out, E.OUT_BF16, sc, None, stream)
+                torch.mm(X, W.view(rows, cols).t(), out=Yb)
 
-        f_us = timed(lambda: E.decode_gemm(p, blob, sc, [X], [Y], None, stream), reps)
-        u_us = timed(unfused, reps)
-        logits.append({"m": m, "fused_us": f_us, "unfused_us": u_us, "speedup": u_us / f_us})
-        log(f"lm head logits m={m}: fused {f_us:.1f} us, decode + GEMM {u_us:.1f} us")
+            f_us = timed(lambda: E.decode_gemm(p, blob, sc, [X], [Y], None, stream), reps)
+            u_us = timed(unfused, reps)
+            logits.append({"m": m, "chunk_symbols": C, "fused_us": f_us, "unfused_us": u_us,
+                           "speedup": u_us / f_us})
+            log(f"lm head logits m={m}, {C}-symbol chunks: fused {f_us:.1f} us, "
+                f"decode + GEMM {u_us:.1f} us")
     cpu = None
     if not args.no_cpu_baseline:
         p, blob, sc, nbytes, nch = conts[32768]
@@ -1353,26 +1368,40 @@ def bench_workloads(args):
     coded("e4m3 4096x4096", synth.e4m3_matrix(), ("codes", "bf16"))
     coded("llama2-13b block", synth.llama2_13b_block(), ("bf16",))
 
+    # The BF16 matrix at several chunk sizes (the pages fix none): each chunk
+    # carries 64 x 4-byte states, so smaller chunks cost more bits, and a
+    # lone matrix fills the GPU with more chunks.
     w = synth.bf16_weights()[0]
     e, sm = E.bf16_split(w["bf16"], n_threads=nthreads)
-    b = E.encode_batch([dict(kind=E.KIND_BF16EXP, rows=w["rows"], cols=w["cols"],
-                             chunk_symbols=w["chunk_symbols"], symbols=e)], n_threads=nthreads)
-    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
-    blob, smd = torch.from_numpy(b.blob).to(dev), torch.from_numpy(sm).to(dev)
     n = w["rows"] * w["cols"]
+    smd = torch.from_numpy(sm).to(dev)
     out = torch.empty(n, dtype=torch.int16, device=dev)
-    med, p10, p90 = timed(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))
-    split_bits = out.cpu().numpy().view(np.uint16)
-    checks["bf16 8192x8192 equals the source weights"] = bool(np.array_equal(split_bits, w["bf16"]))
-    kept["bf16 split"] = (b, sm, split_bits, n)
-    rows_out.append({"workload": "bf16 8192x8192 exponent stream + sign/mantissa", "output": "bf16",
-                     "params": n, "chunks": int(p.n_chunks),
-                     "bits_per_param": 8.0 * (b.blob.size + n) / n,
-                     "us_median": med, "us_p10": p10, "us_p90": p90,
-                     "params_per_s": n / (med / 1e6),
-                     "alg_gbs": (b.blob.size + n + 2 * n) / (med / 1e6) / 1e9})
-    log(f"bf16 8192x8192 split: {med:.1f} us, {rows_out[-1]['alg_gbs']:.0f} GB/s")
-    del blob, smd, out
+    for C in (8192, 16384, 32768, 65536):
+        b = E.encode_batch([dict(kind=E.KIND_BF16EXP, rows=w["rows"], cols=w["cols"],
+                                 chunk_symbols=C, symbols=e)], n_threads=nthreads)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+        blob = torch.from_numpy(b.blob).to(dev)
+        out.zero_()
+        med, p10, p90 = timed(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))
+        split_bits = out.cpu().numpy().view(np.uint16)
+        checks[f"bf16 8192x8192 ({C}-symbol chunks) equals the source weights"] = bool(
+            np.array_equal(split_bits, w["bf16"]))
+        if C == w["chunk_symbols"]:
+            kept["bf16 split"] = (b, sm, split_bits, n)
+        rows_out.append({"workload": "bf16 8192x8192 exponent stream + sign/mantissa",
+                         "output": "bf16", "chunk_symbols": C,
+                         "params": n, "chunks": int(p.n_chunks),
+                         "bits_per_param": 8.0 * (b.blob.size + n) / n,
+                         "exponent_bits_per_param": 8.0 * b.blob.size / n,
+                         "us_median": med, "us_p10": p10, "us_p90": p90,
+                         "params_per_s": n / (med / 1e6),
+                         "alg_gbs": (b.blob.size + n + 2 * n) / (med / 1e6) / 1e9})
+        log(f"bf16 8192x8192 split, {C}-symbol chunks ({p.n_chunks}): {med:.1f} us, "
+            f"{rows_out[-1]['alg_gbs']:.0f} GB/s, {rows_out[-1]['exponent_bits_per_param']:.3f} "
+            "exponent bits per weight")
+        del blob
+        p.close()
+    del smd, out
 
     coded("llama2-70b layer 0", synth.llama2_70b_layer(0, nthreads=nthreads), ("bf16",))
     del flush

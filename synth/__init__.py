@@ -210,11 +210,13 @@ def llama2_13b_block(sigma: float = 1.0, shapes=None):
 
 
 def bf16_weights(rows: int = 8192, cols: int = 8192, sigma: float = 0.02):
-    """BF16 weights N(0, sigma) (RNE from fp32) as uint16 bit patterns."""
+    """BF16 weights N(0, sigma) (RNE from fp32) as uint16 bit patterns;
+    8,192-symbol chunks (one row of the 8192 x 8192 matrix) for the
+    exponent stream."""
     import torch
     w = normal_f32(sigma, rows * cols, key(W_BF16_SPLIT, 0, 0, 0))
     bits = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    return [dict(name="w", kind=KIND_BF16EXP, rows=rows, cols=cols, chunk_symbols=65536,
+    return [dict(name="w", kind=KIND_BF16EXP, rows=rows, cols=cols, chunk_symbols=8192,
                  bf16=bits.copy(), dist=("bf16-normal", sigma))]
 
 

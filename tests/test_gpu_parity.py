@@ -134,12 +134,13 @@ def test_llama2_13b_block_bf16(E):
     np.testing.assert_array_equal(got, want)
 
 
-def test_bf16_exponent_split_8192x8192(E):
-    _say("bf16 exponent split 8192x8192")
+@pytest.mark.parametrize("C", [8192, 65536])
+def test_bf16_exponent_split_8192x8192(E, C):
+    _say(f"bf16 exponent split 8192x8192, {C}-symbol chunks")
     w = synth.bf16_weights()[0]
     e, sm = oracle.bf16_split(w["bf16"])
     spec = dict(kind=oracle.KIND_BF16EXP, rows=w["rows"], cols=w["cols"], symbols=e,
-                chunk_symbols=65536)
+                chunk_symbols=C)
     c = oracle.encode_container([spec])
     got, gst = gpu_decode(E, c, None, split_sm=sm)
     assert np.all(gst == 0)
