@@ -2,7 +2,7 @@
 codes and bf16 output equal the oracle's adaptive decode; BF16 exponent
 streams with per-chunk tables rebuild every bf16 word; a chunk whose table
 is corrupt reports ENTQ_CHUNK_BAD_TABLE while its neighbours decode; a whole
-70B-shaped layer is checked on sampled chunks."""
+70B-shaped layer is checked chunk by chunk, every element."""
 import numpy as np
 import pytest
 

@@ -108,6 +108,45 @@ def test_one_hot_activations_return_the_oracle_weights_exactly(E):
             assert np.array_equal(ys[t].view(np.uint32), want.view(np.uint32)), (t, m)
 
 
+def test_regions_and_scale_rows_far_out(E):
+    """Chunk regions more than 4 GiB into the blob and scale rows more than
+    4 M rows into the scale array: one-hot products still return the
+    oracle's weights exactly (64-bit offsets in the fused kernel)."""
+    import torch
+    specs = _mixed_specs()
+    b = E.encode_batch(specs)
+    W = _oracle_weights(b, specs)
+    G = (1 << 32) + 4096
+    row_shift = (1 << 22) + 3
+    t = b.tensors.copy()
+    t["scale_row_offset"] += row_shift
+    ch = b.chunks.copy()
+    ch["byte_offset"] += np.uint64(G)
+    p = E.plan(t, b.freq, ch, G + b.blob.size)
+    blob = torch.empty(G + b.blob.size, dtype=torch.uint8, device="cuda")
+    blob[G:] = torch.from_numpy(b.blob).cuda()
+    sc = np.concatenate([sp["scales"] for sp in specs])
+    scales = torch.zeros(row_shift + sc.size, dtype=torch.float32, device="cuda")
+    scales[row_shift:] = torch.from_numpy(sc).cuda()
+    rng = np.random.default_rng(9)
+    for m in (1, 16, 40):
+        _say(f"one-hot, far regions and scale rows, m={m}")
+        xs, cols_hit = [], []
+        for sp in specs:
+            c = rng.choice(sp["cols"], m, replace=False)
+            x = np.zeros((m, sp["cols"]), np.float32)
+            x[np.arange(m), c] = 1.0
+            xs.append(x)
+            cols_hit.append(c)
+        ys = _run(E, p, blob, scales, xs, specs)
+        for k, sp in enumerate(specs):
+            want = _f32(W[k][:, cols_hit[k]]).T
+            assert np.array_equal(ys[k].view(np.uint32), want.view(np.uint32)), (k, m)
+    p.close()
+    del blob
+    torch.cuda.empty_cache()
+
+
 def test_random_activations_within_the_accumulation_bound(E):
     specs = _mixed_specs()
     b, p, blob, scales = _setup(E, specs)

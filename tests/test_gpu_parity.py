@@ -272,6 +272,114 @@ def test_gaps_in_output_and_scale_layout(E):
     p.close()
 
 
+def _far_plan(E, c, byte_shift, elem_shift, row_shift, adaptive=False):
+    """A plan of container c with every chunk region moved byte_shift bytes
+    into the blob, every tensor's output elem_shift elements on and its
+    scale rows row_shift rows on."""
+    tens = np.zeros(len(c.tensors), E.TENSOR_DESC)
+    freq = None if adaptive else np.zeros((len(c.tensors), 256), np.uint16)
+    for t, td in enumerate(c.tensors):
+        tens[t] = (td["kind"], td["rows"], td["cols"], td["chunk_symbols"], td["n_symbols"],
+                   td["out_elem_offset"] + elem_shift, td["scale_row_offset"] + row_shift)
+        if not adaptive:
+            freq[t] = td["freq"]
+    ch = np.zeros(c.n_chunks, E.CHUNK_DESC)
+    ch["tensor"], ch["n_symbols"], ch["n_words"] = c.chunks[:, 0], c.chunks[:, 1], c.chunks[:, 2]
+    ch["byte_offset"] = c.chunks[:, 3] + np.uint64(byte_shift)
+    ch["elem_offset"] = c.chunks[:, 4]
+    return E.plan(tens, freq, ch, byte_shift + c.blob.size)
+
+
+def _far_blob(c, byte_shift):
+    import torch
+    blob = torch.empty(byte_shift + c.blob.size, dtype=torch.uint8, device="cuda")
+    blob[byte_shift:] = torch.from_numpy(c.blob).cuda()
+    return blob
+
+
+def _check_far_output(out, shift, want, fill):
+    """out[shift:] equals want; nothing before it was written (checked on
+    the device, without copying gigabytes back)."""
+    import torch
+    torch.cuda.synchronize()
+    assert not bool((out[:shift] != fill).any()), "a write landed before the tensor's offset"
+    got = out[shift:].cpu().numpy()
+    np.testing.assert_array_equal(got.view(want.dtype), want)
+
+
+def test_offsets_past_4_gib(E):
+    """Chunk regions more than 4 GiB into the blob, outputs more than 4 GiB
+    into the output buffer (codes, bf16 and exponent-split outputs) and scale
+    rows far into the scale array land exactly where the chunk index and the
+    tensor table put them, for the streaming, element-wise and per-chunk-table
+    kernels: every offset and address is 64-bit."""
+    import torch
+    G = 1 << 32
+    specs = [synth.random_int8_tensor(16, 1024, 2.0, 41, 4096),   # streaming kernel
+             dict(synth.e4m3_matrix(24, 512)[0], chunk_symbols=4096),
+             synth.random_int8_tensor(7, 333, 1.5, 42, 960)]      # element-wise kernel
+    row_shift = (1 << 22) + 5
+    for adaptive in (False, True):
+        # per-chunk tables take rows of whole 256-symbol blocks only
+        sp = specs[:2] if adaptive else specs
+        scales = all_scales(sp)
+        far_scales = torch.zeros(row_shift + scales.size, dtype=torch.float32, device="cuda")
+        far_scales[row_shift:] = torch.from_numpy(scales).cuda()
+        c = oracle.encode_container_adaptive(sp) if adaptive else oracle.encode_container(sp)
+        if adaptive:
+            syms, st = oracle.decode_container_adaptive_symbols(c)
+            want_codes = np.concatenate(syms)
+            want_bf16, _ = oracle.decode_container_adaptive_bf16(c, scales)
+        else:
+            want_codes, st = expected_codes(c)
+            want_bf16, _ = oracle.decode_container_bf16(c, scales)
+        assert np.all(st == 0)
+        total = want_codes.size
+        blob = _far_blob(c, G + 4096)
+        # codes: byte offsets past 4 GiB
+        shift = G + 48
+        _say(f"offsets past 4 GiB ({'per-chunk' if adaptive else 'shared'} tables): codes")
+        p = _far_plan(E, c, G + 4096, shift, 0, adaptive)
+        status = torch.full((c.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((shift + total,), 0x5A, dtype=torch.uint8, device="cuda")
+        E.decode(p, blob, out, E.OUT_CODES, None, status)
+        _check_far_output(out, shift, want_codes, 0x5A)
+        assert np.all(status.cpu().numpy() == 0)
+        p.close()
+        del out
+        # bf16: element offsets past 2^31 (bytes past 4 GiB), scale rows past 4 M
+        shift = (G >> 1) + 16
+        _say(f"offsets past 4 GiB ({'per-chunk' if adaptive else 'shared'} tables): bf16")
+        p = _far_plan(E, c, G + 4096, shift, row_shift, adaptive)
+        out = torch.full((shift + total,), 0x5A5A, dtype=torch.int16, device="cuda")
+        E.decode(p, blob, out, E.OUT_BF16, far_scales, status)
+        _check_far_output(out, shift, want_bf16, 0x5A5A)
+        assert np.all(status.cpu().numpy() == 0)
+        p.close()
+        del out, blob
+        torch.cuda.empty_cache()
+    # exponent streams: output and sign/mantissa bytes past 2^31 elements
+    w = synth.bf16_weights(3, 70_000, sigma=0.5)[0]["bf16"]
+    e, sm = oracle.bf16_split(w)
+    for C in (4096, 960):
+        _say(f"offsets past 4 GiB: exponent stream, C{C}")
+        c = oracle.encode_container([dict(kind=oracle.KIND_BF16EXP, rows=3, cols=70_000,
+                                          symbols=e, chunk_symbols=C)])
+        blob = _far_blob(c, G + 4096)
+        shift = (G >> 1) + 16
+        p = _far_plan(E, c, G + 4096, shift, 0)
+        far_sm = torch.zeros(shift + sm.size, dtype=torch.uint8, device="cuda")
+        far_sm[shift:] = torch.from_numpy(sm).cuda()
+        status = torch.full((c.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((shift + w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
+        E.decode_bf16_split(p, blob, far_sm, out, status)
+        _check_far_output(out, shift, w, 0x5A5A)
+        assert np.all(status.cpu().numpy() == 0)
+        p.close()
+        del out, blob, far_sm
+        torch.cuda.empty_cache()
+
+
 def test_corrupt_streams_report_the_oracles_status(E):
     _say("corruption statuses")
     specs = [synth.random_int8_tensor(16, 4096, 2.0, 20, 4096)]
