@@ -131,3 +131,26 @@ def test_fused_refuses_mismatched_activations_and_results(E, P):
     sm = torch.zeros(2560, dtype=torch.uint8)
     _rejects(E, E.decode_gemm_bf16_split, P, blob, sm[:5], xs, ys, stream=0,
              match="signmant holds 5")
+
+
+def test_linear_refuses(E, P):
+    from entropy_coded_weight_amd.linear import linear
+    blob = torch.zeros(900, dtype=torch.uint8)
+    sc = torch.ones(7, dtype=torch.float32)
+    xs, ys = _xy(65, [(4, 256), (3, 512)])
+    _rejects(E, linear, P, blob, sc, xs, ys, weights=torch.zeros(2559, dtype=torch.int16),
+             stream=0, match="out holds 2559")
+    _rejects(E, linear, P, blob, sc, xs, ys, weights=torch.zeros(2560, dtype=torch.uint8),
+             stream=0, match="1-byte elements, expected 2")
+    bad = [xs[0], torch.zeros(65, 511, dtype=torch.bfloat16)]
+    _rejects(E, linear, P, blob, sc, bad, ys, stream=0, match="x\\[1\\] has 511 columns")
+    _rejects(E, linear, P, blob, sc[:6], xs, ys, stream=0, match="scales holds 6")
+    P.adaptive = True
+    _rejects(E, linear, P, blob, sc, xs, ys, stream=0, match="per-tensor tables")
+    P.adaptive = False
+    P.tensors["kind"][1] = E.KIND_BF16EXP
+    _rejects(E, linear, P, blob, sc, xs, ys, stream=0, match="exponent streams")
+    # up to 64 rows the call is the fused one, with its checks
+    xs, ys = _xy(64, [(4, 256), (3, 512)])
+    P.tensors["kind"][1] = E.KIND_INT8
+    _rejects(E, linear, P, blob[:899], sc, xs, ys, stream=0, match="compressed holds")

@@ -168,6 +168,42 @@ def test_random_activations_within_the_accumulation_bound(E):
                 assert np.isnan(ys[t][:, sp["rows"]:]).all()  # nothing written past the rows
 
 
+def test_linear_with_more_than_64_rows(E):
+    """linear(): beyond 64 activation rows the layer is decoded once and each
+    product is a library GEMM in fp32 accumulation -- within the same bound
+    of the fp64 product of the oracle's weights; up to 64 rows it is the
+    fused kernel, bit for bit."""
+    import torch
+    from entropy_coded_weight_amd.linear import FUSED_MAX_ROWS, linear
+    specs = _mixed_specs()
+    b, p, blob, scales = _setup(E, specs)
+    W = _oracle_weights(b, specs)
+    rng = np.random.default_rng(11)
+    weights = torch.empty(p.out_elems, dtype=torch.int16, device="cuda")
+    for m in (FUSED_MAX_ROWS, FUSED_MAX_ROWS + 1, 300):
+        _say(f"linear, m={m}")
+        xs_h = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+                     & np.uint16(0xBFFF)) for sp in specs]
+        xs = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs_h]
+        ys = [torch.full((m, sp["rows"]), float("nan"), dtype=torch.float32, device="cuda")
+              for sp in specs]
+        status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        linear(p, blob, scales, xs, ys, weights=weights, chunk_status=status)
+        torch.cuda.synchronize()
+        assert (status.cpu().numpy() == 0).all()
+        if m <= FUSED_MAX_ROWS:
+            fused = _run(E, p, blob, scales, xs_h, specs)
+        for t, sp in enumerate(specs):
+            w = _f32(W[t]).astype(np.float64)
+            x = xs_h[t].astype(np.float64)
+            ref = x @ w.T
+            bound = sp["cols"] * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T)
+            got = ys[t].cpu().numpy()
+            assert (np.abs(got - ref) <= bound + 1e-30).all(), (t, m)
+            if m <= FUSED_MAX_ROWS:
+                assert np.array_equal(got.view(np.uint32), fused[t].view(np.uint32)), (t, m)
+
+
 def test_packed_activations_give_the_same_bits(E):
     """With a workspace the activations are first copied into the waves'
     read order; the products are the same bit for bit, padded strides and
