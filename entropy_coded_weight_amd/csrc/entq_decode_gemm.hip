@@ -25,7 +25,9 @@
 // (fixed order) and written out.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "entq.h"
 #include "entq_internal.h"
@@ -353,8 +355,19 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
         pack_blocks = 0;
         return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
     };
-    for (int t = 0; t < plan->n_tensors; ++t) {
-        const HostTensor &h = plan->host_tensors[t];
+    // Workgroups of tensors with the most symbols per chunk (the longest
+    // rows) are dispatched first, so that the launch ends on short
+    // workgroups: with the down projection's 3.5 times longer rows last, the
+    // layer's last 512 workgroups ran alone on the GPU (581 against 575 us
+    // per 70B-shaped layer at m = 16).
+    std::vector<int> order((size_t)plan->n_tensors);
+    for (int i = 0; i < plan->n_tensors; ++i) order[(size_t)i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        return plan->host_tensors[(size_t)a].chunk_symbols >
+               plan->host_tensors[(size_t)b].chunk_symbols;
+    });
+    for (const int t : order) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
         if (h.n_symbols == 0) continue;
         const uint64_t groups = ((uint64_t)h.n_chunks + kWaves - 1) / kWaves;
         const uint64_t pb = ((uint64_t)16 * groups_m * (h.cols / 4) + 255) / 256;
