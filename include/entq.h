@@ -49,7 +49,9 @@
  *                   (sm & 0x7F), exp the decoded symbol, sm the raw byte.
  *
  * Ownership: every device buffer is allocated by the caller; the library
- * never allocates device memory. A plan is host memory owned by the library
+ * never allocates device memory (its only device memory of its own is the
+ * fixed static array of entq_decode_gemm_static, part of its code object,
+ * one per GPU it runs on). A plan is host memory owned by the library
  * until entq_plan_destroy; it points into the caller's device workspace,
  * which must outlive the plan and every decode enqueued with it.
  * Asynchrony: device work is enqueued on the given HIP stream (NULL = the
