@@ -32,6 +32,8 @@
 //    multiple of the 256-symbol block.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "entq.h"
 #include "entq_internal.h"
 #include "entq_stream.h"
@@ -390,18 +392,21 @@ int launch_mode(const entq_plan_t *plan, bool stream, int64_t first, int64_t cou
 }  // namespace
 
 int64_t resident_workgroups() {
-    static int64_t cached[64] = {0};
+    // per device, computed once (threads that race here store the same value)
+    static std::atomic<int64_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
+    int64_t v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
         int64_t per_cu = stream_occupancy<kModeSplit>();  // the largest LDS footprint
         if (per_cu <= 0) per_cu = 1;
-        cached[dev] = (int64_t)cus * per_cu;
+        v = (int64_t)cus * per_cu;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 int launch_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
