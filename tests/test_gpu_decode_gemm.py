@@ -147,6 +147,40 @@ def test_regions_and_scale_rows_far_out(E):
     torch.cuda.empty_cache()
 
 
+def test_more_tensors_than_one_launch_takes(E):
+    """19 tensors (a launch takes 16): int8 and e4m3, 1 to 11 blocks per row,
+    1 to 4 rows per chunk, in an order the launcher rearranges (longest rows
+    first). One-hot activations return the oracle's weights exactly."""
+    rng = np.random.default_rng(21)
+    specs = []
+    for i in range(19):
+        cols = int(rng.choice([256, 512, 768, 1024, 2816]))
+        rows = int(rng.integers(3, 41))
+        chunk_rows = int(rng.integers(1, 5))
+        if i % 5 == 2:
+            sp = synth.e4m3_matrix(rows=rows, cols=cols)[0]
+        else:
+            sp = synth.random_int8_tensor(rows, cols, float(rng.uniform(0.8, 3.0)), 800 + i,
+                                          cols * chunk_rows)
+        sp["chunk_symbols"] = cols * chunk_rows
+        specs.append(sp)
+    b, p, blob, scales = _setup(E, specs)
+    W = _oracle_weights(b, specs)
+    for m in (5, 33):
+        _say(f"19 tensors, one-hot, m={m}")
+        xs, cols_hit = [], []
+        for sp in specs:
+            c = rng.choice(sp["cols"], m, replace=False)
+            x = np.zeros((m, sp["cols"]), np.float32)
+            x[np.arange(m), c] = 1.0
+            xs.append(x)
+            cols_hit.append(c)
+        ys = _run(E, p, blob, scales, xs, specs)
+        for t, sp in enumerate(specs):
+            want = _f32(W[t][:, cols_hit[t]]).T
+            assert np.array_equal(ys[t].view(np.uint32), want.view(np.uint32)), (t, m)
+
+
 def test_random_activations_within_the_accumulation_bound(E):
     specs = _mixed_specs()
     b, p, blob, scales = _setup(E, specs)
