@@ -209,6 +209,7 @@ def main():
         if cpu is not None:
             cpu["all_threads"] = {
                 "value": parity["oracle_params_per_s"], "unit": "params/s",
+                "gbs": alg_bytes_layer * args.layers / parity["oracle_s"] / 1e9,
                 "threads": parity["oracle_threads"],
                 "sample": f"all {args.layers} layers ({parity['elements_compared']} params): the "
                           "same single-threaded oracle functions over disjoint row-aligned chunk "
@@ -403,6 +404,12 @@ def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
         assert np.all(st == 0)
         outs.append(oracle.dequant_tensor(sym, sp["rows"], sp["cols"], sp["kind"], sp["scales"]))
     dt = time.perf_counter() - t
+    # the same byte accounting as the GPU line: compressed regions, scales, bf16 written
+    comp = 0
+    for ti in range(len(specs)):
+        nw = b.chunks[b.chunks["tensor"] == ti]["n_words"].astype(np.int64)
+        comp += int(np.sum((256 + 2 * nw + 15) // 16 * 16))
+    alg = comp + 4 * sum(int(s["rows"]) for s in specs) + 2 * n_sample
     ok = bool(np.array_equal(np.concatenate(outs), gpu))
     log(f"cpu oracle: {n_sample} params in {dt:.2f}s ({n_sample / dt / 1e6:.1f} M params/s); "
         f"matches GPU: {ok}")
@@ -412,6 +419,8 @@ def cpu_baseline(sample, plan0, blob0, scales0, out_gpu, stream):
     return {"value": n_sample / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"layer 0, first {len(specs)} tensors ({n_sample} params): single-threaded "
                       "C oracle rANS decode + fp32 dequant + RNE bf16 from the same compressed bytes",
+            "gbs": alg / dt / 1e9, "sample_seconds": dt,
+            "x80_layers_seconds_extrapolated": dt * 80.0 * (plan0.out_elems / n_sample),
             "host_cores": cores, "cpu_model": model}
 
 
