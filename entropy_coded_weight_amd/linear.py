@@ -40,7 +40,8 @@ def linear(p: Plan, compressed, scales, xs, ys, weights=None, chunk_status=None,
     if np.any(p.tensors["kind"] == KIND_BF16EXP):
         raise EntqError(EINVAL, "linear takes Int8 and E4M3 tensors; exponent streams use "
                                 "decode_gemm_bf16_split")
-    if weights is None:
+    own = weights is None
+    if own:
         weights = torch.empty(p.out_elems, dtype=torch.int16, device=p.device)
     decode(p, compressed, weights, OUT_BF16, scales, chunk_status, stream)
     w = weights.view(torch.bfloat16)
@@ -51,6 +52,8 @@ def linear(p: Plan, compressed, scales, xs, ys, weights=None, chunk_status=None,
              else torch.cuda.default_stream(p.device))
     else:
         s = stream
+    if own:
+        weights.record_stream(s)  # allocated here, used on s
     with torch.cuda.stream(s):
         for t in range(p.n_tensors):
             rows, cols = int(p.tensors[t]["rows"]), int(p.tensors[t]["cols"])
