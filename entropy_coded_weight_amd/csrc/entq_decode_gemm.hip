@@ -173,9 +173,20 @@ __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_gem
                                                             (uint64_t)kb * kBlockSyms);
             }
             if (live) {
-#pragma unroll
-                for (uint32_t t = 0; t < kBlockSteps; ++t)
-                    stream_step<false>(x, s.pos, T, row_tile + 64u * t, lane, true);
+                // Priority falls as a wave works through the block's steps, so that
+                // the waves behind -- the ones the workgroup will wait for at the
+                // block's barrier -- win issue against those ahead and against the
+                // other workgroup on the CU (573.6 -> 563.7 us per 70B-shaped layer
+                // at m = 16).
+                static_assert(kBlockSteps == 4, "one priority level per step");
+                __builtin_amdgcn_s_setprio(3);
+                stream_step<false>(x, s.pos, T, row_tile, lane, true);
+                __builtin_amdgcn_s_setprio(2);
+                stream_step<false>(x, s.pos, T, row_tile + 64u, lane, true);
+                __builtin_amdgcn_s_setprio(1);
+                stream_step<false>(x, s.pos, T, row_tile + 128u, lane, true);
+                __builtin_amdgcn_s_setprio(0);
+                stream_step<false>(x, s.pos, T, row_tile + 192u, lane, true);
                 // lane k: columns 4k .. 4k+3 of the block, made bf16 in place
                 const uint2 d = *reinterpret_cast<const uint2 *>(row_tile + 4u * lane);
                 uint2 w;
