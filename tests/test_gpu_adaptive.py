@@ -178,3 +178,45 @@ def test_exponent_streams_with_per_chunk_tables(E):
     y2 = torch.zeros(1, 1, dtype=torch.float32, device="cuda")
     with pytest.raises(E.EntqError):
         E.decode_gemm_bf16_split(p, blob, torch.from_numpy(sm_all).cuda(), [x, x2], [y, y2])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_batches_with_per_chunk_tables(E, seed):
+    """Batches of 1-6 tensors with per-chunk tables: random rows, block-aligned
+    row lengths, chunk sizes (multiples of 256 up to 2^16, some not dividing
+    the tensor), int8 of random spread or e4m3, now and then a one-symbol or a
+    uniformly random tensor. Codes and bf16 equal the oracle's adaptive decode,
+    statuses too."""
+    rng = np.random.default_rng(3000 + seed)
+    specs = []
+    for i in range(int(rng.integers(1, 7))):
+        rows = int(rng.integers(1, 48))
+        cols = int(rng.choice([256, 512, 768, 1024, 2560, 4096]))
+        C = int(rng.choice([256, 512, 1280, 4096, 16384, 65536]))
+        u = rng.random()
+        if u < 0.25:
+            sp = synth.e4m3_matrix(rows=rows, cols=cols)[0]
+            sp["chunk_symbols"] = C
+        else:
+            sp = synth.random_int8_tensor(rows, cols, float(rng.uniform(0.3, 6.0)),
+                                          4000 + 10 * seed + i, C)
+            if u > 0.9:
+                sp["symbols"] = np.full(sp["symbols"].shape, int(rng.integers(0, 256)), np.uint8)
+            elif u > 0.8:
+                sp["symbols"] = synth.random_bytes(rows * cols, 4100 + 10 * seed + i).view(np.uint8)
+        specs.append(sp)
+    _say(f"random per-chunk-table batch {seed}: " + ", ".join(
+        f"{s['rows']}x{s['cols']}/C{s['chunk_symbols']}" for s in specs))
+    c = oracle.encode_container_adaptive(specs)
+    p, blob = _plan(E, c)
+    total = sum(td["n_symbols"] for td in c.tensors)
+    syms, st = oracle.decode_container_adaptive_symbols(c)
+    assert (st == 0).all()
+    got, gst = _decode(E, p, blob, total, E.OUT_CODES)
+    np.testing.assert_array_equal(got, np.concatenate(syms))
+    np.testing.assert_array_equal(gst, st)
+    scales = np.concatenate([np.asarray(s["scales"], np.float32) for s in specs])
+    want, _ = oracle.decode_container_adaptive_bf16(c, scales)
+    got, gst = _decode(E, p, blob, total, E.OUT_BF16, scales)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(gst, st)
