@@ -132,6 +132,10 @@ def test_llama2_13b_block_bf16(E):
     got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales)
     np.testing.assert_array_equal(gst, st)
     np.testing.assert_array_equal(got, want)
+    want_codes, st = expected_codes(c)
+    got, gst = gpu_decode(E, c, E.OUT_CODES)
+    np.testing.assert_array_equal(gst, st)
+    np.testing.assert_array_equal(got, want_codes)
 
 
 @pytest.mark.parametrize("C", [8192, 65536])
@@ -160,6 +164,14 @@ def test_llama2_70b_layer0_full(E):
     got, gst = gpu_decode(E, c, E.OUT_BF16, scales=scales)
     assert np.all(gst == 0)
     np.testing.assert_array_equal(got, want)
+    del got, want
+    # codes output of the same container: the source codes (the oracle decode of this
+    # container, inside decode_container_bf16, returned every chunk with status 0)
+    _say("llama2-70b layer 0, codes")
+    got, gst = gpu_decode(E, c, E.OUT_CODES)
+    assert np.all(gst == 0)
+    np.testing.assert_array_equal(got, np.concatenate([np.asarray(s["symbols"], np.uint8)
+                                                       for s in specs]))
 
 
 def test_llama2_70b_last_layer_against_source(E):
