@@ -144,6 +144,10 @@ uint32_t orc_mul_f32_bits(uint32_t vb, uint32_t sb)
 }
 
 /* Dequantisation of one code: bf16 = RNE16(fl32(value(code) * scale)).
+ * [Codes of a full-range base format times per-channel scales: EntQuant
+ *  summary technical part §2 "Codificación de Pesos"; the product is fixed
+ *  as one fp32 multiply rounded to bf16, the library's reading of a decode
+ *  "to usable weights".]
  * One IEEE single-precision multiply, rounded to nearest even, then the
  * fp32 -> bf16 rounding above. */
 uint16_t orc_dequant_bf16(uint8_t code, int kind, float scale)
@@ -173,6 +177,10 @@ uint16_t orc_bf16_merge(uint8_t exp_byte, uint8_t sm_byte)
 /* ------------------------------------------------------------------------ */
 
 /* Quantise symbol counts to frequencies that sum to M = 4096.
+ * [The pages fix no rule: the EntQuant summary, technical part §2
+ *  "Codificación de Pesos", says only that the symbol stream is entropy
+ *  coded. This rule is the library's reading; any table that sums to M and
+ *  gives every present symbol f >= 1 decodes exactly.]
  *   present symbol s : f[s] = max(1, round(c[s] * M / N))  (half rounds up)
  *   absent symbol    : f[s] = 0
  *   while the sum exceeds M: take 1 from the largest f (smallest symbol on a
@@ -262,6 +270,10 @@ int orc_table_valid(const uint16_t freq[256])
 /* ------------------------------------------------------------------------ */
 
 /* Encode n symbols with K interleaved lanes.
+ * [Range ANS encode step: Duda, "Asymmetric numeral systems" (2013);
+ *  interleaved states: Giesen, "Interleaved entropy coders" (2014). The pages
+ *  name the coder only: EntQuant summary technical part §2, and rANS in the
+ *  discussion under the DFloat11 write-up.]
  *
  * The decoder reads symbols front to back, so the encoder walks them back to
  * front. Every lane starts at x = L. For symbol i (lane j = i mod K, symbol s
@@ -313,7 +325,10 @@ int64_t orc_encode_chunk(const uint8_t *sym, uint32_t n, uint32_t K,
     return (int64_t)n_emitted;
 }
 
-/* Decode n symbols with K interleaved lanes, front to back.
+/* [Range ANS decode step (Duda 2013) with interleaved lanes (Giesen 2014);
+ *  the device decodes during inference: EntQuant summary technical part §2
+ *  "Decodificación en Tiempo de Inferencia".]
+ * Decode n symbols with K interleaved lanes, front to back.
  * States x_j start at states[j]; the word pointer p starts at 0. For symbol
  * i = 0, 1, ..., n-1 (lane j = i mod K; so within a step of K symbols the
  * lanes go in ascending order):
@@ -370,7 +385,10 @@ int orc_decode_chunk(const uint32_t *states, const uint16_t *words,
 /* 4. Container: one tensor as a run of chunk regions                        */
 /* ------------------------------------------------------------------------ */
 
-/* A tensor of n symbols is cut into chunks of C symbols (the last one may be
+/* [Independent segments decoded at once: EntroLLM summary, "Metodología"
+ *  item 3; weights decoded on the device before a block runs: EntQuant
+ *  summary technical part §2 "Decodificación en Tiempo de Inferencia".]
+ * A tensor of n symbols is cut into chunks of C symbols (the last one may be
  * shorter): chunk k holds symbols [kC, min((k+1)C, n)). Each chunk region is
  *     uint32 states[64]   little-endian, state of lane j at index j
  *     uint16 words[n_w]   little-endian, in decoder order
