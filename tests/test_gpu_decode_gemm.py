@@ -370,6 +370,48 @@ def test_bf16_split_one_hot_returns_the_source_weights(E, rows, blocks, chunk_ro
         assert np.array_equal(y.view(np.uint32), _f32(w[:, c]).T.view(np.uint32)), m
 
 
+def test_bf16_split_over_more_tensors_than_one_launch_takes(E):
+    """18 exponent-stream tensors (a launch takes 16), 1 to 7 blocks per row and
+    1 to 4 rows per chunk, reordered by the launcher (longest rows first): with
+    one-hot activations every output is a source bf16 weight, bit for bit."""
+    import torch
+    rng = np.random.default_rng(23)
+    specs, ws, sms = [], [], []
+    for i in range(18):
+        cols = 256 * int(rng.integers(1, 8))
+        rows = int(rng.integers(2, 30))
+        w = rng.integers(0, 1 << 16, size=rows * cols, dtype=np.uint64).astype(np.uint16)
+        w[(w & 0x7F80) == 0x7F80] &= 0xBFFF  # finite weights, so that 1.0 * w is w
+        w[w == 0x8000] = 0  # a -0 weight would come out +0 (+0 + -0 = +0 in the sums)
+        e, sm = oracle.bf16_split(w)
+        specs.append(dict(kind=oracle.KIND_BF16EXP, rows=rows, cols=cols, symbols=e,
+                          chunk_symbols=cols * int(rng.integers(1, 5))))
+        ws.append(w.reshape(rows, cols))
+        sms.append(sm)
+    b = E.encode_batch(specs)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    sm_all = torch.from_numpy(np.concatenate(sms)).cuda()
+    m = 9
+    xs, ys, hit = [], [], []
+    for sp in specs:
+        c = rng.choice(sp["cols"], m, replace=False)
+        x = np.zeros((m, sp["cols"]), np.float32)
+        x[np.arange(m), c] = 1.0
+        xs.append(torch.from_numpy(x).to(torch.bfloat16).cuda())
+        ys.append(torch.full((m, sp["rows"]), float("nan"), dtype=torch.float32, device="cuda"))
+        hit.append(c)
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    _say("bf16 split, 18 tensors, one-hot, m=9")
+    E.decode_gemm_bf16_split(p, blob, sm_all, xs, ys, status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    for t in range(len(specs)):
+        want = _f32(ws[t][:, hit[t]]).T
+        assert np.array_equal(ys[t].cpu().numpy().view(np.uint32), want.view(np.uint32)), t
+    p.close()
+
+
 def test_bf16_split_8192x8192_within_the_accumulation_bound(E):
     _say("bf16 split 8192x8192, 8-row chunks, m = 16, every row")
     rows = cols = 8192
