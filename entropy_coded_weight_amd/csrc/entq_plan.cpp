@@ -301,8 +301,9 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     if (hipMemcpyAsync(d_workspace, img, lay.total, hipMemcpyHostToDevice, (hipStream_t)stream) !=
             hipSuccess ||
         hipEventRecord(ev, (hipStream_t)stream) != hipSuccess) {
-        hipStreamSynchronize((hipStream_t)stream);  // a copy may have been enqueued
-        hipEventDestroy(ev);
+        // cleanup after a failure: errors here change nothing the caller can act on
+        (void)hipStreamSynchronize((hipStream_t)stream);  // a copy may have been enqueued
+        (void)hipEventDestroy(ev);
         delete p;
         std::free(img);
         return ENTQ_EHIP;
@@ -357,8 +358,9 @@ entq_status entq_plan_adaptive(const entq_tensor_desc *tensors, int n_tensors,
 void entq_plan_destroy(entq_plan_t *plan) {
     if (!plan) return;
     if (plan->upload_done) {
-        hipEventSynchronize((hipEvent_t)plan->upload_done);  // the upload read host_staging
-        hipEventDestroy((hipEvent_t)plan->upload_done);
+        // destroy cannot report errors; waiting is what keeps host_staging valid
+        (void)hipEventSynchronize((hipEvent_t)plan->upload_done);  // the upload read host_staging
+        (void)hipEventDestroy((hipEvent_t)plan->upload_done);
     }
     std::free(plan->host_staging);
     delete plan;
