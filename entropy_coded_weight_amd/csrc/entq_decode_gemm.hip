@@ -333,6 +333,10 @@ uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m) {
 int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *scales,
                        const uint8_t *signmant, const entq_gemm_io *io, int m,
                        uint8_t *workspace, int32_t *status, void *stream) {
+    // a few activation rows: the product on the vector units, waves free of
+    // one another (no tiles, no barrier), and no workspace
+    if (m <= kGemvMaxRows && plan->n_tensors <= kGemvMaxTensors)
+        return launch_decode_gemv(plan, blob, scales, signmant, io, m, status, stream);
     GemmArgs args = {};
     args.m = (uint32_t)m;
     PackArgs pack = {};

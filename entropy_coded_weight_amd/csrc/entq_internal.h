@@ -82,6 +82,7 @@ struct HostTensor {
     int64_t chunk_base;     // its first DevChunk (chunks in element order)
     int64_t n_chunks;
     uint64_t out_elem_offset;
+    uint64_t scale_row_offset;
 };
 
 }  // namespace entq
@@ -130,6 +131,15 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
                        const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
                        uint8_t *workspace, int32_t *status, void *stream);
 uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m);
+// The same product for at most kGemvMaxRows activation rows without matrix
+// cores (entq_decode.hip), for plans of at most kGemvMaxTensors tensors whose
+// chunks hold whole rows of a multiple of kBlockSyms columns; signmant
+// non-null for BF16 exponent streams.
+constexpr int kGemvMaxRows = 4;
+constexpr int kGemvMaxTensors = 16;
+int launch_decode_gemv(const entq_plan_t *plan, const void *blob, const float *scales,
+                       const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
+                       int32_t *status, void *stream);
 // Workgroups of the decode kernels that fit on the current device at once
 // (compute units x workgroups per compute unit); 0 if HIP cannot tell.
 int64_t resident_workgroups();

@@ -268,6 +268,16 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * holds whole rows). d_chunk_status as in entq_decode. Enqueued on stream;
  * the summation order is fixed (results are reproducible run to run).
  *
+ * Two kernels compute the product. For m <= 4 (and plans of at most 16
+ * tensors) it runs on the vector units inside the decode loop: each lane
+ * adds the products of its 4 weights per 256 columns with v_dot2_f32_bf16,
+ * the 64 lanes' sums of a weight row are added in a fixed tree, and no
+ * workspace is used. Otherwise weight tiles go through the matrix cores
+ * (v_mfma_f32_16x16x16_bf16) and partial sums are added across waves. Both
+ * stay within cols * 2^-24 * sum_c |X[i][c] W[r][c]| of the exact product;
+ * their summation orders differ, so results at m <= 4 and m > 4 are not
+ * bitwise comparable.
+ *
  * d_workspace: NULL, or device memory (256-byte aligned, at least
  * entq_decode_gemm_workspace_bytes(plan, m) bytes, else ENTQ_EALIGN /
  * ENTQ_EWORKSPACE) into which the call first copies each tensor's
@@ -275,7 +285,8 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
  * reads one contiguous run per 256 columns instead of 16 rows of 32 bytes.
  * The results are the same bit for bit either way; with more than 16
  * activation rows the workspace makes the call several times faster. The
- * workspace must not be used by other work while the call runs. */
+ * workspace must not be used by other work while the call runs. For m <= 4
+ * it is not touched. */
 typedef struct {
     const void *d_x;
     uint64_t ldx;

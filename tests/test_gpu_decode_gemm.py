@@ -308,19 +308,121 @@ def test_rejects_chunks_that_split_rows(E):
 
 
 def test_llama2_70b_layer_every_row(E):
-    _say("70B-shaped layer 0 with row-aligned chunks, m = 16, every output row")
+    """A whole 70B-shaped layer in chunks of whole rows (at most 65,536
+    symbols: 8 rows of 8,192 columns, 2 of 28,672), every output row against
+    the oracle's weights, for m = 16 (matrix cores) and m = 4 and 1 (the
+    vector-unit product, several chunks per wave)."""
     specs = synth.llama2_70b_layer(0)
     for sp in specs:
         sp["chunk_symbols"] = sp["cols"] * max(1, 65536 // sp["cols"])
     b, p, blob, scales = _setup(E, specs)
     rng = np.random.default_rng(7)
-    xs = [(rng.standard_normal((16, sp["cols"])) * 0.5).astype(np.float32) for sp in specs]
-    xs = [_f32((x.view(np.uint32) >> 16).astype(np.uint16)) for x in xs]  # bf16 values
-    ys = _run(E, p, blob, scales, xs, specs)
+    runs = []
+    for m in (16, 4, 1):
+        _say(f"70B-shaped layer 0 with row-aligned chunks, m = {m}")
+        xs = [(rng.standard_normal((m, sp["cols"])) * 0.5).astype(np.float32) for sp in specs]
+        xs = [_f32((x.view(np.uint32) >> 16).astype(np.uint16)) for x in xs]  # bf16 values
+        runs.append((m, xs, _run(E, p, blob, scales, xs, specs)))
     for t, sp in enumerate(specs):
         W = oracle_rows.tensor_from_oracle(b.blob, b.chunks[b.chunks["tensor"] == t], b.freq[t],
                                            sp)
-        assert oracle_rows.check_product(ys[t], xs[t], W) == sp["rows"], sp["name"]
+        for m, xs, ys in runs:
+            assert oracle_rows.check_product(ys[t], xs[t], W) == sp["rows"], (sp["name"], m)
+
+
+# ---- up to 4 activation rows: the product on the vector units ----
+
+def _few_row_specs():
+    """More chunks (1,350) than the GPU holds workgroups, so waves take
+    several chunks in turn; chunks of 1, 2 and 8 rows (the last one 3 rows);
+    int8 and e4m3; 2, 3 and 11 blocks per row."""
+    specs = [synth.random_int8_tensor(1024, 512, 1.7, 710, 512)]
+    e = synth.e4m3_matrix(rows=600, cols=768)[0]
+    e["chunk_symbols"] = 768 * 2
+    specs.append(e)
+    specs.append(synth.random_int8_tensor(203, 2816, 2.6, 711, 2816 * 8))
+    return specs
+
+
+def test_few_rows_one_hot_return_the_oracle_weights_exactly(E):
+    import torch
+    specs = _few_row_specs()
+    b, p, blob, scales = _setup(E, specs)
+    assert p.n_chunks == 1024 + 300 + 26
+    W = _oracle_weights(b, specs)
+    rng = np.random.default_rng(31)
+    for m in (1, 2, 3, 4):
+        _say(f"few rows, one-hot, m={m}")
+        xs, ys, hit = [], [], []
+        for sp in specs:
+            c = rng.choice(sp["cols"], m, replace=False)
+            x = np.zeros((m, sp["cols"]), np.float32)
+            x[np.arange(m), c] = 1.0
+            xs.append(torch.from_numpy(x).to(torch.bfloat16).cuda())
+            # one row more than m: it must stay untouched
+            ys.append(torch.full((m + 1, sp["rows"]), float("nan"), dtype=torch.float32,
+                                 device="cuda"))
+            hit.append(c)
+        status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        E.decode_gemm(p, blob, scales, xs, [y[:m] for y in ys], status)
+        torch.cuda.synchronize()
+        assert (status.cpu().numpy() == 0).all()
+        for t in range(len(specs)):
+            y = ys[t].cpu().numpy()
+            want = _f32(W[t][:, hit[t]]).T
+            assert np.array_equal(y[:m].view(np.uint32), want.view(np.uint32)), (t, m)
+            assert np.isnan(y[m]).all(), (t, m)
+
+
+def test_few_rows_random_within_the_accumulation_bound(E):
+    specs = _few_row_specs()
+    b, p, blob, scales = _setup(E, specs)
+    W = _oracle_weights(b, specs)
+    rng = np.random.default_rng(32)
+    for m, pad_x, pad_y in ((1, 0, 0), (2, 4, 1), (3, 12, 0), (4, 0, 5)):
+        _say(f"few rows, random, m={m}, padded strides {pad_x}/{pad_y}")
+        xs = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+                   & np.uint16(0xBFFF)) for sp in specs]  # finite bf16 values, |x| < 4
+        ys = _run(E, p, blob, scales, xs, specs, pad_x, pad_y)
+        for t, sp in enumerate(specs):
+            assert oracle_rows.check_product(ys[t][:, :sp["rows"]], xs[t], W[t]) == sp["rows"]
+            if pad_y:
+                assert np.isnan(ys[t][:, sp["rows"]:]).all()
+
+
+def test_few_rows_report_the_decodes_chunk_status(E):
+    """Corrupt chunks: the product reports, chunk by chunk, the status the
+    decode reports for the same bytes (m = 1 and 3; the vector-unit kernel
+    shares the decode's word ring and end check)."""
+    import torch
+    specs = _few_row_specs()
+    b = E.encode_batch(specs)
+    rng = np.random.default_rng(33)
+    blob_h = b.blob.copy()
+    bad = rng.choice(b.chunks.size, 40, replace=False)
+    for c in bad:  # flip bytes inside the chunk's word stream
+        ch = b.chunks[c]
+        lo = int(ch["byte_offset"]) + 256
+        hi = lo + 2 * int(ch["n_words"])
+        pos = rng.integers(lo, hi, 3)
+        blob_h[pos] ^= np.uint8(0x5A)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(blob_h).cuda()
+    scales = torch.from_numpy(np.concatenate([sp["scales"] for sp in specs])).cuda()
+    out = torch.empty(p.out_elems, dtype=torch.int16, device="cuda")
+    want = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, blob, out, E.OUT_BF16, scales, want)
+    torch.cuda.synchronize()
+    want = want.cpu().numpy()
+    assert (want != 0).sum() >= 20 and (want[np.setdiff1d(np.arange(p.n_chunks), bad)] == 0).all()
+    for m in (1, 3):
+        _say(f"few rows, corrupt chunks, m={m}")
+        xs = [torch.ones(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+        ys = [torch.empty(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+        got = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        E.decode_gemm(p, blob, scales, xs, ys, got)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), want), m
 
 
 def _bf16_setup(E, rows, cols, C):
@@ -353,9 +455,9 @@ def _run_split(E, p, blob, sm, x, rows):
 
 
 @pytest.mark.parametrize("rows,blocks,chunk_rows,ms", [
-    (72, 3, 4, (1, 16, 33)),   # 3 blocks per row; 18 chunks: a partial second workgroup
-    (40, 5, 3, (16,)),         # 5 and 7 blocks per row: the sign+mantissa prefetch's
-    (35, 7, 2, (7, 64)),       # unrolled loop plus a remainder; the last chunk short
+    (72, 3, 4, (1, 2, 16, 33)),  # 3 blocks per row; 18 chunks: a partial second workgroup
+    (40, 5, 3, (3, 16)),         # 5 and 7 blocks per row: the sign+mantissa prefetch's
+    (35, 7, 2, (4, 7, 64)),      # unrolled loop plus a remainder; the last chunk short
 ])
 def test_bf16_split_one_hot_returns_the_source_weights(E, rows, blocks, chunk_rows, ms):
     cols = 256 * blocks
@@ -413,14 +515,15 @@ def test_bf16_split_over_more_tensors_than_one_launch_takes(E):
 
 
 def test_bf16_split_8192x8192_within_the_accumulation_bound(E):
-    _say("bf16 split 8192x8192, 8-row chunks, m = 16, every row")
     rows = cols = 8192
     p, blob, sm, w = _bf16_setup(E, rows, cols, 65536)
     rng = np.random.default_rng(12)
-    x = (rng.standard_normal((16, cols)) * 0.5).astype(np.float32)
-    x = _f32((x.view(np.uint32) >> 16).astype(np.uint16))
-    y = _run_split(E, p, blob, sm, x, rows)
-    assert oracle_rows.check_product(y, x, w) == rows  # every row
+    for m in (16, 1):  # matrix cores; the vector-unit product (two chunks per wave)
+        _say(f"bf16 split 8192x8192, 8-row chunks, m = {m}, every row")
+        x = (rng.standard_normal((m, cols)) * 0.5).astype(np.float32)
+        x = _f32((x.view(np.uint32) >> 16).astype(np.uint16))
+        y = _run_split(E, p, blob, sm, x, rows)
+        assert oracle_rows.check_product(y, x, w) == rows  # every row
 
 
 def test_bf16_split_rejects_code_tensors(E):
