@@ -757,7 +757,9 @@ def bench_fused(args):
     Y = X . W^T (q,k,v,gate,up from X [m, 8192], o from an [m, 8192] and down
     from an [m, 28672] activation, synthetic bf16) for m activation rows.
     Fused: one entq_decode_gemm launch per layer (fp32 Y, the bf16 weights
-    never written) on a container of one-row chunks (--row-chunk-max).
+    never written; matrix cores for m > 4, the vector units inside the
+    decode loop for m <= 4) on a container of one-row chunks
+    (--row-chunk-max).
     Unfused: entq_decode into a bf16 layer buffer, then seven torch.mm (bf16
     Y), on the container the decode runs fastest on (whole rows in chunks of
     at most 65,536 symbols, as the layer-decode line's). HIP events around
@@ -781,7 +783,7 @@ def bench_fused(args):
     stream = torch.cuda.current_stream()
     gen = torch.Generator().manual_seed(0)
     results = []
-    for m in [int(v) for v in (args.tokens or "16,4,1,32,64").split(",") if v]:
+    for m in [int(v) for v in (args.tokens or "16,4,2,1,32,64").split(",") if v]:
         X = (torch.randn(m, 8192, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         H = (torch.randn(m, 28672, generator=gen) * 0.5).to(torch.bfloat16).to(dev)
         xs = [H if n == "down" else X for n, r, c, o in views]
@@ -834,6 +836,7 @@ def bench_fused(args):
         results.append(row)
         del X, H, xs, ys, yb
     split = fused_bf16_split_case(E, synth, torch, dev, stream, args)
+    split_m1 = fused_bf16_split_case(E, synth, torch, dev, stream, args, m=1)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = fused_cpu_baseline(E, layers[0], meta0, views, stream, torch, dev)
@@ -870,6 +873,7 @@ def bench_fused(args):
                                                                  for l in dec_layers])),
             "results": results,
             "bf16_split_8192x8192": split,
+            "bf16_split_8192x8192_m1": split_m1,
         },
         "roofline": {
             "bound": "hbm",
@@ -890,8 +894,8 @@ LMHEAD_METRIC = "decoded params/s for the LLaMA-2-70B output projection (32,000 
 def fused_bf16_split_case(E, synth, torch, dev, stream, args, m=16, chunk_rows=None):
     """BF16 weights 8192 x 8192 stored as a coded exponent stream + raw
     sign+mantissa bytes (chunk_rows-row chunks: a tensor on its own needs
-    enough chunks to fill the GPU, 16 per fused workgroup), m = 16
-    activation rows: fused
+    enough chunks to fill the GPU, 16 per fused workgroup), m activation
+    rows: fused
     (entq_decode_gemm_bf16_split) against entq_decode_bf16_split + torch.mm,
     and the split decode alone; medians of per-launch HIP events."""
     rows = cols = 8192
