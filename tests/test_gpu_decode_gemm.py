@@ -166,7 +166,7 @@ def test_more_tensors_than_one_launch_takes(E):
         specs.append(sp)
     b, p, blob, scales = _setup(E, specs)
     W = _oracle_weights(b, specs)
-    for m in (5, 33):
+    for m in (2, 5, 33):  # (more than 16 tensors: the matrix cores also for m <= 4)
         _say(f"19 tensors, one-hot, m={m}")
         xs, cols_hit = [], []
         for sp in specs:
@@ -494,7 +494,13 @@ def test_bf16_split_over_more_tensors_than_one_launch_takes(E):
     p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
     blob = torch.from_numpy(b.blob).cuda()
     sm_all = torch.from_numpy(np.concatenate(sms)).cuda()
-    m = 9
+    for m in (9, 3):  # (more than 16 tensors: the matrix cores also for m <= 4)
+        _split_one_hot_many(E, p, blob, sm_all, specs, ws, rng, m)
+    p.close()
+
+
+def _split_one_hot_many(E, p, blob, sm_all, specs, ws, rng, m):
+    import torch
     xs, ys, hit = [], [], []
     for sp in specs:
         c = rng.choice(sp["cols"], m, replace=False)
@@ -504,14 +510,13 @@ def test_bf16_split_over_more_tensors_than_one_launch_takes(E):
         ys.append(torch.full((m, sp["rows"]), float("nan"), dtype=torch.float32, device="cuda"))
         hit.append(c)
     status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
-    _say("bf16 split, 18 tensors, one-hot, m=9")
+    _say(f"bf16 split, 18 tensors, one-hot, m={m}")
     E.decode_gemm_bf16_split(p, blob, sm_all, xs, ys, status)
     torch.cuda.synchronize()
     assert (status.cpu().numpy() == 0).all()
     for t in range(len(specs)):
         want = _f32(ws[t][:, hit[t]]).T
-        assert np.array_equal(ys[t].cpu().numpy().view(np.uint32), want.view(np.uint32)), t
-    p.close()
+        assert np.array_equal(ys[t].cpu().numpy().view(np.uint32), want.view(np.uint32)), (t, m)
 
 
 def test_bf16_split_8192x8192_within_the_accumulation_bound(E):

@@ -75,11 +75,11 @@ def test_decode_graph_replays(E):
     p.close()
 
 
-def test_static_fused_product_graph_replays(E):
+@pytest.mark.parametrize("m", [16, 1])  # matrix cores; the vector-unit product
+def test_static_fused_product_graph_replays(E, m):
     import torch
     specs = _specs(fused_only=True)
     b, p, blob, scales = _setup(E, specs)
-    m = 16
     rng = np.random.default_rng(3)
 
     def fill_activations(xs):
@@ -93,7 +93,7 @@ def test_static_fused_product_graph_replays(E):
     ye = [torch.empty_like(y) for y in ys]
     status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
     fill_activations(xs)
-    _say("eager static fused product")
+    _say(f"eager static fused product, m={m}")
     E.decode_gemm_static(p, blob, scales, xs, ye, status)  # also looks the scratch up once
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
