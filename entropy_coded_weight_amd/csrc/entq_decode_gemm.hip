@@ -63,14 +63,6 @@ struct GemmArgs {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// Split mode: blocks of sign+mantissa bytes in flight per wave.
-constexpr uint32_t kSmAhead = 4;
-
-// Sign+mantissa bytes that lane k merges into its 4 columns of a block.
-__device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t lane) {
-    return *reinterpret_cast<const uint32_t *>(sm_block + 4u * lane);
-}
-
 // MT: groups of 16 activation rows. SPLIT: the weights are BF16 rebuilt from
 // a coded exponent stream and raw sign+mantissa bytes (no scales). PACKED:
 // x is the packed copy written by pack_activations (below), so each wave's

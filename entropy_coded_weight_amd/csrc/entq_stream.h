@@ -1,8 +1,10 @@
 // entq_stream.h -- device pieces of the streaming rANS decoder shared by the
-// decode kernels and the fused decode-GEMM kernel: the per-wave word ring in
-// LDS fed by direct global->LDS loads, the decode step, and the fp32 scale /
-// bf16 rounding of decoded Int8 or Float8 codes. Included by .hip sources
-// only (one private copy per translation unit).
+// decode kernels and the two fused decode + product kernels: the per-wave
+// word ring in LDS fed by direct global->LDS loads, the decode step, the
+// fp32 scale / bf16 rounding of decoded Int8 or Float8 codes, the BF16
+// merge, and the per-wave staging and priority of the kernels that give each
+// wave its own run of chunks. Included by .hip sources only (one private
+// copy per translation unit).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -246,6 +248,52 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t d, float scale) {
 __device__ __forceinline__ uint32_t merge2(uint32_t q) {
     return ((q >> 1) & 0x7F807F80u) | ((q << 8) & 0x80008000u) | (q & 0x007F007Fu);
 }
+
+// ---------------------------------------------------------------------------
+// pieces of the kernels that give each wave its own run of chunks
+// ---------------------------------------------------------------------------
+
+// Per-wave staging: a decoded step stores, per lane, the high half of its
+// slot-table entry (symbol << 8), so the symbol is byte 1 of a 16-bit slot.
+struct alignas(16) WaveStage {
+    uint16_t stage[kBlockSyms];
+};
+
+// Split mode: blocks of sign+mantissa bytes in flight per wave.
+constexpr uint32_t kSmAhead = 4;
+
+// Sign+mantissa bytes that lane k merges into its 4 outputs (columns) of a
+// block.
+__device__ __forceinline__ uint32_t load_sm4(const uint8_t *sm_block, uint32_t lane) {
+    return *reinterpret_cast<const uint32_t *>(sm_block + 4u * lane);
+}
+
+// Progress-based wave priority: a wave drops one level once it has done
+// half of its blocks, again at three quarters and at seven eighths (half of
+// what is left each time), so waves that are behind win issue arbitration
+// near the end. (The default favours the oldest waves: the younger
+// workgroup on a CU, and the younger waves of a workgroup, then finish long
+// after the rest, with the CU half idle. Drops every quarter of the blocks,
+// or from the first eighth on, left a longer tail.)
+struct Prio {
+    uint32_t my_blocks, done, at, level;
+    __device__ __forceinline__ void start(uint32_t blocks) {
+        my_blocks = blocks;
+        done = 0;
+        at = blocks / 2 ? blocks / 2 : 1;
+        level = 3;
+        __builtin_amdgcn_s_setprio(3);
+    }
+    __device__ __forceinline__ void tick() {
+        if (__builtin_expect(++done == at, 0)) {
+            at += (my_blocks - at) / 2 ? (my_blocks - at) / 2 : 1;
+            --level;
+            if (level == 2) __builtin_amdgcn_s_setprio(2);
+            else if (level == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
+    }
+};
 
 }  // namespace
 }  // namespace entq
