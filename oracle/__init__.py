@@ -345,6 +345,52 @@ def decode_container_bf16(c: Container, scales: np.ndarray):
 ADAPTIVE_TABLE_BYTES = 2 * 256
 
 
+# ---- tile-ordered chunks (the library's layout for the fused product) ----
+#
+# The pages cut a tensor's coded stream into independently decodable
+# segments [EntroLLM, "Metodología", item 3] and leave the order of the
+# symbols inside them open; the discussion under the DFloat11 write-up asks
+# for tiles decompressed inside the matrix multiply. In this layout a tensor
+# [rows x cols] (rows a multiple of 16, cols a multiple of C, C a multiple of
+# 16) is cut into chunks of 16 rows x C columns: band b = rows 16b .. 16b+15,
+# column chunk c = columns cC .. cC+C-1, chunk index b * (cols / C) + c.
+# Inside a chunk, stream position p = 256 t + 64 s + l (t: 16-column tile,
+# s: 0..3, l: 0..63) holds the weight at row 16 b + (l mod 16) and column
+# c C + 16 t + 4 (l div 16) + s. The chunks follow one another in index order.
+# Only the order of the symbols changes: counts, tables and the coder do not.
+
+def tile_order(codes: np.ndarray, rows: int, cols: int, C: int) -> np.ndarray:
+    """The tensor's symbols (row-major, rows x cols) in tile order."""
+    assert rows % 16 == 0 and C % 16 == 0 and C > 0 and cols % C == 0
+    w = np.ascontiguousarray(codes).reshape(rows, cols)
+    out = np.empty(rows * cols, w.dtype)
+    p = np.arange(16 * C)
+    t, s, l = p // 256, (p // 64) % 4, p % 64
+    r_in, c_in = l % 16, 16 * t + 4 * (l // 16) + s   # within the chunk
+    k = 0
+    for b in range(rows // 16):
+        for c in range(cols // C):
+            out[k * 16 * C:(k + 1) * 16 * C] = w[16 * b + r_in, c * C + c_in]
+            k += 1
+    return out
+
+
+def untile(stream: np.ndarray, rows: int, cols: int, C: int) -> np.ndarray:
+    """Inverse of tile_order: the row-major [rows, cols] tensor."""
+    assert rows % 16 == 0 and C % 16 == 0 and C > 0 and cols % C == 0
+    stream = np.ascontiguousarray(stream).ravel()
+    w = np.empty((rows, cols), stream.dtype)
+    p = np.arange(16 * C)
+    t, s, l = p // 256, (p // 64) % 4, p % 64
+    r_in, c_in = l % 16, 16 * t + 4 * (l // 16) + s
+    k = 0
+    for b in range(rows // 16):
+        for c in range(cols // C):
+            w[16 * b + r_in, c * C + c_in] = stream[k * 16 * C:(k + 1) * 16 * C]
+            k += 1
+    return w
+
+
 def adaptive_region_bytes(n_words: int) -> int:
     return (ADAPTIVE_TABLE_BYTES + 4 * CONTAINER_LANES + 2 * n_words + 15) // 16 * 16
 
