@@ -117,6 +117,9 @@ def lib():
             "entq_pack_device_adaptive_batch": (c.c_int, [vp, c.c_int, vp, vp]),
             "entq_build_freq_device": (c.c_int, [vp, c.c_uint32, u64, vp, vp]),
             "entq_decode_gemm_static": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
+            "entq_tile_order": (c.c_int, [vp, c.c_uint32, c.c_uint32, c.c_uint32, vp, c.c_int]),
+            "entq_decode_gemm_tiles_workspace_bytes": (u64, [vp, c.c_int]),
+            "entq_decode_gemm_tiles": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -138,7 +141,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_build_freq_chunks", "entq_encode_device_adaptive_batch",
             "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
             "entq_build_freq_device", "entq_decode_gemm_workspace_bytes",
-            "entq_decode_gemm_static"]
+            "entq_decode_gemm_static", "entq_tile_order", "entq_decode_gemm_tiles_workspace_bytes",
+            "entq_decode_gemm_tiles"]
 
 
 def _str(status: int) -> str:
@@ -416,6 +420,51 @@ def decode_gemm_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=N
                                            _ptr(ws) if ws is not None else None, int(wsb),
                                            _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm_bf16_split")
+
+
+def tile_order(codes: np.ndarray, rows: int, cols: int, chunk_cols: int,
+               n_threads: int | None = None) -> np.ndarray:
+    """The symbols of a row-major [rows, cols] tensor in tile order for chunks
+    of 16 rows x chunk_cols columns (entq_tile_order); encode them with
+    chunk_symbols = 16 * chunk_cols for decode_gemm_tiles."""
+    codes = np.ascontiguousarray(codes).view(np.uint8).ravel()
+    if codes.size != rows * cols:
+        raise EntqError(EINVAL, f"{codes.size} codes for a {rows} x {cols} tensor")
+    out = np.empty(codes.size, np.uint8)
+    _check(lib().entq_tile_order(_ptr(codes) if codes.size else None, rows, cols, chunk_cols,
+                                 _ptr(out) if out.size else None, n_threads or default_threads()),
+           "entq_tile_order")
+    return out
+
+
+def decode_gemm_tiles(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None,
+                      workspace=None):
+    """decode_gemm for a plan of tile-ordered tensors (entq_decode_gemm_tiles):
+    xs, ys as for decode_gemm (m <= 64). workspace: a device uint8 tensor
+    (256-byte aligned, entq_decode_gemm_tiles_workspace_bytes long) for the
+    column chunks' partial sums, or None to allocate one when needed."""
+    import torch
+    io, m = _gemm_io(p, xs, ys)
+    _blob_buffer(p, "compressed", compressed)
+    _device_buffer(p, "scales", scales, p.scale_rows, dtypes=(torch.float32,))
+    _status_buffer(p, chunk_status)
+    need = int(lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, int(m))) if p.handle.value \
+        else 0
+    if workspace is None:
+        if need:
+            raw = torch.empty(need + 256, dtype=torch.uint8, device=p.workspace.device)
+            shift = (-raw.data_ptr()) % 256
+            workspace = raw[shift:shift + need]
+            if stream is not None:
+                workspace.record_stream(stream)  # allocated here, used on another stream
+    else:
+        _device_buffer(p, "workspace", workspace, need, elem_size=1)
+    wsb = workspace.numel() if workspace is not None else 0
+    st = lib().entq_decode_gemm_tiles(p.handle, _ptr(compressed), _ptr(scales) or None,
+                                      _ptr(io) if len(xs) else None, int(m),
+                                      _ptr(workspace) if workspace is not None else None,
+                                      int(wsb), _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_gemm_tiles")
 
 
 def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):

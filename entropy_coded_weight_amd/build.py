@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libentq.so")
 
 SOURCES = ["entq_decode.hip", "entq_decode_gemv.hip", "entq_decode_gemm.hip",
-           "entq_decode_adaptive.hip", "entq_plan.cpp", "entq_encode.cpp", "entq_encode_dev.hip"]
+           "entq_decode_tiles.hip", "entq_decode_adaptive.hip", "entq_plan.cpp", "entq_encode.cpp", "entq_encode_dev.hip"]
 
 
 def hipcc() -> str:

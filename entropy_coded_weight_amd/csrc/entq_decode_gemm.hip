@@ -313,6 +313,37 @@ uint64_t packed_bytes(uint32_t cols, int groups_m) {
     return ((uint64_t)16 * groups_m * cols * 2 + 255) & ~(uint64_t)255;
 }
 
+int launch_pack_activations(const entq_plan_t *plan, const entq_gemm_io *io, int m,
+                            const uint64_t *offsets, uint8_t *workspace, void *stream) {
+    const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
+    PackArgs pack = {};
+    pack.m = (uint32_t)m;
+    pack.groups = (uint32_t)groups_m;
+    uint64_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (pack.n_tensors)
+            hipLaunchKernelGGL(pack_activations, dim3((unsigned)blocks), dim3(256), 0,
+                               (hipStream_t)stream, pack);
+        pack.n_tensors = 0;
+        blocks = 0;
+        return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+    };
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
+        if (h.n_symbols == 0) continue;
+        const uint64_t pb = ((uint64_t)16 * groups_m * (h.cols / 4) + 255) / 256;
+        if (pack.n_tensors == (uint32_t)kGemmMaxTensors || blocks + pb > 0x7FFFFFFFull) {
+            const int r = flush();
+            if (r != ENTQ_OK) return r;
+        }
+        pack.t[pack.n_tensors++] = {static_cast<const uint16_t *>(io[t].d_x),
+                                    reinterpret_cast<uint16_t *>(workspace + offsets[t]),
+                                    io[t].ldx, h.cols, (uint32_t)blocks};
+        blocks += pb;
+    }
+    return flush();
+}
+
 uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m) {
     const int groups_m = (m + (int)kGemmM - 1) / (int)kGemmM;
     uint64_t total = 0;

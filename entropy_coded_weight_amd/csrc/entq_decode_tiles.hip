@@ -1,0 +1,405 @@
+// entq_decode_tiles.hip -- gfx950 kernels of the fused decode + product on
+// tile-ordered chunks: every wave decodes its own chunks and feeds the
+// matrix cores straight from its registers.
+//
+// The discussion under the DFloat11 write-up asks for a matrix multiply
+// that decompresses each tile as it goes, and EntQuant expects fused kernels
+// to make entropy-coded weights cheaper at inference [EntQuant,
+// "Float8@2bits: Entropy Coding Enables Data-Free Model Compression",
+// technical summary §5]. The pages leave the order of the symbols inside a
+// coded segment open; this file reads chunks whose symbols are in tile
+// order (entq_tile_order): a chunk covers 16 weight rows (a band) and C
+// columns, and its stream position 256 t + 64 s + l holds the weight at row
+// l mod 16 of the band and column 16 t + 4 (l div 16) + s of the chunk.
+//
+// Mapping onto CDNA4. Lane l decodes stream position 64 s + l at step s of
+// a 4-step block, so after the block it holds, in registers, the 4 weights
+// of row l mod 16 at columns 16 t + 4 (l div 16) .. +3: exactly its part of
+// the B operand of v_mfma_f32_16x16x16_bf16 for that 16 x 16 tile (B[k][n]
+// = W[row n][column k]). The lane dequantises them with its row's scale,
+// loads the matching activation columns (A = 16 activation rows x 16
+// columns) and issues one MFMA per 16 activation rows. No LDS stage, no
+// workgroup barrier, no lockstep: every wave walks its own run of chunks as
+// in the bf16 decode (word ring, slot table and progress priority
+// unchanged). At a chunk's end the wave holds Y for its 16 weight rows over
+// the chunk's C columns: it writes them straight to Y when the chunk spans
+// all columns, else to a partial-sum slot of the workspace, and a second
+// kernel adds the column chunks' partial sums in column order.
+#include <hip/hip_runtime.h>
+
+#include "entq.h"
+#include "entq_internal.h"
+#include "entq_stream.h"
+
+namespace entq {
+namespace {
+
+constexpr int kTileMaxTensors = 16;   // tensors of a plan
+constexpr uint32_t kTileM = 16;       // activation rows of one MFMA
+constexpr int kTileMaxGroups = 4;     // up to 64 activation rows
+
+struct TileTensor {
+    const uint16_t *x;  // bf16 activations: m rows, row stride ldx elements,
+                        // or their packed copy (PACKED)
+    float *y;           // fp32 results: m rows, row stride ldy
+    float *part;        // partial sums [n_cc][m][rows], when n_cc > 1
+    uint64_t ldx, ldy;
+    uint64_t out0;      // the tensor's first stream element (out_elem_offset)
+    uint64_t row0;      // its first scale row
+    uint32_t rows, chunk_cols, n_cc;
+};
+struct TileArgs {
+    TileTensor t[kTileMaxTensors];
+    uint32_t m;
+};
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// One decode step without staging: the lane's slot-table entry (f | sym <<
+// 24) is returned, the state updated and renormalised as in stream_step.
+__device__ __forceinline__ uint32_t tile_step(uint32_t &x, uint32_t &pos, const uint2 *T,
+                                              uint32_t lane) {
+    const uint2 e = T[x & (kProbScale - 1)];
+    x = __umul24(e.x, x >> kProbBits) + e.y;
+    const bool need = x < kStateLow;
+    const uint64_t mask = __ballot(need);
+    const uint32_t w = *reinterpret_cast<lds_u16 *>((pos + lane_prefix(mask)) << 1);
+    x = __builtin_amdgcn_perm(x, w, need ? 0x05040100u : 0x07060504u);
+    pos += (uint32_t)__popcll(mask);
+    return e.x;
+}
+
+// bf16 of two codes (bytes 1 and 3 of d) times a per-lane scale; otherwise
+// as dequant2 (the code is the product's first operand, NaN codes patched).
+template <bool E4M3>
+__device__ __forceinline__ uint32_t dequant2_lane(uint32_t d, float scale) {
+    float v0, v1;
+    if (E4M3) {
+        v0 = __builtin_amdgcn_cvt_f32_fp8((int)d, 1);
+        v1 = __builtin_amdgcn_cvt_f32_fp8((int)d, 3);
+    } else {
+        v0 = (float)((int32_t)(d << 16) >> 24);
+        v1 = (float)((int32_t)d >> 24);
+    }
+    const uint32_t r = bf16x2_bits(mul_value_scale(v0, scale), mul_value_scale(v1, scale));
+    return E4M3 ? e4m3_nan_patch2(d, r) : r;
+}
+
+// PACKED: x is the packed copy of the activations (launch_pack_activations):
+// the A fragments of one 16-column slice and group are 512 contiguous bytes,
+// where the activations' own layout gives 16 rows of 32 bytes (partial cache
+// lines, which cost more than the pre-pass copy once more than a few rows
+// are read).
+template <int MT, bool E4M3, bool PRIO, bool PACKED>
+__device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__restrict__ blob,
+                                           const uint2 *T, uint16_t *ring_lds, uint32_t lane,
+                                           const float *__restrict__ scales, const TileTensor &gt,
+                                           uint32_t m, Prio &pr, int32_t *__restrict__ status) {
+    const uint8_t *region = blob + ch.byte_offset;
+    uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
+    Stream s;
+    ring_open(s, region + kStateBytes, lds_addr(ring_lds), ch.n_words, lane);
+    // which band and column chunk: chunks are whole 16 x C pieces in order
+    const uint32_t C = gt.chunk_cols;
+    const uint64_t k = (ch.out_elem - gt.out0) / (16ull * C);
+    const uint32_t band = (uint32_t)(k / gt.n_cc), cc = (uint32_t)(k % gt.n_cc);
+    const uint32_t r16 = lane & 15;                  // weight row in the band; activation row
+    const float scale = scales[gt.row0 + 16ull * band + r16];
+    // activations: a uniform base and 32-bit byte offsets (the host keeps
+    // ldx <= 2^24, so 64 rows span less than 2 GiB), so the loads need no
+    // 64-bit address registers per group
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(gt.x);
+    const uint32_t xoff =
+        PACKED ? 2u * ((cc * C / 16u) * MT * 256u + 4u * lane)
+               : 2u * (r16 * (uint32_t)gt.ldx + cc * C + 4u * (lane >> 4));
+    const uint32_t group_bytes = PACKED ? 512u : 32u * (uint32_t)gt.ldx;
+    const uint32_t tile_bytes = PACKED ? 512u * MT : 32u;  // per 16-column slice
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states, scale, first ring units
+    s.landed = s.issued;
+    ring_horizon(s);
+
+    float4_t acc[MT];
+#pragma unroll
+    for (int g = 0; g < MT; ++g) acc[g] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t blocks = ch.n_symbols / kBlockSyms;  // C / 16 tiles
+    for (uint32_t t = 0; t < blocks; ++t) {
+        if (PRIO) pr.tick();
+        if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
+        // this tile's activation columns (in flight while it decodes; at
+        // least one load follows every ring refill, as ring_service's wait
+        // for all but the latest operation requires)
+        uint2 a[MT];
+#pragma unroll
+        for (int g = 0; g < MT; ++g) {
+            const uint2 *src =
+                reinterpret_cast<const uint2 *>(xb + (xoff + g * group_bytes + tile_bytes * t));
+            if (PACKED)  // rows m and beyond are zeros in the packed copy
+                a[g] = *src;
+            else
+                a[g] = (16u * g + r16 < m) ? *src : make_uint2(0, 0);
+        }
+        const uint32_t e0 = tile_step(x, s.pos, T, lane);
+        const uint32_t e1 = tile_step(x, s.pos, T, lane);
+        const uint32_t e2 = tile_step(x, s.pos, T, lane);
+        const uint32_t e3 = tile_step(x, s.pos, T, lane);
+        // codes of columns +0, +1 in bytes 1 and 3, then of +2, +3
+        const uint32_t d0 = __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
+        const uint32_t d1 = __builtin_amdgcn_perm(e3, e2, 0x070C030Cu);
+        const uint2 w = make_uint2(dequant2_lane<E4M3>(d0, scale), dequant2_lane<E4M3>(d1, scale));
+#pragma unroll
+        for (int g = 0; g < MT; ++g)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(short4_t, a[g]), __builtin_bit_cast(short4_t, w), acc[g], 0, 0,
+                0);
+    }
+    // lane l holds Y[16 g + 4 (l div 16) + i][band row l mod 16], i = 0..3
+    const uint32_t wrow = 16u * band + r16;
+    float *dst;
+    uint64_t ld;
+    if (gt.n_cc > 1) {
+        dst = gt.part + (uint64_t)cc * m * gt.rows;
+        ld = gt.rows;
+    } else {
+        dst = gt.y;
+        ld = gt.ldy;
+    }
+#pragma unroll
+    for (int g = 0; g < MT; ++g)
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            const uint32_t mrow = 16u * g + 4u * (lane >> 4) + i;
+            if (mrow < m) dst[(uint64_t)mrow * ld + wrow] = acc[g][i];
+        }
+    const uint64_t bad_state = __ballot(x != kStateLow);
+    if (status && lane == 0)
+        status[ch.status_index] = (ring_consumed(s) != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+                                  : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
+    wait_vm<0>();  // no global->LDS load may outlive the chunk
+}
+
+// amdgpu_waves_per_eu(8): at most 64 vector registers per lane, so that two
+// 16-wave workgroups share a CU also with four 16-row groups of activations
+// (the compiler would otherwise take 78 there and halve the waves).
+template <int MT, bool PRIO, bool PACKED>
+__global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS
+__attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
+    const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
+    const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks,
+    const uint8_t *__restrict__ blob, const float *__restrict__ scales,
+    int32_t *__restrict__ status, TileArgs args) {
+    __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
+    __shared__ uint2 T[kProbScale];
+
+    const DevTask task = tasks[blockIdx.x];
+    const bool e4m3 = tensors[task.tensor].kind == ENTQ_SYM_E4M3;
+    const TileTensor &gt = args.t[task.tensor];
+    load_table(T, tables, task.tensor);
+    __syncthreads();
+
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    // the task's chunks in rounds of equal width, as in the bf16 decode
+    const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
+    const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    Prio pr = {};
+    if (PRIO) {
+        uint32_t my_blocks = 0;
+        for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
+            my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
+        pr.start(my_blocks);
+    }
+    for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
+        const DevChunk ch = chunks[task.first_chunk + c];
+        if (e4m3)
+            tile_chunk<MT, true, PRIO, PACKED>(ch, blob, T, RING[wave], lane, scales, gt, args.m,
+                                               pr, status);
+        else
+            tile_chunk<MT, false, PRIO, PACKED>(ch, blob, T, RING[wave], lane, scales, gt, args.m,
+                                                pr, status);
+    }
+}
+
+// Y of the tensors whose chunks split the columns: the column chunks'
+// partial sums added in column order, one thread per result.
+struct ReduceTensor {
+    const float *part;
+    float *y;
+    uint64_t ldy;
+    uint32_t rows, n_cc, first_block;
+};
+struct ReduceArgs {
+    ReduceTensor t[kTileMaxTensors];
+    uint32_t n_tensors, m;
+};
+
+__global__ __launch_bounds__(256) void reduce_partials(ReduceArgs args) {
+    uint32_t ti = 0;
+    while (ti + 1 < args.n_tensors && args.t[ti + 1].first_block <= blockIdx.x) ++ti;
+    const ReduceTensor &rt = args.t[ti];
+    const uint64_t i = (uint64_t)(blockIdx.x - rt.first_block) * 256 + threadIdx.x;
+    const uint64_t per_cc = (uint64_t)args.m * rt.rows;
+    if (i >= per_cc) return;
+    float sum = 0.f;
+    for (uint32_t c = 0; c < rt.n_cc; ++c) sum += rt.part[c * per_cc + i];
+    const uint64_t mrow = i / rt.rows, r = i % rt.rows;
+    rt.y[mrow * rt.ldy + r] = sum;
+}
+
+template <int MT, bool PACKED>
+void launch_tiles_mt(bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
+                     const uint8_t *blob, const float *scales, int32_t *status,
+                     const TileArgs &args) {
+    const dim3 block(kThreads);
+    if (prio)
+        hipLaunchKernelGGL((decode_tile_gemm<MT, true, PACKED>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           scales, status, args);
+    else
+        hipLaunchKernelGGL((decode_tile_gemm<MT, false, PACKED>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           scales, status, args);
+}
+
+template <bool PACKED>
+void launch_tiles(int groups, bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
+                  const uint8_t *blob, const float *scales, int32_t *status,
+                  const TileArgs &args) {
+    if (groups == 1)
+        launch_tiles_mt<1, PACKED>(prio, grid, st, plan, blob, scales, status, args);
+    else if (groups == 2)
+        launch_tiles_mt<2, PACKED>(prio, grid, st, plan, blob, scales, status, args);
+    else if (groups == 3)
+        launch_tiles_mt<3, PACKED>(prio, grid, st, plan, blob, scales, status, args);
+    else
+        launch_tiles_mt<4, PACKED>(prio, grid, st, plan, blob, scales, status, args);
+}
+
+// Activations are packed (launch_pack_activations) above this many rows:
+// with one row only the lanes of row 0 load anything at all. (70B-shaped
+// layers, 8,192-column chunks: m = 2, 4 unpacked 358.5, 363.7 us; packed
+// m = 5, 8, 16: 339.2, 338.1, 343.3 us; m = 1 unpacked 356.0 us.)
+constexpr int kTilePackAbove = 1;
+
+uint64_t part_bytes(const HostTensor &h, int m) {
+    const uint32_t C = h.chunk_symbols / 16;
+    const uint32_t ncc = h.cols / C;
+    if (ncc <= 1) return 0;
+    return ((uint64_t)ncc * m * h.rows * 4 + 255) & ~(uint64_t)255;
+}
+
+// Workspace: the packed activations (m > kTilePackAbove), then the partial
+// sums, tensor by tensor in plan order.
+uint64_t tiles_workspace_bytes(const entq_plan_t *plan, int m) {
+    const int groups = (m + (int)kTileM - 1) / (int)kTileM;
+    uint64_t total = 0;
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
+        if (h.n_symbols == 0) continue;
+        if (m > kTilePackAbove) total += packed_bytes(h.cols, groups);
+        total += part_bytes(h, m);
+    }
+    return total;
+}
+
+entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, int m) {
+    if (!plan || plan->adaptive || !io || m < 1 || m > (int)kTileM * kTileMaxGroups ||
+        plan->n_tensors > kTileMaxTensors || plan->n_tasks > 0x7FFFFFFF)
+        return ENTQ_EINVAL;
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
+        if (h.n_symbols == 0) continue;
+        if (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3) return ENTQ_EINVAL;
+        // chunks of 16 whole rows x C columns, C a multiple of 16 dividing cols
+        if (h.rows % 16 || h.chunk_symbols % kBlockSyms) return ENTQ_EINVAL;
+        const uint32_t C = h.chunk_symbols / 16;
+        if (h.cols == 0 || h.cols % C) return ENTQ_EINVAL;
+        const entq_gemm_io &g = io[t];
+        if (!g.d_x || !g.d_y || g.ldx < h.cols || g.ldy < h.rows) return ENTQ_EINVAL;
+        if (g.ldx > (1u << 24)) return ENTQ_EINVAL;  // 64 rows of x within 32-bit offsets
+        if ((uintptr_t)g.d_x % 8 || g.ldx % 4 || (uintptr_t)g.d_y % 4) return ENTQ_EALIGN;
+    }
+    return ENTQ_OK;
+}
+
+}  // namespace
+}  // namespace entq
+
+extern "C" {
+
+uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m) {
+    if (!plan || m < 1 || m > (int)entq::kTileM * entq::kTileMaxGroups) return 0;
+    return entq::tiles_workspace_bytes(plan, m);
+}
+
+entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compressed,
+                                   const float *d_scales, const entq_gemm_io *io, int m,
+                                   void *d_workspace, uint64_t workspace_bytes,
+                                   int32_t *d_chunk_status, void *stream) {
+    using namespace entq;
+    entq_status st = check_tiles_args(plan, io, m);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    const uint64_t need = tiles_workspace_bytes(plan, m);
+    if (need && !d_workspace) return ENTQ_EWORKSPACE;
+    if (d_workspace && (uintptr_t)d_workspace % 256) return ENTQ_EALIGN;
+    if (workspace_bytes < need) return ENTQ_EWORKSPACE;
+    if (plan->n_tasks == 0) return ENTQ_OK;
+
+    TileArgs args = {};
+    args.m = (uint32_t)m;
+    ReduceArgs red = {};
+    red.m = (uint32_t)m;
+    uint64_t off = 0, red_blocks = 0;
+    uint8_t *ws = static_cast<uint8_t *>(d_workspace);
+    const int groups = (m + (int)kTileM - 1) / (int)kTileM;
+    const bool packed = m > kTilePackAbove;
+    uint64_t pack_off[kTileMaxTensors] = {};
+    if (packed)
+        for (int t = 0; t < plan->n_tensors; ++t)
+            if (plan->host_tensors[(size_t)t].n_symbols) {
+                pack_off[t] = off;
+                off += packed_bytes(plan->host_tensors[(size_t)t].cols, groups);
+            }
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
+        if (h.n_symbols == 0) continue;
+        TileTensor &g = args.t[t];
+        g.x = packed ? reinterpret_cast<const uint16_t *>(ws + pack_off[t])
+                     : static_cast<const uint16_t *>(io[t].d_x);
+        g.y = io[t].d_y;
+        g.ldx = io[t].ldx;
+        g.ldy = io[t].ldy;
+        g.out0 = h.out_elem_offset;
+        g.row0 = h.scale_row_offset;
+        g.rows = h.rows;
+        g.chunk_cols = h.chunk_symbols / 16;
+        g.n_cc = h.cols / g.chunk_cols;
+        g.part = nullptr;
+        if (g.n_cc > 1) {
+            g.part = reinterpret_cast<float *>(ws + off);
+            off += part_bytes(h, m);
+            ReduceTensor &r = red.t[red.n_tensors++];
+            r = {g.part, g.y, g.ldy, g.rows, g.n_cc, (uint32_t)red_blocks};
+            red_blocks += ((uint64_t)m * h.rows + 255) / 256;
+        }
+    }
+    if (red_blocks > 0x7FFFFFFF) return ENTQ_EINVAL;
+    const hipStream_t s = (hipStream_t)stream;
+    const bool prio = plan->n_chunks > plan->n_tasks;
+    const dim3 grid((unsigned)plan->n_tasks);
+    const uint8_t *b = static_cast<const uint8_t *>(d_compressed);
+    if (packed) {
+        const int r = launch_pack_activations(plan, io, m, pack_off, ws, stream);
+        if (r != ENTQ_OK) return (entq_status)r;
+        launch_tiles<true>(groups, prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    } else {
+        launch_tiles<false>(groups, prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    }
+    if (red.n_tensors)
+        hipLaunchKernelGGL(reduce_partials, dim3((unsigned)red_blocks), dim3(256), 0, s, red);
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+}  // extern "C"

@@ -323,4 +323,31 @@ entq_status entq_bf16_split(const uint16_t *w, uint64_t n, uint8_t *exp_out, uin
     return ENTQ_OK;
 }
 
+// Tile order of one tensor (see include/entq.h): chunk k = (band b, column
+// chunk c), inside it position 256 t + 64 s + l holds row 16 b + l % 16,
+// column c C + 16 t + 4 (l / 16) + s.
+entq_status entq_tile_order(const uint8_t *codes, uint32_t rows, uint32_t cols,
+                            uint32_t chunk_cols, uint8_t *out, int n_threads) {
+    if (rows % 16 || chunk_cols == 0 || chunk_cols % 16 || cols % chunk_cols) return ENTQ_EINVAL;
+    const uint64_t n = (uint64_t)rows * cols;
+    if (n && (!codes || !out)) return ENTQ_EINVAL;
+    const uint32_t ncc = cols / chunk_cols;
+    const uint64_t chunks = (uint64_t)(rows / 16) * ncc;
+    const uint64_t per = 16ull * chunk_cols;
+    int nt = pick_threads(n_threads, n / (1u << 20) + 1);
+    parallel_ranges(nt, chunks, [&](int, uint64_t kb, uint64_t ke) {
+        for (uint64_t k = kb; k < ke; ++k) {
+            const uint64_t b = k / ncc, c = k % ncc;
+            uint8_t *dst = out + k * per;
+            for (uint64_t p = 0; p < per; ++p) {
+                const uint64_t t = p >> 8, sidx = (p >> 6) & 3, l = p & 63;
+                const uint64_t row = 16 * b + (l & 15);
+                const uint64_t col = c * chunk_cols + 16 * t + 4 * (l >> 4) + sidx;
+                dst[p] = codes[row * cols + col];
+            }
+        }
+    });
+    return ENTQ_OK;
+}
+
 }  // extern "C"

@@ -131,6 +131,13 @@ int launch_decode_gemm(const entq_plan_t *plan, const void *blob, const float *s
                        const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
                        uint8_t *workspace, int32_t *status, void *stream);
 uint64_t gemm_workspace_bytes(const entq_plan_t *plan, int m);
+// Bytes of one tensor's packed activations for m rows (16-row groups,
+// 256-byte aligned), and the launch that writes them: tensor t's copy at
+// workspace + offsets[t] (fragment of 16-column slice T, group g, lane l at
+// element (T * groups + g) * 256 + 4 l; zeros for rows m and beyond).
+uint64_t packed_bytes(uint32_t cols, int groups_m);
+int launch_pack_activations(const entq_plan_t *plan, const entq_gemm_io *io, int m,
+                            const uint64_t *offsets, uint8_t *workspace, void *stream);
 // The same product for at most kGemvMaxRows activation rows without matrix
 // cores (entq_decode.hip), for plans of at most kGemvMaxTensors tensors whose
 // chunks hold whole rows of a multiple of kBlockSyms columns; signmant

@@ -336,6 +336,62 @@ entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_e
                                         int m, void *d_workspace, uint64_t workspace_bytes,
                                         int32_t *d_chunk_status, void *stream);
 
+/* ---- Fused product on tile-ordered chunks ----
+ *
+ * The pages cut the coded stream into independently decodable segments
+ * [EntroLLM, "Metodología", item 3] and leave the order of symbols inside a
+ * segment open; the discussion under the DFloat11 write-up asks for tiles
+ * decompressed inside the matrix multiply. In the library's tile order a
+ * tensor [rows x cols] (rows a multiple of 16; C, the columns per chunk, a
+ * multiple of 16 dividing cols) is cut into chunks of 16 rows x C columns:
+ * chunk k = band b = k / (cols / C) (rows 16b .. 16b+15) and column chunk
+ * c = k % (cols / C) (columns cC .. cC+C-1), and position p = 256 t + 64 s
+ * + l (0 <= s < 4, 0 <= l < 64) of the chunk holds the weight at row
+ * 16 b + l % 16, column c C + 16 t + 4 (l / 16) + s. Only the order of the
+ * symbols changes; the table, coder and container are as for any tensor:
+ * encode the reordered symbols with chunk_symbols = 16 C. entq_decode on
+ * such a tensor returns its codes in tile order (ENTQ_OUT_CODES); its bf16
+ * output, whose scale rows assume row-major order, is not meaningful. */
+
+/* The symbols of one row-major tensor (codes, rows x cols bytes) in tile
+ * order with chunk_cols = C columns per chunk, into out (rows x cols bytes,
+ * caller-owned, not overlapping codes). ENTQ_EINVAL if the shape does not
+ * fit the tile order. n_threads <= 0: all hardware threads. */
+entq_status entq_tile_order(const uint8_t *codes, uint32_t rows, uint32_t cols,
+                            uint32_t chunk_cols, uint8_t *out, int n_threads);
+
+/* Bytes of workspace entq_decode_gemm_tiles needs for this plan and m (0 for
+ * invalid arguments, or for m = 1 when every tensor's chunks span all its
+ * columns): for m > 1 the activations packed in the order the waves read
+ * them (as entq_decode_gemm_workspace_bytes counts them), and for each
+ * tensor with cols / C > 1 column chunks 4 bytes x (cols / C) x m x rows of
+ * partial sums, each rounded up to 256. */
+uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m);
+
+/* Y_t = X_t . W_t^T as entq_decode_gemm computes it (io[], m <= 64, fp32
+ * results, W_t the bf16 of code x row scale rounded to nearest even), for a
+ * plan whose non-empty tensors (at most 16; kind INT8 or E4M3) are in tile
+ * order: rows a multiple of 16, chunk_symbols = 16 C with C a multiple of
+ * 16 that divides cols, and ldx at most 2^24 (else ENTQ_EINVAL). Every wave
+ * decodes its own chunks and, for each 16 x 16 tile, issues one
+ * v_mfma_f32_16x16x16_bf16
+ * per 16 activation rows straight from its registers: no workgroup barrier
+ * and no staging of weights. For m > 1 a first enqueued kernel copies the
+ * activations into d_workspace in the order the waves read them (512
+ * contiguous bytes per 16 columns and 16 rows). A chunk's 16 x C product
+ * goes to Y directly when C = cols; otherwise to a partial-sum slot of
+ * d_workspace, and a last enqueued kernel adds a row's column chunks in
+ * column order. d_workspace: required whenever the size query is non-zero
+ * (256-byte aligned, at least that size, else ENTQ_EALIGN /
+ * ENTQ_EWORKSPACE; not used by other work while the call runs). Results are reproducible run to run and stay within
+ * cols * 2^-24 * sum_c |X[i][c] W[r][c]| of the exact product; their
+ * summation order differs from entq_decode_gemm's. d_chunk_status as in
+ * entq_decode. */
+entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compressed,
+                                   const float *d_scales, const entq_gemm_io *io, int m,
+                                   void *d_workspace, uint64_t workspace_bytes,
+                                   int32_t *d_chunk_status, void *stream);
+
 /* ---- On-device encoder (one wavefront per chunk; same regions as the
  * host encoder, byte for byte) ----
  *

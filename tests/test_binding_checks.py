@@ -133,6 +133,21 @@ def test_fused_refuses_mismatched_activations_and_results(E, P):
              match="signmant holds 5")
 
 
+def test_tiled_product_refuses(E, P):
+    blob = torch.zeros(900, dtype=torch.uint8)
+    sc = torch.ones(7, dtype=torch.float32)
+    xs, ys = _xy(3, [(4, 256), (3, 512)])
+    _rejects(E, E.decode_gemm_tiles, P, blob, sc, xs[:1], ys[:1], stream=0,
+             match="for 2 tensors")
+    _rejects(E, E.decode_gemm_tiles, P, blob, sc[:6], xs, ys, stream=0, match="scales holds 6")
+    _rejects(E, E.decode_gemm_tiles, P, blob[:899], sc, xs, ys, stream=0,
+             match="compressed holds")
+    _rejects(E, E.decode_gemm_tiles, P, blob, sc, xs, ys, torch.zeros(4, dtype=torch.int32),
+             stream=0, match="chunk_status holds 4")
+    _rejects(E, E.decode_gemm_tiles, P, blob, sc, xs, ys, stream=0,
+             workspace=torch.zeros(16, dtype=torch.uint8, device="meta"), match="workspace is on")
+
+
 def test_linear_refuses(E, P):
     from entropy_coded_weight_amd.linear import linear
     blob = torch.zeros(900, dtype=torch.uint8)

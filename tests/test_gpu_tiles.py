@@ -1,0 +1,257 @@
+"""GPU parity of the fused product on tile-ordered chunks
+(entq_decode_gemm_tiles, through the C ABI). The container holds each
+tensor's codes in the library's tile order (oracle.tile_order pins it); the
+expected weights are the oracle's: its decode of the container's chunks,
+put back in row-major order by oracle.untile and dequantised by the oracle.
+With one-hot activation rows every output is 1.0 * w, so the kernel must
+return the oracle's bf16 weights bit for bit; with random activations the
+fp32 result may differ from the fp64 product by at most cols * 2^-24 *
+sum |x w| (products of two bf16 are exact in fp32; at most cols additions,
+each rounding once)."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_rows
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-tiles] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def E():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import entropy_coded_weight_amd as E
+    E.lib()
+    return E
+
+
+def _f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _tiled(E, specs, C_of):
+    """specs with their symbols put in tile order (C = C_of(spec) columns
+    per chunk), the container, plan and device buffers."""
+    import torch
+    tiled = []
+    for sp in specs:
+        C = C_of(sp)
+        st = E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C)
+        tiled.append(dict(sp, symbols=st, chunk_symbols=16 * C, C=C))
+    b = E.encode_batch(tiled)
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    scales = torch.from_numpy(np.concatenate([sp["scales"] for sp in specs])).cuda()
+    return tiled, b, p, blob, scales
+
+
+def _oracle_weights(b, tiled):
+    """bf16 bits [rows, cols] of every tensor from the oracle's decode of the
+    container, untiled and dequantised by the oracle."""
+    out = []
+    for t, sp in enumerate(tiled):
+        ch = b.chunks[b.chunks["tensor"] == t]
+        desc = oracle_rows.desc_of(ch)
+        sym, st = oracle.decode_tensor(b.blob, desc, b.freq[t], sp["rows"] * sp["cols"])
+        assert (st == 0).all()
+        codes = oracle.untile(sym, sp["rows"], sp["cols"], sp["C"])
+        w = oracle.dequant_tensor(codes.ravel(), sp["rows"], sp["cols"], sp["kind"],
+                                  sp["scales"])
+        out.append(w.reshape(sp["rows"], sp["cols"]))
+    return out
+
+
+def _run(E, p, blob, scales, xs_host, specs, pad_x=0, pad_y=0, extra_rows=0, workspace=None):
+    import torch
+    xs, ys = [], []
+    for x, sp in zip(xs_host, specs):
+        m, c = x.shape
+        xd = torch.zeros(m, c + pad_x, dtype=torch.bfloat16)
+        xd[:, :c] = torch.from_numpy(x).to(torch.bfloat16)
+        xs.append(xd.cuda())
+        ys.append(torch.full((m + extra_rows, sp["rows"] + pad_y), float("nan"),
+                             dtype=torch.float32, device="cuda"))
+    m = xs_host[0].shape[0]
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode_gemm_tiles(p, blob, scales, xs, [y[:m] for y in ys], status, workspace=workspace)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    return [y.cpu().numpy() for y in ys]
+
+
+def _mixed():
+    """int8 48 x 512 in 2 column chunks of 256; e4m3 32 x 768 in one chunk
+    per band (results straight to Y); int8 64 x 2816 in 11 column chunks of
+    256: 63 chunks. Returns the specs and their columns per chunk."""
+    specs = [synth.random_int8_tensor(48, 512, 1.4, 720, 512),
+             synth.e4m3_matrix(rows=32, cols=768)[0],
+             synth.random_int8_tensor(64, 2816, 2.3, 721, 2816)]
+    Cs = {sp["name"]: c for sp, c in zip(specs, (256, 768, 256))}
+    return specs, (lambda sp: Cs[sp["name"]])
+
+
+def test_codes_decode_in_tile_order(E):
+    """The container is an ordinary one: entq_decode returns its codes in
+    tile order, equal to the oracle's tile order of the source codes."""
+    import torch
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    out = torch.empty(p.out_elems, dtype=torch.uint8, device="cuda")
+    E.decode(p, blob, out, E.OUT_CODES)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    off = 0
+    for sp, ts in zip(specs, tiled):
+        n = sp["rows"] * sp["cols"]
+        want = oracle.tile_order(np.ascontiguousarray(sp["symbols"]).view(np.uint8),
+                                 sp["rows"], sp["cols"], ts["C"])
+        assert np.array_equal(got[off:off + n], want), sp["name"]
+        off += n
+
+
+def test_one_hot_activations_return_the_oracle_weights_exactly(E):
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    W = _oracle_weights(b, tiled)
+    rng = np.random.default_rng(41)
+    for m in (1, 5, 16, 17, 33, 64):
+        _say(f"one-hot, m={m}")
+        xs, hit = [], []
+        for sp in specs:
+            c = rng.choice(sp["cols"], m, replace=False)
+            x = np.zeros((m, sp["cols"]), np.float32)
+            x[np.arange(m), c] = 1.0
+            xs.append(x)
+            hit.append(c)
+        ys = _run(E, p, blob, scales, xs, specs, extra_rows=1)
+        for t in range(len(specs)):
+            want = _f32(W[t][:, hit[t]]).T
+            assert np.array_equal(ys[t][:m].view(np.uint32), want.view(np.uint32)), (t, m)
+            assert np.isnan(ys[t][m]).all(), (t, m)  # nothing written past m rows
+
+
+def test_random_activations_within_the_accumulation_bound(E):
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    W = _oracle_weights(b, tiled)
+    rng = np.random.default_rng(42)
+    for m, pad_x, pad_y in ((16, 0, 0), (3, 12, 2), (40, 4, 0), (64, 0, 5)):
+        _say(f"random, m={m}, padded strides {pad_x}/{pad_y}")
+        xs = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+                   & np.uint16(0xBFFF)) for sp in specs]  # finite bf16 values, |x| < 4
+        ys = _run(E, p, blob, scales, xs, specs, pad_x, pad_y)
+        for t, sp in enumerate(specs):
+            assert oracle_rows.check_product(ys[t][:, :sp["rows"]], xs[t], W[t]) == sp["rows"]
+            if pad_y:
+                assert np.isnan(ys[t][:, sp["rows"]:]).all()
+
+
+def test_results_are_reproducible_and_the_workspace_is_checked(E):
+    import torch
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    rng = np.random.default_rng(43)
+    for m in (1, 4, 16, 40):
+        _say(f"workspace over stale bytes, m={m}")
+        xs = [rng.standard_normal((m, sp["cols"])).astype(np.float32) for sp in specs]
+        n = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, m))
+        # partial sums of the two tensors split in columns (2 x 48 and 11 x 64
+        # rows, x m x 4 bytes) and, above one row, the packed activations
+        groups = -(-m // 16)
+        want = sum(-(-4 * k * m * r // 256) * 256 for k, r in ((2, 48), (11, 64)))
+        if m > 1:
+            want += sum(-(-32 * groups * sp["cols"] // 256) * 256 for sp in specs)
+        assert n == want, m
+        ws = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")  # stale bytes
+        a = _run(E, p, blob, scales, xs, specs, workspace=ws)
+        c = _run(E, p, blob, scales, xs, specs)
+        for t in range(len(specs)):
+            assert np.array_equal(a[t].view(np.uint32), c[t].view(np.uint32)), (t, m)
+    xd = [torch.zeros(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+    yd = [torch.zeros(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+    n = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, m))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_tiles(p, blob, scales, xd, yd, workspace=ws[:n - 256])
+    raw = torch.empty(n + 512, dtype=torch.uint8, device="cuda")
+    base = (-raw.data_ptr()) % 256
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_tiles(p, blob, scales, xd, yd, workspace=raw[base + 16:base + 16 + n])
+
+
+def test_rejects_tensors_outside_the_tile_layout(E):
+    import torch
+    x = torch.zeros(2, 512, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(2, 40, dtype=torch.float32, device="cuda")
+    # 40 rows (not a multiple of 16)
+    sp = synth.random_int8_tensor(40, 512, 1.0, 722, 16 * 256)
+    b = E.encode_batch([sp])
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    blob = torch.from_numpy(b.blob).cuda()
+    sc = torch.from_numpy(sp["scales"]).cuda()
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_tiles(p, blob, sc, [x], [y])
+    # chunks of 16 x 384 columns: 384 does not divide 512
+    sp = synth.random_int8_tensor(32, 512, 1.0, 723, 16 * 384)
+    b = E.encode_batch([sp])
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_tiles(p, torch.from_numpy(b.blob).cuda(),
+                            torch.from_numpy(sp["scales"]).cuda(),
+                            [x], [torch.zeros(2, 32, dtype=torch.float32, device="cuda")])
+
+
+def test_corrupt_chunks_report_the_decodes_status(E):
+    import torch
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    rng = np.random.default_rng(44)
+    blob_h = b.blob.copy()
+    bad = rng.choice(b.chunks.size, 20, replace=False)
+    for c in bad:
+        ch = b.chunks[c]
+        lo = int(ch["byte_offset"]) + 256
+        pos = rng.integers(lo, lo + 2 * int(ch["n_words"]), 3)
+        blob_h[pos] ^= np.uint8(0x5A)
+    blob = torch.from_numpy(blob_h).cuda()
+    out = torch.empty(p.out_elems, dtype=torch.uint8, device="cuda")
+    want = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, blob, out, E.OUT_CODES, None, want)
+    torch.cuda.synchronize()
+    want = want.cpu().numpy()
+    assert (want != 0).sum() >= 10
+    for m in (1, 16, 40):
+        _say(f"corrupt chunks, m={m}")
+        xs = [torch.ones(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+        ys = [torch.empty(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+        got = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+        E.decode_gemm_tiles(p, blob, scales, xs, ys, got)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), want), m
+
+
+def test_llama2_70b_layer_every_row(E):
+    """A whole 70B-shaped layer in tile order with 4,096 columns per chunk
+    (65,536 symbols: 2 column chunks of the 8,192-column tensors, 7 of the
+    down projection), every output row against the oracle's weights, for
+    m = 16, 64 and 1."""
+    specs = synth.llama2_70b_layer(0)
+    tiled, b, p, blob, scales = _tiled(E, specs, lambda sp: 4096)
+    rng = np.random.default_rng(45)
+    runs = []
+    for m in (16, 64, 1):
+        _say(f"70B-shaped layer 0 in tile order, m = {m}")
+        xs = [(rng.standard_normal((m, sp["cols"])) * 0.5).astype(np.float32) for sp in specs]
+        xs = [_f32((x.view(np.uint32) >> 16).astype(np.uint16)) for x in xs]  # bf16 values
+        runs.append((m, xs, _run(E, p, blob, scales, xs, specs)))
+    _say("oracle weights of layer 0")
+    W = _oracle_weights(b, tiled)
+    for t, sp in enumerate(specs):
+        for m, xs, ys in runs:
+            assert oracle_rows.check_product(ys[t], xs[t], W[t]) == sp["rows"], (sp["name"], m)

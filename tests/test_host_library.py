@@ -109,6 +109,22 @@ def test_bf16_split_matches_oracle(E):
     np.testing.assert_array_equal(s1, s2)
 
 
+@pytest.mark.parametrize("rows,cols,C", [(16, 16, 16), (32, 64, 32), (48, 768, 256),
+                                         (64, 4096, 1024), (16, 28672, 4096)])
+def test_tile_order_matches_oracle(E, rows, cols, C):
+    rng = np.random.default_rng(rows * 7 + C)
+    w = rng.integers(0, 256, rows * cols, dtype=np.uint8)
+    np.testing.assert_array_equal(E.tile_order(w, rows, cols, C, n_threads=3),
+                                  oracle.tile_order(w, rows, cols, C))
+
+
+def test_tile_order_rejects_shapes_outside_the_layout(E):
+    w = np.zeros(64 * 48, np.uint8)
+    for rows, cols, C in ((24, 128, 64), (48, 64, 24), (48, 64, 48), (48, 64, 0)):
+        with pytest.raises(E.EntqError):
+            E.tile_order(w[:rows * cols], rows, cols, C)
+
+
 def test_encode_batch_matches_oracle_container(E):
     specs = [synth.random_int8_tensor(64, 192, 1.5, s, 4096) for s in range(3)]
     b = E.encode_batch(specs, n_threads=2)
@@ -251,3 +267,5 @@ def test_device_calls_validate_before_launching(E):
     assert L.entq_pack_device_adaptive_batch(pack.ctypes.data, 1, fake, None) == -1
     # fused product: workspace size of no plan
     assert L.entq_decode_gemm_workspace_bytes(None, 16) == 0
+    assert L.entq_decode_gemm_tiles_workspace_bytes(None, 16) == 0
+    assert L.entq_decode_gemm_tiles(None, fake, fake, fake, 16, None, 0, None, None) == -1
