@@ -78,6 +78,9 @@ def parse():
     ap.add_argument("--row-chunk-max", type=int, default=8192,
                     help="fused: a chunk holds as many whole rows as fit in this many symbols "
                          "(at least one; 8192: one row of every 70B-shaped tensor per chunk)")
+    ap.add_argument("--tile-cols", type=int, default=8192,
+                    help="fused: columns per tile-ordered chunk (the widest multiple of 16 "
+                         "dividing a tensor's columns that is at most this)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain fp32 negate (read N MiB, write N MiB) before timing, as a "
                          "known-size reference for hardware byte counters")
@@ -752,14 +755,53 @@ def compressed_layers_row_aligned(args, E, synth, dev, torch, row_chunk_max=None
     return layers, out_elems, tens, meta0
 
 
+def tile_cols(cols, target):
+    """Columns per tile-ordered chunk: the widest multiple of 16 that divides
+    cols and is at most target."""
+    for k in range(1, cols + 1):
+        if cols % k == 0 and (cols // k) % 16 == 0 and cols // k <= target:
+            return cols // k
+    raise ValueError(f"no tile width for {cols} columns")
+
+
+def compressed_layers_tiled(args, E, synth, dev, torch, target):
+    """The 80 layers in tile order (chunks of 16 rows x tile_cols(cols,
+    target) columns), put in order on the host and encoded on the device."""
+    nthreads = args.threads or synth.default_threads()
+    t0 = time.time()
+    layers, meta0 = [], None
+    for layer in range(args.layers):
+        specs = synth.llama2_70b_layer(layer, nthreads=nthreads)
+        ds = []
+        for sp in specs:
+            C = tile_cols(sp["cols"], target)
+            st = E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C, nthreads)
+            ds.append(dict(sp, symbols=torch.from_numpy(st).to(dev), chunk_symbols=16 * C, C=C))
+        b = E.encode_batch_device(ds)
+        p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
+        sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)
+        layers.append((p, b.blob.clone(), sc))
+        if layer == 0:
+            meta0 = (b.chunks, b.freq, [dict(sp, symbols=None) for sp in ds])
+        del ds, b
+        if layer % 10 == 0 or layer == args.layers - 1:
+            log(f"layer {layer} encoded on the device in tile order, chunks of 16 rows x at most "
+                f"{target} columns ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return layers, meta0
+
+
 def bench_fused(args):
     """One step = one pass over the 80 layers computing every projection
     Y = X . W^T (q,k,v,gate,up from X [m, 8192], o from an [m, 8192] and down
     from an [m, 28672] activation, synthetic bf16) for m activation rows.
-    Fused: one entq_decode_gemm launch per layer (fp32 Y, the bf16 weights
-    never written; matrix cores for m > 4, the vector units inside the
-    decode loop for m <= 4) on a container of one-row chunks
-    (--row-chunk-max).
+    Fused: one entq_decode_gemm_tiles call per layer (fp32 Y, the bf16
+    weights never written) on the layers in tile order, chunks of 16 rows x
+    at most --tile-cols columns (8,192 columns; 7,168 for the down
+    projection). Beside it the row-major fused call, entq_decode_gemm, on a
+    container of one-row chunks (--row-chunk-max): matrix cores in 16-chunk
+    lockstep for m > 4, the vector units inside the decode loop for m <= 4.
     Unfused: entq_decode into a bf16 layer buffer, then seven torch.mm (bf16
     Y), on the container the decode runs fastest on (whole rows in chunks of
     at most 65,536 symbols, as the layer-decode line's). HIP events around
@@ -772,8 +814,9 @@ def bench_fused(args):
     E.lib()
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    layers, out_elems, tens, meta0 = compressed_layers_row_aligned(args, E, synth, dev, torch)
+    rows_layers, out_elems, tens, _ = compressed_layers_row_aligned(args, E, synth, dev, torch)
     dec_layers = compressed_layers_row_aligned(args, E, synth, dev, torch, 65536)[0]
+    layers, meta0 = compressed_layers_tiled(args, E, synth, dev, torch, args.tile_cols)
     names = [n for n, _, _ in synth.LLAMA2_70B_LAYER]
     views = [(names[t], int(tens["rows"][t]), int(tens["cols"][t]), int(tens["out_elem_offset"][t]))
              for t in range(len(tens))]
@@ -790,8 +833,21 @@ def bench_fused(args):
         ys = [torch.empty(m, r, dtype=torch.float32, device=dev) for n, r, c, o in views]
         yb = [torch.empty(m, r, dtype=torch.bfloat16, device=dev) for n, r, c, o in views]
 
+        ws_n = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(layers[0][0].handle, m))
+        ws_raw = torch.empty(ws_n + 256, dtype=torch.uint8, device=dev)
+        ws_at = (-ws_raw.data_ptr()) % 256
+        ws = ws_raw[ws_at:ws_at + ws_n] if ws_n else None
+
         def fused(ev=None):
             for li, (p_, blob, sc_) in enumerate(layers):
+                if ev is not None:
+                    ev[li][0].record(stream)
+                E.decode_gemm_tiles(p_, blob, sc_, xs, ys, None, stream, ws)
+                if ev is not None:
+                    ev[li][1].record(stream)
+
+        def fused_row_chunks(ev=None):
+            for li, (p_, blob, sc_) in enumerate(rows_layers):
                 if ev is not None:
                     ev[li][0].record(stream)
                 E.decode_gemm(p_, blob, sc_, xs, ys, None, stream)
@@ -818,7 +874,8 @@ def bench_fused(args):
                     ev[li][1].record(stream)
 
         row = {"m": m}
-        for name, fn in (("fused", fused), ("unfused", unfused), ("decode_only", decode_only)):
+        for name, fn in (("fused", fused), ("fused_row_chunks", fused_row_chunks),
+                         ("unfused", unfused), ("decode_only", decode_only)):
             for _ in range(args.warmup):
                 fn()
             torch.cuda.synchronize()
@@ -834,7 +891,7 @@ def bench_fused(args):
         row["speedup"] = row["unfused_ms_per_step"] / row["fused_ms_per_step"]
         log(f"fused m={m}: " + ", ".join(f"{k} {v:.3f}" for k, v in row.items() if k != "m"))
         results.append(row)
-        del X, H, xs, ys, yb
+        del X, H, xs, ys, yb, ws, ws_raw
     split = fused_bf16_split_case(E, synth, torch, dev, stream, args)
     split_m1 = fused_bf16_split_case(E, synth, torch, dev, stream, args, m=1)
     cpu = None
@@ -866,9 +923,13 @@ def bench_fused(args):
             "layers": args.layers,
             "params_per_layer": out_elems,
             "compressed_bytes_per_layer": blob_mean,
-            "chunking": f"fused: whole rows, at most {args.row_chunk_max} symbols per chunk "
-                        "(at least one row); unfused and decode only: whole rows, at most "
-                        "65,536 symbols per chunk",
+            "chunking": f"fused: tile order, chunks of 16 rows x at most {args.tile_cols} "
+                        "columns (the widest multiple of 16 dividing the tensor's columns); "
+                        f"fused_row_chunks: whole rows, at most {args.row_chunk_max} symbols "
+                        "per chunk (at least one row); unfused and decode only: whole rows, at "
+                        "most 65,536 symbols per chunk",
+            "fused_row_chunks_compressed_bytes_per_layer": float(np.mean([l[1].numel()
+                                                                          for l in rows_layers])),
             "unfused_compressed_bytes_per_layer": float(np.mean([l[1].numel()
                                                                  for l in dec_layers])),
             "results": results,
@@ -943,10 +1004,12 @@ def fused_bf16_split_case(E, synth, torch, dev, stream, args, m=16, chunk_rows=N
 
 
 def fused_cpu_baseline(E, layer0, meta0, views, stream, torch, dev, m=16, n_tensors=4):
-    """The oracle (single-threaded C decode + dequant, then a one-thread fp64
-    product) for the first n_tensors tensors of layer 0 and m = 16
-    activation rows, timed on this host; the GPU's fused results for the
-    same tensors must lie within the fp32 accumulation bound of it."""
+    """The oracle (single-threaded C decode of the tile-ordered chunks, the
+    inverse of the tile order, C dequant, then a one-thread fp64 product) for
+    the first n_tensors tensors of layer 0 and m = 16 activation rows, timed
+    on this host; the GPU's fused results for the same tensors must lie
+    within the fp32 accumulation bound of it."""
+    import oracle
     from threadpoolctl import threadpool_limits
     p0, blob_d, sc_d = layer0
     chunks, freq, specs = meta0
@@ -956,30 +1019,37 @@ def fused_cpu_baseline(E, layer0, meta0, views, stream, torch, dev, m=16, n_tens
     H = (torch.randn(m, 28672, generator=gen) * 0.5).to(torch.bfloat16)
     xs = [(H if n == "down" else X).to(dev) for n, r, c, o in views]
     ys = [torch.empty(m, r, dtype=torch.float32, device=dev) for n, r, c, o in views]
-    E.decode_gemm(p0, blob_d, sc_d, xs, ys, None, stream)
+    E.decode_gemm_tiles(p0, blob_d, sc_d, xs, ys, None, stream)
     torch.cuda.synchronize()
     xf = X.float().numpy().astype(np.float64)
     spent, params, ok = 0.0, 0, True
     with threadpool_limits(1):
         for t in range(n_tensors):
             sp = specs[t]
-            ch = chunks[chunks["tensor"] == t]
-            bits, dt, n = oracle_tensor_sample(blob, ch, freq[t], sp, len(ch))
+            rows, cols = int(sp["rows"]), int(sp["cols"])
+            ch = np.sort(chunks[chunks["tensor"] == t], order="elem_offset")
+            desc = np.stack([ch["n_symbols"], ch["n_words"], ch["byte_offset"],
+                             ch["elem_offset"]], axis=1).astype(np.uint64)
             t0 = time.perf_counter()
+            sym, st = oracle.decode_tensor(blob, desc, freq[t], rows * cols)
+            codes = oracle.untile(sym, rows, cols, int(sp["C"]))
+            bits = oracle.dequant_tensor(codes.ravel(), rows, cols, sp["kind"], sp["scales"])
             w = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            w = w.reshape(sp["rows"], sp["cols"])
+            w = w.reshape(rows, cols)
             ref = xf @ w.T
-            spent += dt + time.perf_counter() - t0
-            bound = sp["cols"] * 2.0 ** -24 * (np.abs(xf) @ np.abs(w).T)
+            spent += time.perf_counter() - t0
+            assert (st == 0).all()
+            bound = cols * 2.0 ** -24 * (np.abs(xf) @ np.abs(w).T)
             ok &= bool((np.abs(ys[t].cpu().numpy() - ref) <= bound).all())
-            params += n
+            params += rows * cols
     log(f"cpu oracle, fused sample: {params} weights x {m} rows in {spent:.2f}s "
         f"({params / spent / 1e6:.1f} M weights/s); GPU within bound: {ok}")
     if not ok:
         raise SystemExit("fused results differ from the oracle beyond the accumulation bound")
     return {"value": params / spent, "unit": "weights/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0, first {n_tensors} tensors ({params} weights), m = {m}: "
-                      "single-threaded C oracle decode + dequant, fp64 product on one thread"}
+            "sample": f"layer 0, first {n_tensors} tensors ({params} weights, tile order), "
+                      f"m = {m}: single-threaded C oracle decode + inverse tile order + "
+                      "dequant, fp64 product on one thread"}
 
 
 def bench_lm_head(args):

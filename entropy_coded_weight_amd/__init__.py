@@ -442,7 +442,8 @@ def decode_gemm_tiles(p: Plan, compressed, scales, xs, ys, chunk_status=None, st
     """decode_gemm for a plan of tile-ordered tensors (entq_decode_gemm_tiles):
     xs, ys as for decode_gemm (m <= 64). workspace: a device uint8 tensor
     (256-byte aligned, entq_decode_gemm_tiles_workspace_bytes long) for the
-    column chunks' partial sums, or None to allocate one when needed."""
+    packed activations and the column chunks' partial sums, or None to
+    allocate one."""
     import torch
     io, m = _gemm_io(p, xs, ys)
     _blob_buffer(p, "compressed", compressed)

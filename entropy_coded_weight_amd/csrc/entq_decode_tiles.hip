@@ -21,9 +21,10 @@
 // columns) and issues one MFMA per 16 activation rows. No LDS stage, no
 // workgroup barrier, no lockstep: every wave walks its own run of chunks as
 // in the bf16 decode (word ring, slot table and progress priority
-// unchanged). At a chunk's end the wave holds Y for its 16 weight rows over
+// unchanged). The activations are first copied into the order the waves
+// read them. At a chunk's end the wave holds Y for its 16 weight rows over
 // the chunk's C columns: it writes them straight to Y when the chunk spans
-// all columns, else to a partial-sum slot of the workspace, and a second
+// all columns, else to a partial-sum slot of the workspace, and a last
 // kernel adds the column chunks' partial sums in column order.
 #include <hip/hip_runtime.h>
 
@@ -39,11 +40,10 @@ constexpr uint32_t kTileM = 16;       // activation rows of one MFMA
 constexpr int kTileMaxGroups = 4;     // up to 64 activation rows
 
 struct TileTensor {
-    const uint16_t *x;  // bf16 activations: m rows, row stride ldx elements,
-                        // or their packed copy (PACKED)
+    const uint16_t *x;  // the packed copy of the activations (see tile_chunk)
     float *y;           // fp32 results: m rows, row stride ldy
     float *part;        // partial sums [n_cc][m][rows], when n_cc > 1
-    uint64_t ldx, ldy;
+    uint64_t ldy;
     uint64_t out0;      // the tensor's first stream element (out_elem_offset)
     uint64_t row0;      // its first scale row
     uint32_t rows, chunk_cols, n_cc;
@@ -86,12 +86,14 @@ __device__ __forceinline__ uint32_t dequant2_lane(uint32_t d, float scale) {
     return E4M3 ? e4m3_nan_patch2(d, r) : r;
 }
 
-// PACKED: x is the packed copy of the activations (launch_pack_activations):
-// the A fragments of one 16-column slice and group are 512 contiguous bytes,
-// where the activations' own layout gives 16 rows of 32 bytes (partial cache
-// lines, which cost more than the pre-pass copy once more than a few rows
-// are read).
-template <int MT, bool E4M3, bool PRIO, bool PACKED>
+// The activations are read from their packed copy (launch_pack_activations):
+// the A fragments of one 16-column slice and group of 16 rows are 512
+// contiguous bytes, where the activations' own layout gives 16 rows of 32
+// bytes (partial cache lines). Measured on 70B-shaped layers with
+// 8,192-column chunks, reading X in its own layout: m = 1, 2, 4: 356.0,
+// 358.5, 363.7 us, m = 16 419.8 us, m = 64 1,549 us; from the packed copy:
+// m = 2 .. 16 336-343 us, m = 64 539 us (the copy included).
+template <int MT, bool E4M3, bool PRIO>
 __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__restrict__ blob,
                                            const uint2 *T, uint16_t *ring_lds, uint32_t lane,
                                            const float *__restrict__ scales, const TileTensor &gt,
@@ -106,15 +108,11 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
     const uint32_t band = (uint32_t)(k / gt.n_cc), cc = (uint32_t)(k % gt.n_cc);
     const uint32_t r16 = lane & 15;                  // weight row in the band; activation row
     const float scale = scales[gt.row0 + 16ull * band + r16];
-    // activations: a uniform base and 32-bit byte offsets (the host keeps
-    // ldx <= 2^24, so 64 rows span less than 2 GiB), so the loads need no
-    // 64-bit address registers per group
+    // activations: a uniform base and 32-bit byte offsets (a packed copy
+    // holds 32 x groups x cols bytes), so the loads need no 64-bit address
+    // registers per group
     const uint8_t *xb = reinterpret_cast<const uint8_t *>(gt.x);
-    const uint32_t xoff =
-        PACKED ? 2u * ((cc * C / 16u) * MT * 256u + 4u * lane)
-               : 2u * (r16 * (uint32_t)gt.ldx + cc * C + 4u * (lane >> 4));
-    const uint32_t group_bytes = PACKED ? 512u : 32u * (uint32_t)gt.ldx;
-    const uint32_t tile_bytes = PACKED ? 512u * MT : 32u;  // per 16-column slice
+    const uint32_t xoff = 2u * ((cc * C / 16u) * MT * 256u + 4u * lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states, scale, first ring units
     s.landed = s.issued;
     ring_horizon(s);
@@ -131,14 +129,8 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
         // for all but the latest operation requires)
         uint2 a[MT];
 #pragma unroll
-        for (int g = 0; g < MT; ++g) {
-            const uint2 *src =
-                reinterpret_cast<const uint2 *>(xb + (xoff + g * group_bytes + tile_bytes * t));
-            if (PACKED)  // rows m and beyond are zeros in the packed copy
-                a[g] = *src;
-            else
-                a[g] = (16u * g + r16 < m) ? *src : make_uint2(0, 0);
-        }
+        for (int g = 0; g < MT; ++g)  // (rows m and beyond are zeros in the copy)
+            a[g] = *reinterpret_cast<const uint2 *>(xb + (xoff + (t * MT + g) * 512u));
         const uint32_t e0 = tile_step(x, s.pos, T, lane);
         const uint32_t e1 = tile_step(x, s.pos, T, lane);
         const uint32_t e2 = tile_step(x, s.pos, T, lane);
@@ -181,7 +173,7 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
 // amdgpu_waves_per_eu(8): at most 64 vector registers per lane, so that two
 // 16-wave workgroups share a CU also with four 16-row groups of activations
 // (the compiler would otherwise take 78 there and halve the waves).
-template <int MT, bool PRIO, bool PACKED>
+template <int MT, bool PRIO>
 __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS
 __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
     const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
@@ -212,11 +204,11 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         if (e4m3)
-            tile_chunk<MT, true, PRIO, PACKED>(ch, blob, T, RING[wave], lane, scales, gt, args.m,
-                                               pr, status);
+            tile_chunk<MT, true, PRIO>(ch, blob, T, RING[wave], lane, scales, gt, args.m, pr,
+                                       status);
         else
-            tile_chunk<MT, false, PRIO, PACKED>(ch, blob, T, RING[wave], lane, scales, gt, args.m,
-                                                pr, status);
+            tile_chunk<MT, false, PRIO>(ch, blob, T, RING[wave], lane, scales, gt, args.m, pr,
+                                        status);
     }
 }
 
@@ -246,40 +238,20 @@ __global__ __launch_bounds__(256) void reduce_partials(ReduceArgs args) {
     rt.y[mrow * rt.ldy + r] = sum;
 }
 
-template <int MT, bool PACKED>
+template <int MT>
 void launch_tiles_mt(bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
                      const uint8_t *blob, const float *scales, int32_t *status,
                      const TileArgs &args) {
     const dim3 block(kThreads);
     if (prio)
-        hipLaunchKernelGGL((decode_tile_gemm<MT, true, PACKED>), grid, block, 0, st,
-                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
-                           scales, status, args);
+        hipLaunchKernelGGL((decode_tile_gemm<MT, true>), grid, block, 0, st, plan->d_tables,
+                           plan->d_tensors, plan->d_chunks, plan->d_tasks, blob, scales, status,
+                           args);
     else
-        hipLaunchKernelGGL((decode_tile_gemm<MT, false, PACKED>), grid, block, 0, st,
-                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
-                           scales, status, args);
+        hipLaunchKernelGGL((decode_tile_gemm<MT, false>), grid, block, 0, st, plan->d_tables,
+                           plan->d_tensors, plan->d_chunks, plan->d_tasks, blob, scales, status,
+                           args);
 }
-
-template <bool PACKED>
-void launch_tiles(int groups, bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
-                  const uint8_t *blob, const float *scales, int32_t *status,
-                  const TileArgs &args) {
-    if (groups == 1)
-        launch_tiles_mt<1, PACKED>(prio, grid, st, plan, blob, scales, status, args);
-    else if (groups == 2)
-        launch_tiles_mt<2, PACKED>(prio, grid, st, plan, blob, scales, status, args);
-    else if (groups == 3)
-        launch_tiles_mt<3, PACKED>(prio, grid, st, plan, blob, scales, status, args);
-    else
-        launch_tiles_mt<4, PACKED>(prio, grid, st, plan, blob, scales, status, args);
-}
-
-// Activations are packed (launch_pack_activations) above this many rows:
-// with one row only the lanes of row 0 load anything at all. (70B-shaped
-// layers, 8,192-column chunks: m = 2, 4 unpacked 358.5, 363.7 us; packed
-// m = 5, 8, 16: 339.2, 338.1, 343.3 us; m = 1 unpacked 356.0 us.)
-constexpr int kTilePackAbove = 1;
 
 uint64_t part_bytes(const HostTensor &h, int m) {
     const uint32_t C = h.chunk_symbols / 16;
@@ -288,16 +260,15 @@ uint64_t part_bytes(const HostTensor &h, int m) {
     return ((uint64_t)ncc * m * h.rows * 4 + 255) & ~(uint64_t)255;
 }
 
-// Workspace: the packed activations (m > kTilePackAbove), then the partial
-// sums, tensor by tensor in plan order.
+// Workspace: the packed activations, then the partial sums, tensor by tensor
+// in plan order.
 uint64_t tiles_workspace_bytes(const entq_plan_t *plan, int m) {
     const int groups = (m + (int)kTileM - 1) / (int)kTileM;
     uint64_t total = 0;
     for (int t = 0; t < plan->n_tensors; ++t) {
         const HostTensor &h = plan->host_tensors[(size_t)t];
         if (h.n_symbols == 0) continue;
-        if (m > kTilePackAbove) total += packed_bytes(h.cols, groups);
-        total += part_bytes(h, m);
+        total += packed_bytes(h.cols, groups) + part_bytes(h, m);
     }
     return total;
 }
@@ -316,7 +287,6 @@ entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, in
         if (h.cols == 0 || h.cols % C) return ENTQ_EINVAL;
         const entq_gemm_io &g = io[t];
         if (!g.d_x || !g.d_y || g.ldx < h.cols || g.ldy < h.rows) return ENTQ_EINVAL;
-        if (g.ldx > (1u << 24)) return ENTQ_EINVAL;  // 64 rows of x within 32-bit offsets
         if ((uintptr_t)g.d_x % 8 || g.ldx % 4 || (uintptr_t)g.d_y % 4) return ENTQ_EALIGN;
     }
     return ENTQ_OK;
@@ -342,7 +312,7 @@ entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compre
     if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
     if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
     const uint64_t need = tiles_workspace_bytes(plan, m);
-    if (need && !d_workspace) return ENTQ_EWORKSPACE;
+    if (need && !d_workspace) return ENTQ_EWORKSPACE;  // (need > 0 for any tensor)
     if (d_workspace && (uintptr_t)d_workspace % 256) return ENTQ_EALIGN;
     if (workspace_bytes < need) return ENTQ_EWORKSPACE;
     if (plan->n_tasks == 0) return ENTQ_OK;
@@ -354,22 +324,18 @@ entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compre
     uint64_t off = 0, red_blocks = 0;
     uint8_t *ws = static_cast<uint8_t *>(d_workspace);
     const int groups = (m + (int)kTileM - 1) / (int)kTileM;
-    const bool packed = m > kTilePackAbove;
     uint64_t pack_off[kTileMaxTensors] = {};
-    if (packed)
-        for (int t = 0; t < plan->n_tensors; ++t)
-            if (plan->host_tensors[(size_t)t].n_symbols) {
-                pack_off[t] = off;
-                off += packed_bytes(plan->host_tensors[(size_t)t].cols, groups);
-            }
+    for (int t = 0; t < plan->n_tensors; ++t)
+        if (plan->host_tensors[(size_t)t].n_symbols) {
+            pack_off[t] = off;
+            off += packed_bytes(plan->host_tensors[(size_t)t].cols, groups);
+        }
     for (int t = 0; t < plan->n_tensors; ++t) {
         const HostTensor &h = plan->host_tensors[(size_t)t];
         if (h.n_symbols == 0) continue;
         TileTensor &g = args.t[t];
-        g.x = packed ? reinterpret_cast<const uint16_t *>(ws + pack_off[t])
-                     : static_cast<const uint16_t *>(io[t].d_x);
+        g.x = reinterpret_cast<const uint16_t *>(ws + pack_off[t]);
         g.y = io[t].d_y;
-        g.ldx = io[t].ldx;
         g.ldy = io[t].ldy;
         g.out0 = h.out_elem_offset;
         g.row0 = h.scale_row_offset;
@@ -390,13 +356,16 @@ entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compre
     const bool prio = plan->n_chunks > plan->n_tasks;
     const dim3 grid((unsigned)plan->n_tasks);
     const uint8_t *b = static_cast<const uint8_t *>(d_compressed);
-    if (packed) {
-        const int r = launch_pack_activations(plan, io, m, pack_off, ws, stream);
-        if (r != ENTQ_OK) return (entq_status)r;
-        launch_tiles<true>(groups, prio, grid, s, plan, b, d_scales, d_chunk_status, args);
-    } else {
-        launch_tiles<false>(groups, prio, grid, s, plan, b, d_scales, d_chunk_status, args);
-    }
+    const int r = launch_pack_activations(plan, io, m, pack_off, ws, stream);
+    if (r != ENTQ_OK) return (entq_status)r;
+    if (groups == 1)
+        launch_tiles_mt<1>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    else if (groups == 2)
+        launch_tiles_mt<2>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    else if (groups == 3)
+        launch_tiles_mt<3>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    else
+        launch_tiles_mt<4>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
     if (red.n_tensors)
         hipLaunchKernelGGL(reduce_partials, dim3((unsigned)red_blocks), dim3(256), 0, s, red);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;

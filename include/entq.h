@@ -361,8 +361,7 @@ entq_status entq_tile_order(const uint8_t *codes, uint32_t rows, uint32_t cols,
                             uint32_t chunk_cols, uint8_t *out, int n_threads);
 
 /* Bytes of workspace entq_decode_gemm_tiles needs for this plan and m (0 for
- * invalid arguments, or for m = 1 when every tensor's chunks span all its
- * columns): for m > 1 the activations packed in the order the waves read
+ * invalid arguments): the activations packed in the order the waves read
  * them (as entq_decode_gemm_workspace_bytes counts them), and for each
  * tensor with cols / C > 1 column chunks 4 bytes x (cols / C) x m x rows of
  * partial sums, each rounded up to 256. */
@@ -372,17 +371,17 @@ uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m);
  * results, W_t the bf16 of code x row scale rounded to nearest even), for a
  * plan whose non-empty tensors (at most 16; kind INT8 or E4M3) are in tile
  * order: rows a multiple of 16, chunk_symbols = 16 C with C a multiple of
- * 16 that divides cols, and ldx at most 2^24 (else ENTQ_EINVAL). Every wave
+ * 16 that divides cols (else ENTQ_EINVAL). Every wave
  * decodes its own chunks and, for each 16 x 16 tile, issues one
  * v_mfma_f32_16x16x16_bf16
  * per 16 activation rows straight from its registers: no workgroup barrier
- * and no staging of weights. For m > 1 a first enqueued kernel copies the
- * activations into d_workspace in the order the waves read them (512
- * contiguous bytes per 16 columns and 16 rows). A chunk's 16 x C product
+ * and no staging of weights. A first enqueued kernel copies the activations
+ * into d_workspace in the order the waves read them (512 contiguous bytes
+ * per 16 columns and 16 rows). A chunk's 16 x C product
  * goes to Y directly when C = cols; otherwise to a partial-sum slot of
  * d_workspace, and a last enqueued kernel adds a row's column chunks in
- * column order. d_workspace: required whenever the size query is non-zero
- * (256-byte aligned, at least that size, else ENTQ_EALIGN /
+ * column order. d_workspace: required (256-byte aligned, at least
+ * entq_decode_gemm_tiles_workspace_bytes, else ENTQ_EALIGN /
  * ENTQ_EWORKSPACE; not used by other work while the call runs). Results are reproducible run to run and stay within
  * cols * 2^-24 * sum_c |X[i][c] W[r][c]| of the exact product; their
  * summation order differs from entq_decode_gemm's. d_chunk_status as in

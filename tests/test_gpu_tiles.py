@@ -162,11 +162,10 @@ def test_results_are_reproducible_and_the_workspace_is_checked(E):
         xs = [rng.standard_normal((m, sp["cols"])).astype(np.float32) for sp in specs]
         n = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, m))
         # partial sums of the two tensors split in columns (2 x 48 and 11 x 64
-        # rows, x m x 4 bytes) and, above one row, the packed activations
+        # rows, x m x 4 bytes) and the packed activations
         groups = -(-m // 16)
         want = sum(-(-4 * k * m * r // 256) * 256 for k, r in ((2, 48), (11, 64)))
-        if m > 1:
-            want += sum(-(-32 * groups * sp["cols"] // 256) * 256 for sp in specs)
+        want += sum(-(-32 * groups * sp["cols"] // 256) * 256 for sp in specs)
         assert n == want, m
         ws = torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")  # stale bytes
         a = _run(E, p, blob, scales, xs, specs, workspace=ws)
