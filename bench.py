@@ -776,7 +776,8 @@ def compressed_layers_tiled(args, E, synth, dev, torch, target):
         for sp in specs:
             C = tile_cols(sp["cols"], target)
             st = E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C, nthreads)
-            ds.append(dict(sp, symbols=torch.from_numpy(st).to(dev), chunk_symbols=16 * C, C=C))
+            ds.append(dict(sp, symbols=torch.from_numpy(st).to(dev), chunk_symbols=16 * C, C=C,
+                           kind=sp["kind"] | E.LAYOUT_TILES))
         b = E.encode_batch_device(ds)
         p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
         sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)
@@ -1033,7 +1034,8 @@ def fused_cpu_baseline(E, layer0, meta0, views, stream, torch, dev, m=16, n_tens
             t0 = time.perf_counter()
             sym, st = oracle.decode_tensor(blob, desc, freq[t], rows * cols)
             codes = oracle.untile(sym, rows, cols, int(sp["C"]))
-            bits = oracle.dequant_tensor(codes.ravel(), rows, cols, sp["kind"], sp["scales"])
+            bits = oracle.dequant_tensor(codes.ravel(), rows, cols, sp["kind"] & 0xFF,
+                                         sp["scales"])
             w = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
             w = w.reshape(rows, cols)
             ref = xf @ w.T

@@ -31,6 +31,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libentq.so")
 
 KIND_INT8, KIND_E4M3, KIND_BF16EXP = 0, 1, 2
+LAYOUT_TILES = 0x100  # or'ed into a tensor's kind: its symbols are in tile order
 OUT_CODES, OUT_BF16 = 0, 1
 CHUNK_OK, CHUNK_BAD_STATE, CHUNK_BAD_WORDS = 0, 1, 2
 PROB_SCALE = 4096

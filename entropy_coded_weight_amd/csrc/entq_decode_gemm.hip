@@ -496,6 +496,7 @@ entq_status check_gemm_args(const entq_plan_t *plan, const entq_gemm_io *io, int
         if (split ? h.kind != ENTQ_SYM_BF16EXP
                   : (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3))
             return ENTQ_EINVAL;
+        if (h.tiles) return ENTQ_EINVAL;  // tile order: entq_decode_gemm_tiles
         if (h.cols == 0 || h.cols % entq::kBlockSyms || h.chunk_symbols % h.cols) return ENTQ_EINVAL;
         if (h.chunk_base > 0xFFFFFFFFll || h.n_chunks > 0xFFFFFFFFll) return ENTQ_EINVAL;
         const entq_gemm_io &g = io[t];

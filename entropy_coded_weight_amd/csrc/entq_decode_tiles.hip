@@ -281,6 +281,7 @@ entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, in
         const HostTensor &h = plan->host_tensors[(size_t)t];
         if (h.n_symbols == 0) continue;
         if (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3) return ENTQ_EINVAL;
+        if (!h.tiles) return ENTQ_EINVAL;  // row-major symbols: entq_decode_gemm
         // chunks of 16 whole rows x C columns, C a multiple of 16 dividing cols
         if (h.rows % 16 || h.chunk_symbols % kBlockSyms) return ENTQ_EINVAL;
         const uint32_t C = h.chunk_symbols / 16;

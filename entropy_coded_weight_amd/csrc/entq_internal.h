@@ -83,7 +83,11 @@ struct HostTensor {
     int64_t n_chunks;
     uint64_t out_elem_offset;
     uint64_t scale_row_offset;
+    bool tiles;             // symbols in tile order (ENTQ_LAYOUT_TILES)
 };
+
+// In a plan's kinds_mask: some non-empty tensor is in tile order.
+constexpr uint32_t kTilesBit = 1u << 31;
 
 }  // namespace entq
 
@@ -104,7 +108,7 @@ struct entq_plan_s {
     uint64_t blob_bytes;
     uint64_t out_elems;
     uint64_t scale_rows;
-    uint32_t kinds_mask;        // bit k set if some non-empty tensor has kind k
+    uint32_t kinds_mask;        // bit k set if some non-empty tensor has kind k; kTilesBit
     const entq::SlotEntry *d_tables;
     const entq::DevTensor *d_tensors;
     const entq::DevChunk *d_chunks;

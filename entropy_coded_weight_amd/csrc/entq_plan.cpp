@@ -96,7 +96,15 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     uint32_t kinds_mask = 0;
     for (int t = 0; t < n_tensors; ++t) {
         const entq_tensor_desc &td = tensors[t];
-        if (td.kind > ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
+        if (td.kind & ~(0xFFu | ENTQ_LAYOUT_TILES)) return ENTQ_EINVAL;
+        const uint32_t kind = td.kind & 0xFFu;
+        if (kind > ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
+        if (td.kind & ENTQ_LAYOUT_TILES) {
+            // 16-row bands of chunk_symbols / 16 columns, whole 16 x 16 tiles
+            if (adaptive || kind == ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
+            if (td.rows % 16 || td.chunk_symbols % entq::kBlockSyms) return ENTQ_EINVAL;
+            if (td.cols % (td.chunk_symbols / 16)) return ENTQ_EINVAL;
+        }
         if (td.chunk_symbols == 0 || td.chunk_symbols % entq::kLanes ||
             td.chunk_symbols > entq::kMaxChunkSymbols)
             return ENTQ_EINVAL;
@@ -105,13 +113,14 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
         if (adaptive) {
             // whole 256-symbol blocks; bf16 rows (scales) of whole blocks
             if (td.chunk_symbols % entq::kBlockSyms || td.out_elem_offset % 16) return ENTQ_EINVAL;
-            if (td.kind != ENTQ_SYM_BF16EXP && td.cols % entq::kBlockSyms) return ENTQ_EINVAL;
+            if (kind != ENTQ_SYM_BF16EXP && td.cols % entq::kBlockSyms) return ENTQ_EINVAL;
         } else {
             uint32_t sum = 0;
             for (int s = 0; s < 256; ++s) sum += freq_tables[(size_t)t * 256 + s];
             if (sum != entq::kProbScale) return ENTQ_EBADTABLE;
         }
-        kinds_mask |= 1u << td.kind;
+        kinds_mask |= 1u << kind;
+        if (td.kind & ENTQ_LAYOUT_TILES) kinds_mask |= entq::kTilesBit;
         if (td.out_elem_offset > UINT64_MAX - td.n_symbols) return ENTQ_EINVAL;
         out_elems = std::max(out_elems, td.out_elem_offset + td.n_symbols);
         scale_rows = std::max(scale_rows, td.scale_row_offset + td.rows);
@@ -251,7 +260,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
             }
         }
         dten[t].cols = tensors[t].cols;
-        dten[t].kind = tensors[t].kind;
+        dten[t].kind = tensors[t].kind & 0xFFu;
     }
     for (int t : order) {
         const entq_tensor_desc &td = tensors[t];
@@ -280,9 +289,9 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     }
     for (int t = 0; t < n_tensors; ++t) {
         const entq_tensor_desc &td = tensors[t];
-        host_tensors[t] = {td.kind, td.rows, td.cols, td.chunk_symbols, td.n_symbols,
+        host_tensors[t] = {td.kind & 0xFFu, td.rows, td.cols, td.chunk_symbols, td.n_symbols,
                            chunk_base[t], (int64_t)slot_of[t].size(), td.out_elem_offset,
-                           td.scale_row_offset};
+                           td.scale_row_offset, (td.kind & ENTQ_LAYOUT_TILES) != 0};
     }
     // the plan object exists before the copy is enqueued, so that no failure
     // after it has to free the copy's source
@@ -388,7 +397,7 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
     if ((uintptr_t)d_compressed % ENTQ_REGION_ALIGN || (uintptr_t)d_out % 16) return ENTQ_EALIGN;
     int mode = entq::kModeCodes;
     if (out_kind == ENTQ_OUT_BF16) {
-        if (plan->kinds_mask & (1u << ENTQ_SYM_BF16EXP)) return ENTQ_EINVAL;
+        if (plan->kinds_mask & ((1u << ENTQ_SYM_BF16EXP) | entq::kTilesBit)) return ENTQ_EINVAL;
         if (!d_scales) return ENTQ_EINVAL;
         if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
         mode = entq::kModeBf16;

@@ -100,11 +100,20 @@ typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
 #define ENTQ_CHUNK_BAD_WORDS 2  /* words ran out or were not all consumed  */
 #define ENTQ_CHUNK_BAD_TABLE 3  /* (per-chunk tables) the chunk's table does not sum to 4096 */
 
+/* A tensor whose symbols are in the library's tile order (entq_tile_order)
+ * carries this flag in its kind: ENTQ_SYM_INT8 | ENTQ_LAYOUT_TILES, or E4M3.
+ * The plan then requires rows a multiple of 16, chunk_symbols a multiple of
+ * 256 and chunk_symbols / 16 dividing cols (else ENTQ_EINVAL); such tensors
+ * go to entq_decode_gemm_tiles (or entq_decode with ENTQ_OUT_CODES, which
+ * returns the codes in tile order) and are refused by the row-major calls
+ * (ENTQ_OUT_BF16, entq_decode_gemm*). */
+#define ENTQ_LAYOUT_TILES 0x100u
+
 /* One tensor of a batch (40 bytes). rows x cols row-major; n_symbols must be
  * rows * cols. Output element i of the tensor goes to out[out_elem_offset +
  * i]; its scale is scales[scale_row_offset + i / cols]. */
 typedef struct {
-    uint32_t kind;            /* entq_symkind                                */
+    uint32_t kind;            /* entq_symkind, | ENTQ_LAYOUT_TILES           */
     uint32_t rows, cols;
     uint32_t chunk_symbols;   /* C: a positive multiple of 64, <= 2^20       */
     uint64_t n_symbols;
@@ -349,9 +358,10 @@ entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_e
  * + l (0 <= s < 4, 0 <= l < 64) of the chunk holds the weight at row
  * 16 b + l % 16, column c C + 16 t + 4 (l / 16) + s. Only the order of the
  * symbols changes; the table, coder and container are as for any tensor:
- * encode the reordered symbols with chunk_symbols = 16 C. entq_decode on
- * such a tensor returns its codes in tile order (ENTQ_OUT_CODES); its bf16
- * output, whose scale rows assume row-major order, is not meaningful. */
+ * encode the reordered symbols with chunk_symbols = 16 C and mark the tensor
+ * ENTQ_LAYOUT_TILES. entq_decode on such a tensor returns its codes in tile
+ * order (ENTQ_OUT_CODES); the bf16 output, whose scale rows assume row-major
+ * order, is refused. */
 
 /* The symbols of one row-major tensor (codes, rows x cols bytes) in tile
  * order with chunk_cols = C columns per chunk, into out (rows x cols bytes,
@@ -370,8 +380,9 @@ uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m);
 /* Y_t = X_t . W_t^T as entq_decode_gemm computes it (io[], m <= 64, fp32
  * results, W_t the bf16 of code x row scale rounded to nearest even), for a
  * plan whose non-empty tensors (at most 16; kind INT8 or E4M3) are in tile
- * order: rows a multiple of 16, chunk_symbols = 16 C with C a multiple of
- * 16 that divides cols (else ENTQ_EINVAL). Every wave
+ * order (kind | ENTQ_LAYOUT_TILES): rows a multiple of 16, chunk_symbols =
+ * 16 C with C a multiple of 16 that divides cols (else ENTQ_EINVAL). Every
+ * wave
  * decodes its own chunks and, for each 16 x 16 tile, issues one
  * v_mfma_f32_16x16x16_bf16
  * per 16 activation rows straight from its registers: no workgroup barrier

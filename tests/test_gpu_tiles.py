@@ -43,7 +43,8 @@ def _tiled(E, specs, C_of):
     for sp in specs:
         C = C_of(sp)
         st = E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C)
-        tiled.append(dict(sp, symbols=st, chunk_symbols=16 * C, C=C))
+        tiled.append(dict(sp, symbols=st, chunk_symbols=16 * C, C=C,
+                          kind=sp["kind"] | E.LAYOUT_TILES))
     b = E.encode_batch(tiled)
     p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
     blob = torch.from_numpy(b.blob).cuda()
@@ -61,7 +62,7 @@ def _oracle_weights(b, tiled):
         sym, st = oracle.decode_tensor(b.blob, desc, b.freq[t], sp["rows"] * sp["cols"])
         assert (st == 0).all()
         codes = oracle.untile(sym, sp["rows"], sp["cols"], sp["C"])
-        w = oracle.dequant_tensor(codes.ravel(), sp["rows"], sp["cols"], sp["kind"],
+        w = oracle.dequant_tensor(codes.ravel(), sp["rows"], sp["cols"], sp["kind"] & 0xFF,
                                   sp["scales"])
         out.append(w.reshape(sp["rows"], sp["cols"]))
     return out
@@ -184,26 +185,34 @@ def test_results_are_reproducible_and_the_workspace_is_checked(E):
         E.decode_gemm_tiles(p, blob, scales, xd, yd, workspace=raw[base + 16:base + 16 + n])
 
 
-def test_rejects_tensors_outside_the_tile_layout(E):
+def test_layouts_are_kept_apart(E):
+    """A tensor marked as tile-ordered goes to the tiled product only (codes
+    out of entq_decode too); a row-major one is refused by it."""
     import torch
-    x = torch.zeros(2, 512, dtype=torch.bfloat16, device="cuda")
-    y = torch.zeros(2, 40, dtype=torch.float32, device="cuda")
-    # 40 rows (not a multiple of 16)
-    sp = synth.random_int8_tensor(40, 512, 1.0, 722, 16 * 256)
-    b = E.encode_batch([sp])
-    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
-    blob = torch.from_numpy(b.blob).cuda()
-    sc = torch.from_numpy(sp["scales"]).cuda()
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    m = 2
+    xs = [torch.zeros(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+    ys = [torch.zeros(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+    out = torch.empty(p.out_elems, dtype=torch.int16, device="cuda")
     with pytest.raises(E.EntqError):
-        E.decode_gemm_tiles(p, blob, sc, [x], [y])
-    # chunks of 16 x 384 columns: 384 does not divide 512
-    sp = synth.random_int8_tensor(32, 512, 1.0, 723, 16 * 384)
-    b = E.encode_batch([sp])
-    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+        E.decode(p, blob, out, E.OUT_BF16, scales)
     with pytest.raises(E.EntqError):
-        E.decode_gemm_tiles(p, torch.from_numpy(b.blob).cuda(),
-                            torch.from_numpy(sp["scales"]).cuda(),
-                            [x], [torch.zeros(2, 32, dtype=torch.float32, device="cuda")])
+        E.decode_gemm(p, blob, scales, xs, ys)
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_static(p, blob, scales, xs, ys)
+    from entropy_coded_weight_amd.linear import linear
+    with pytest.raises(E.EntqError):  # more than 64 rows: would need the bf16 decode
+        linear(p, blob, scales, [torch.zeros(65, sp["cols"], dtype=torch.bfloat16,
+                                             device="cuda") for sp in specs],
+               [torch.zeros(65, sp["rows"], dtype=torch.float32, device="cuda")
+                for sp in specs])
+    # the same codes, row-major, in chunks of the same size: refused by the tiled call
+    rm = [dict(sp, chunk_symbols=16 * C_of(sp)) for sp in specs]
+    b2 = E.encode_batch(rm)
+    p2 = E.plan(b2.tensors, b2.freq, b2.chunks, b2.blob.size)
+    with pytest.raises(E.EntqError):
+        E.decode_gemm_tiles(p2, torch.from_numpy(b2.blob).cuda(), scales, xs, ys)
 
 
 def test_corrupt_chunks_report_the_decodes_status(E):

@@ -199,10 +199,33 @@ def test_plan_rejects_bad_inputs(E):
     t = b.tensors.copy()
     t[0]["kind"] = 7
     assert _try_plan(E, t, b.freq, b.chunks, bb) == -1
+    # unknown flag bits
+    t = b.tensors.copy()
+    t[0]["kind"] = E.KIND_INT8 | 0x200
+    assert _try_plan(E, t, b.freq, b.chunks, bb) == -1
     # workspace too small
     assert _try_plan(E, b.tensors, b.freq, b.chunks, bb, ws_bytes=1000) == -5
     # misaligned workspace
     assert _try_plan(E, b.tensors, b.freq, b.chunks, bb, ws=FAKE_WS + 64) == -4
+
+
+def test_plan_checks_the_tile_layout(E):
+    """A tensor marked ENTQ_LAYOUT_TILES needs rows in 16-row bands, whole
+    16 x 16 tiles per chunk and a chunk width dividing the columns; exponent
+    streams and per-chunk tables do not take it."""
+    def tiled(rows, cols, C, kind=E.KIND_INT8, seed=11):
+        sp = synth.random_int8_tensor(rows, cols, 1.5, seed, 16 * C)
+        sp["kind"] = kind | E.LAYOUT_TILES
+        return E.encode_batch([sp], n_threads=1)
+    b = tiled(32, 512, 256)   # accepted shape: validation passes up to the workspace
+    assert _try_plan(E, b.tensors, b.freq, b.chunks, b.blob.size, ws_bytes=1000) == -5
+    for rows, cols, C in ((24, 512, 256), (32, 512, 192), (32, 768, 512)):
+        b = tiled(rows, cols, C)
+        assert _try_plan(E, b.tensors, b.freq, b.chunks, b.blob.size) == -1, (rows, cols, C)
+    b = tiled(32, 512, 256)
+    t = b.tensors.copy()
+    t[0]["kind"] = E.KIND_BF16EXP | E.LAYOUT_TILES
+    assert _try_plan(E, t, b.freq, b.chunks, b.blob.size) == -1
 
 
 def test_plan_rejects_overlapping_outputs(E):
