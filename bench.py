@@ -1062,7 +1062,9 @@ def bench_lm_head(args):
     encoded in 32,768-symbol chunks (8,000 chunks, whole rows): the line's
     value is that bf16 decode; 65,536 and 16,384 are timed beside it. Also
     logits for m activation rows, fused (entq_decode_gemm) against decode +
-    torch.mm, on the one-row (8,192-symbol) and the 32,768 containers."""
+    torch.mm, on the one-row (8,192-symbol) and the 32,768 containers, and
+    fused on the tensor in tile order (entq_decode_gemm_tiles, chunks of 16
+    rows x 2,048 or 4,096 columns)."""
     import torch
 
     import entropy_coded_weight_amd as E
@@ -1114,6 +1116,18 @@ def bench_lm_head(args):
         log(f"lm head decode, {C}-symbol chunks ({nch}): {us:.1f} us, "
             f"{dec[C]['alg_gbs']:.0f} GB/s")
     W = out.view(torch.bfloat16)
+    # the same codes in tile order: 16-row bands of 2,048 or 4,096 columns
+    tiled = {}
+    head = synth.llama2_70b_lm_head(nthreads=nthreads, chunk_symbols=32768)[0]
+    for Ct in (2048, 4096):
+        st = E.tile_order(head["symbols"], rows, cols, Ct, nthreads)
+        b = E.encode_batch_device([dict(head, symbols=torch.from_numpy(st).to(dev),
+                                        chunk_symbols=16 * Ct,
+                                        kind=head["kind"] | E.LAYOUT_TILES)])
+        tiled[Ct] = (E.plan(b.tensors, b.freq, b.chunks, b.blob.numel()), b.blob.clone(),
+                     torch.from_numpy(head["scales"]).to(dev), int(b.blob.numel()))
+        del b, st
+    del head
     logits = []
     gen = torch.Generator().manual_seed(0)
     for m in [int(v) for v in (args.tokens or "16,1").split(",") if v]:
@@ -1133,6 +1147,14 @@ def bench_lm_head(args):
                            "speedup": u_us / f_us})
             log(f"lm head logits m={m}, {C}-symbol chunks: fused {f_us:.1f} us, "
                 f"decode + GEMM {u_us:.1f} us")
+        for Ct, (p, blob, sc, nbytes) in tiled.items():
+            n_ws = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, m))
+            raw = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
+            ws = raw[(-raw.data_ptr()) % 256:][:n_ws]
+            f_us = timed(lambda: E.decode_gemm_tiles(p, blob, sc, [X], [Y], None, stream, ws),
+                         reps)
+            logits.append({"m": m, "tile_cols": Ct, "compressed_bytes": nbytes, "fused_us": f_us})
+            log(f"lm head logits m={m}, tile order, 16 x {Ct} chunks: fused {f_us:.1f} us")
     cpu = None
     if not args.no_cpu_baseline:
         p, blob, sc, nbytes, nch = conts[32768]

@@ -263,3 +263,19 @@ def test_llama2_70b_layer_every_row(E):
     for t, sp in enumerate(specs):
         for m, xs, ys in runs:
             assert oracle_rows.check_product(ys[t], xs[t], W[t]) == sp["rows"], (sp["name"], m)
+
+
+def test_lm_head_in_tile_order_every_row(E):
+    """The 32,000 x 8,192 output projection alone, in tile order with 2,048
+    columns per chunk (8,000 chunks, 4 column chunks per band: the partial
+    sums and their reduction at full size), every output row at m = 16."""
+    specs = synth.llama2_70b_lm_head(chunk_symbols=32768)
+    tiled, b, p, blob, scales = _tiled(E, specs, lambda sp: 2048)
+    rng = np.random.default_rng(46)
+    m = 16
+    _say("LM head in tile order, m = 16")
+    x = _f32(((rng.standard_normal((m, 8192)) * 0.5).astype(np.float32).view(np.uint32)
+              >> 16).astype(np.uint16))
+    ys = _run(E, p, blob, scales, [x], specs)
+    W = _oracle_weights(b, tiled)
+    assert oracle_rows.check_product(ys[0], x, W[0]) == specs[0]["rows"]
