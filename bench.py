@@ -998,8 +998,25 @@ def fused_bf16_split_case(E, synth, torch, dev, stream, args, m=16, chunk_rows=N
          "unfused_us": med(unfused),
          "split_decode_only_us": med(lambda: E.decode_bf16_split(p, blob, smd, out, None, stream))}
     r["speedup"] = r["unfused_us"] / r["fused_us"]
-    log(f"bf16 split 8192x8192 m={m}: fused {r['fused_us']:.1f} us, split decode + GEMM "
-        f"{r['unfused_us']:.1f} us, split decode alone {r['split_decode_only_us']:.1f} us")
+    # the same weights in tile order (exponents and sign+mantissa bytes), chunks
+    # of 16 rows x Ct columns (a tensor alone must fill the GPU with its chunks)
+    for Ct in (512, 1024, 2048):
+        e_t, sm_t = E.tile_order(e, rows, cols, Ct), E.tile_order(sm, rows, cols, Ct)
+        bt = E.encode_batch([dict(kind=E.KIND_BF16EXP | E.LAYOUT_TILES, rows=rows, cols=cols,
+                                  symbols=e_t, chunk_symbols=16 * Ct)])
+        pt = E.plan(bt.tensors, bt.freq, bt.chunks, bt.blob.size)
+        blob_t = torch.from_numpy(bt.blob).to(dev)
+        sm_td = torch.from_numpy(sm_t).to(dev)
+        n_ws = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(pt.handle, m))
+        raw = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
+        ws = raw[(-raw.data_ptr()) % 256:][:n_ws]
+        r[f"tiles_{Ct}_fused_us"] = med(lambda: E.decode_gemm_tiles_bf16_split(
+            pt, blob_t, sm_td, [X], [Y], None, stream, ws))
+        pt.close()
+    log(f"bf16 split 8192x8192 m={m}: fused {r['fused_us']:.1f} us (tile order, 512 / 1024 / "
+        f"2048 columns per chunk: {r['tiles_512_fused_us']:.1f} / {r['tiles_1024_fused_us']:.1f} "
+        f"/ {r['tiles_2048_fused_us']:.1f} us), split decode + GEMM {r['unfused_us']:.1f} us, "
+        f"split decode alone {r['split_decode_only_us']:.1f} us")
     p.close()
     return r
 

@@ -121,6 +121,8 @@ def lib():
             "entq_tile_order": (c.c_int, [vp, c.c_uint32, c.c_uint32, c.c_uint32, vp, c.c_int]),
             "entq_decode_gemm_tiles_workspace_bytes": (u64, [vp, c.c_int]),
             "entq_decode_gemm_tiles": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp, vp]),
+            "entq_decode_gemm_tiles_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp,
+                                                            vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -143,7 +145,7 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
             "entq_build_freq_device", "entq_decode_gemm_workspace_bytes",
             "entq_decode_gemm_static", "entq_tile_order", "entq_decode_gemm_tiles_workspace_bytes",
-            "entq_decode_gemm_tiles"]
+            "entq_decode_gemm_tiles", "entq_decode_gemm_tiles_bf16_split"]
 
 
 def _str(status: int) -> str:
@@ -438,6 +440,24 @@ def tile_order(codes: np.ndarray, rows: int, cols: int, chunk_cols: int,
     return out
 
 
+def _tiles_workspace(p: Plan, m: int, workspace, stream):
+    """The workspace of the tiled product (packed activations, partial sums):
+    the given one after its checks, or one allocated here."""
+    import torch
+    need = int(lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, int(m))) if p.handle.value \
+        else 0
+    if workspace is None:
+        if need:
+            raw = torch.empty(need + 256, dtype=torch.uint8, device=p.workspace.device)
+            shift = (-raw.data_ptr()) % 256
+            workspace = raw[shift:shift + need]
+            if stream is not None:
+                workspace.record_stream(stream)  # allocated here, used on another stream
+    else:
+        _device_buffer(p, "workspace", workspace, need, elem_size=1)
+    return workspace, (workspace.numel() if workspace is not None else 0)
+
+
 def decode_gemm_tiles(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None,
                       workspace=None):
     """decode_gemm for a plan of tile-ordered tensors (entq_decode_gemm_tiles):
@@ -450,23 +470,29 @@ def decode_gemm_tiles(p: Plan, compressed, scales, xs, ys, chunk_status=None, st
     _blob_buffer(p, "compressed", compressed)
     _device_buffer(p, "scales", scales, p.scale_rows, dtypes=(torch.float32,))
     _status_buffer(p, chunk_status)
-    need = int(lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, int(m))) if p.handle.value \
-        else 0
-    if workspace is None:
-        if need:
-            raw = torch.empty(need + 256, dtype=torch.uint8, device=p.workspace.device)
-            shift = (-raw.data_ptr()) % 256
-            workspace = raw[shift:shift + need]
-            if stream is not None:
-                workspace.record_stream(stream)  # allocated here, used on another stream
-    else:
-        _device_buffer(p, "workspace", workspace, need, elem_size=1)
-    wsb = workspace.numel() if workspace is not None else 0
+    ws, wsb = _tiles_workspace(p, m, workspace, stream)
     st = lib().entq_decode_gemm_tiles(p.handle, _ptr(compressed), _ptr(scales) or None,
                                       _ptr(io) if len(xs) else None, int(m),
-                                      _ptr(workspace) if workspace is not None else None,
-                                      int(wsb), _ptr(chunk_status) or None, _stream(stream))
+                                      _ptr(ws) if ws is not None else None, int(wsb),
+                                      _ptr(chunk_status) or None, _stream(stream))
     _check(st, "entq_decode_gemm_tiles")
+
+
+def decode_gemm_tiles_bf16_split(p: Plan, exp_stream, signmant, xs, ys, chunk_status=None,
+                                 stream=None, workspace=None):
+    """decode_gemm_tiles for tile-ordered BF16 exponent streams: signmant (1-byte
+    elements, at least out_elems) holds the sign+mantissa bytes in the same
+    tile order as the exponents."""
+    io, m = _gemm_io(p, xs, ys)
+    _blob_buffer(p, "exp_stream", exp_stream)
+    _device_buffer(p, "signmant", signmant, p.out_elems, elem_size=1)
+    _status_buffer(p, chunk_status)
+    ws, wsb = _tiles_workspace(p, m, workspace, stream)
+    st = lib().entq_decode_gemm_tiles_bf16_split(p.handle, _ptr(exp_stream), _ptr(signmant),
+                                                 _ptr(io) if len(xs) else None, int(m),
+                                                 _ptr(ws) if ws is not None else None, int(wsb),
+                                                 _ptr(chunk_status) or None, _stream(stream))
+    _check(st, "entq_decode_gemm_tiles_bf16_split")
 
 
 def decode_bf16_split(p: Plan, exp_stream, signmant, out, chunk_status=None, stream=None):

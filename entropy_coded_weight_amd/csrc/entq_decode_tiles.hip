@@ -93,11 +93,15 @@ __device__ __forceinline__ uint32_t dequant2_lane(uint32_t d, float scale) {
 // 8,192-column chunks, reading X in its own layout: m = 1, 2, 4: 356.0,
 // 358.5, 363.7 us, m = 16 419.8 us, m = 64 1,549 us; from the packed copy:
 // m = 2 .. 16 336-343 us, m = 64 539 us (the copy included).
-template <int MT, bool E4M3, bool PRIO>
+// SPLIT: BF16 weights from a coded exponent stream and raw sign+mantissa
+// bytes, both in tile order (no scales).
+template <int MT, bool E4M3, bool SPLIT, bool PRIO>
 __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__restrict__ blob,
                                            const uint2 *T, uint16_t *ring_lds, uint32_t lane,
-                                           const float *__restrict__ scales, const TileTensor &gt,
-                                           uint32_t m, Prio &pr, int32_t *__restrict__ status) {
+                                           const float *__restrict__ scales,
+                                           const uint8_t *__restrict__ signmant,
+                                           const TileTensor &gt, uint32_t m, Prio &pr,
+                                           int32_t *__restrict__ status) {
     const uint8_t *region = blob + ch.byte_offset;
     uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
     Stream s;
@@ -107,7 +111,9 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
     const uint64_t k = (ch.out_elem - gt.out0) / (16ull * C);
     const uint32_t band = (uint32_t)(k / gt.n_cc), cc = (uint32_t)(k % gt.n_cc);
     const uint32_t r16 = lane & 15;                  // weight row in the band; activation row
-    const float scale = scales[gt.row0 + 16ull * band + r16];
+    const float scale = SPLIT ? 0.f : scales[gt.row0 + 16ull * band + r16];
+    // split: this lane's sign+mantissa bytes, stream positions 64 s + l of each tile
+    const uint8_t *smc = SPLIT ? signmant + ch.out_elem + lane : nullptr;
     // activations: a uniform base and 32-bit byte offsets (a packed copy
     // holds 32 x groups x cols bytes), so the loads need no 64-bit address
     // registers per group
@@ -131,6 +137,14 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
 #pragma unroll
         for (int g = 0; g < MT; ++g)  // (rows m and beyond are zeros in the copy)
             a[g] = *reinterpret_cast<const uint2 *>(xb + (xoff + (t * MT + g) * 512u));
+        uint32_t sm0 = 0, sm1 = 0, sm2 = 0, sm3 = 0;
+        if (SPLIT) {
+            const uint8_t *sp = smc + 256ull * t;
+            sm0 = sp[0];
+            sm1 = sp[64];
+            sm2 = sp[128];
+            sm3 = sp[192];
+        }
         const uint32_t e0 = tile_step(x, s.pos, T, lane);
         const uint32_t e1 = tile_step(x, s.pos, T, lane);
         const uint32_t e2 = tile_step(x, s.pos, T, lane);
@@ -138,7 +152,12 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
         // codes of columns +0, +1 in bytes 1 and 3, then of +2, +3
         const uint32_t d0 = __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
         const uint32_t d1 = __builtin_amdgcn_perm(e3, e2, 0x070C030Cu);
-        const uint2 w = make_uint2(dequant2_lane<E4M3>(d0, scale), dequant2_lane<E4M3>(d1, scale));
+        uint2 w;
+        if (SPLIT)  // per 16-bit half: exponent << 8 | sign+mantissa, then bf16
+            w = make_uint2(merge2((d0 & 0xFF00FF00u) | sm0 | (sm1 << 16)),
+                           merge2((d1 & 0xFF00FF00u) | sm2 | (sm3 << 16)));
+        else
+            w = make_uint2(dequant2_lane<E4M3>(d0, scale), dequant2_lane<E4M3>(d1, scale));
 #pragma unroll
         for (int g = 0; g < MT; ++g)
             acc[g] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
@@ -173,13 +192,13 @@ __device__ __forceinline__ void tile_chunk(const DevChunk &ch, const uint8_t *__
 // amdgpu_waves_per_eu(8): at most 64 vector registers per lane, so that two
 // 16-wave workgroups share a CU also with four 16-row groups of activations
 // (the compiler would otherwise take 78 there and halve the waves).
-template <int MT, bool PRIO>
+template <int MT, bool PRIO, bool SPLIT>
 __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS
 __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
     const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
     const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks,
     const uint8_t *__restrict__ blob, const float *__restrict__ scales,
-    int32_t *__restrict__ status, TileArgs args) {
+    const uint8_t *__restrict__ signmant, int32_t *__restrict__ status, TileArgs args) {
     __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
 
@@ -203,12 +222,15 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
     }
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
-        if (e4m3)
-            tile_chunk<MT, true, PRIO>(ch, blob, T, RING[wave], lane, scales, gt, args.m, pr,
-                                       status);
+        if (SPLIT)
+            tile_chunk<MT, false, true, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant, gt,
+                                              args.m, pr, status);
+        else if (e4m3)
+            tile_chunk<MT, true, false, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant, gt,
+                                              args.m, pr, status);
         else
-            tile_chunk<MT, false, PRIO>(ch, blob, T, RING[wave], lane, scales, gt, args.m, pr,
-                                        status);
+            tile_chunk<MT, false, false, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant,
+                                               gt, args.m, pr, status);
     }
 }
 
@@ -238,19 +260,33 @@ __global__ __launch_bounds__(256) void reduce_partials(ReduceArgs args) {
     rt.y[mrow * rt.ldy + r] = sum;
 }
 
-template <int MT>
+template <int MT, bool SPLIT>
 void launch_tiles_mt(bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
-                     const uint8_t *blob, const float *scales, int32_t *status,
-                     const TileArgs &args) {
+                     const uint8_t *blob, const float *scales, const uint8_t *signmant,
+                     int32_t *status, const TileArgs &args) {
     const dim3 block(kThreads);
     if (prio)
-        hipLaunchKernelGGL((decode_tile_gemm<MT, true>), grid, block, 0, st, plan->d_tables,
-                           plan->d_tensors, plan->d_chunks, plan->d_tasks, blob, scales, status,
-                           args);
+        hipLaunchKernelGGL((decode_tile_gemm<MT, true, SPLIT>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           scales, signmant, status, args);
     else
-        hipLaunchKernelGGL((decode_tile_gemm<MT, false>), grid, block, 0, st, plan->d_tables,
-                           plan->d_tensors, plan->d_chunks, plan->d_tasks, blob, scales, status,
-                           args);
+        hipLaunchKernelGGL((decode_tile_gemm<MT, false, SPLIT>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           scales, signmant, status, args);
+}
+
+template <bool SPLIT>
+void launch_tiles(int groups, bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
+                  const uint8_t *blob, const float *scales, const uint8_t *signmant,
+                  int32_t *status, const TileArgs &args) {
+    if (groups == 1)
+        launch_tiles_mt<1, SPLIT>(prio, grid, st, plan, blob, scales, signmant, status, args);
+    else if (groups == 2)
+        launch_tiles_mt<2, SPLIT>(prio, grid, st, plan, blob, scales, signmant, status, args);
+    else if (groups == 3)
+        launch_tiles_mt<3, SPLIT>(prio, grid, st, plan, blob, scales, signmant, status, args);
+    else
+        launch_tiles_mt<4, SPLIT>(prio, grid, st, plan, blob, scales, signmant, status, args);
 }
 
 uint64_t part_bytes(const HostTensor &h, int m) {
@@ -273,14 +309,17 @@ uint64_t tiles_workspace_bytes(const entq_plan_t *plan, int m) {
     return total;
 }
 
-entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, int m) {
+entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, int m,
+                             bool split) {
     if (!plan || plan->adaptive || !io || m < 1 || m > (int)kTileM * kTileMaxGroups ||
         plan->n_tensors > kTileMaxTensors || plan->n_tasks > 0x7FFFFFFF)
         return ENTQ_EINVAL;
     for (int t = 0; t < plan->n_tensors; ++t) {
         const HostTensor &h = plan->host_tensors[(size_t)t];
         if (h.n_symbols == 0) continue;
-        if (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3) return ENTQ_EINVAL;
+        if (split ? h.kind != ENTQ_SYM_BF16EXP
+                  : (h.kind != ENTQ_SYM_INT8 && h.kind != ENTQ_SYM_E4M3))
+            return ENTQ_EINVAL;
         if (!h.tiles) return ENTQ_EINVAL;  // row-major symbols: entq_decode_gemm
         // chunks of 16 whole rows x C columns, C a multiple of 16 dividing cols
         if (h.rows % 16 || h.chunk_symbols % kBlockSyms) return ENTQ_EINVAL;
@@ -293,27 +332,13 @@ entq_status check_tiles_args(const entq_plan_t *plan, const entq_gemm_io *io, in
     return ENTQ_OK;
 }
 
-}  // namespace
-}  // namespace entq
-
-extern "C" {
-
-uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m) {
-    if (!plan || m < 1 || m > (int)entq::kTileM * entq::kTileMaxGroups) return 0;
-    return entq::tiles_workspace_bytes(plan, m);
-}
-
-entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compressed,
-                                   const float *d_scales, const entq_gemm_io *io, int m,
-                                   void *d_workspace, uint64_t workspace_bytes,
-                                   int32_t *d_chunk_status, void *stream) {
-    using namespace entq;
-    entq_status st = check_tiles_args(plan, io, m);
-    if (st != ENTQ_OK) return st;
-    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
-    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+// Both entry points: checks done, the pack, product and reduction enqueued.
+entq_status run_tiles(const entq_plan_t *plan, const void *d_compressed, const float *d_scales,
+                      const uint8_t *d_signmant, const entq_gemm_io *io, int m,
+                      void *d_workspace, uint64_t workspace_bytes, int32_t *d_chunk_status,
+                      void *stream) {
     const uint64_t need = tiles_workspace_bytes(plan, m);
-    if (need && !d_workspace) return ENTQ_EWORKSPACE;  // (need > 0 for any tensor)
+    if (need && !d_workspace) return ENTQ_EWORKSPACE;
     if (d_workspace && (uintptr_t)d_workspace % 256) return ENTQ_EALIGN;
     if (workspace_bytes < need) return ENTQ_EWORKSPACE;
     if (plan->n_tasks == 0) return ENTQ_OK;
@@ -359,17 +384,49 @@ entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compre
     const uint8_t *b = static_cast<const uint8_t *>(d_compressed);
     const int r = launch_pack_activations(plan, io, m, pack_off, ws, stream);
     if (r != ENTQ_OK) return (entq_status)r;
-    if (groups == 1)
-        launch_tiles_mt<1>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
-    else if (groups == 2)
-        launch_tiles_mt<2>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
-    else if (groups == 3)
-        launch_tiles_mt<3>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+    if (d_signmant)
+        launch_tiles<true>(groups, prio, grid, s, plan, b, d_scales, d_signmant, d_chunk_status,
+                           args);
     else
-        launch_tiles_mt<4>(prio, grid, s, plan, b, d_scales, d_chunk_status, args);
+        launch_tiles<false>(groups, prio, grid, s, plan, b, d_scales, d_signmant,
+                            d_chunk_status, args);
     if (red.n_tensors)
         hipLaunchKernelGGL(reduce_partials, dim3((unsigned)red_blocks), dim3(256), 0, s, red);
     return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
+}  // namespace
+}  // namespace entq
+
+extern "C" {
+
+uint64_t entq_decode_gemm_tiles_workspace_bytes(const entq_plan_t *plan, int m) {
+    if (!plan || m < 1 || m > (int)entq::kTileM * entq::kTileMaxGroups) return 0;
+    return entq::tiles_workspace_bytes(plan, m);
+}
+
+entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compressed,
+                                   const float *d_scales, const entq_gemm_io *io, int m,
+                                   void *d_workspace, uint64_t workspace_bytes,
+                                   int32_t *d_chunk_status, void *stream) {
+    entq_status st = entq::check_tiles_args(plan, io, m, false);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_compressed || !d_scales)) return ENTQ_EINVAL;
+    if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
+    return entq::run_tiles(plan, d_compressed, d_scales, nullptr, io, m, d_workspace,
+                           workspace_bytes, d_chunk_status, stream);
+}
+
+entq_status entq_decode_gemm_tiles_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
+                                              const uint8_t *d_signmant, const entq_gemm_io *io,
+                                              int m, void *d_workspace,
+                                              uint64_t workspace_bytes, int32_t *d_chunk_status,
+                                              void *stream) {
+    entq_status st = entq::check_tiles_args(plan, io, m, true);
+    if (st != ENTQ_OK) return st;
+    if (plan->n_chunks && (!d_exp_stream || !d_signmant)) return ENTQ_EINVAL;
+    return entq::run_tiles(plan, d_exp_stream, nullptr, d_signmant, io, m, d_workspace,
+                           workspace_bytes, d_chunk_status, stream);
 }
 
 }  // extern "C"

@@ -101,7 +101,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
         if (kind > ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
         if (td.kind & ENTQ_LAYOUT_TILES) {
             // 16-row bands of chunk_symbols / 16 columns, whole 16 x 16 tiles
-            if (adaptive || kind == ENTQ_SYM_BF16EXP) return ENTQ_EINVAL;
+            if (adaptive) return ENTQ_EINVAL;
             if (td.rows % 16 || td.chunk_symbols % entq::kBlockSyms) return ENTQ_EINVAL;
             if (td.cols % (td.chunk_symbols / 16)) return ENTQ_EINVAL;
         }

@@ -101,12 +101,13 @@ typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
 #define ENTQ_CHUNK_BAD_TABLE 3  /* (per-chunk tables) the chunk's table does not sum to 4096 */
 
 /* A tensor whose symbols are in the library's tile order (entq_tile_order)
- * carries this flag in its kind: ENTQ_SYM_INT8 | ENTQ_LAYOUT_TILES, or E4M3.
- * The plan then requires rows a multiple of 16, chunk_symbols a multiple of
- * 256 and chunk_symbols / 16 dividing cols (else ENTQ_EINVAL); such tensors
- * go to entq_decode_gemm_tiles (or entq_decode with ENTQ_OUT_CODES, which
- * returns the codes in tile order) and are refused by the row-major calls
- * (ENTQ_OUT_BF16, entq_decode_gemm*). */
+ * carries this flag in its kind: ENTQ_SYM_INT8 | ENTQ_LAYOUT_TILES, or E4M3,
+ * or BF16EXP. The plan then requires rows a multiple of 16, chunk_symbols a
+ * multiple of 256 and chunk_symbols / 16 dividing cols, and shared tables
+ * (else ENTQ_EINVAL); such tensors go to entq_decode_gemm_tiles and
+ * entq_decode_gemm_tiles_bf16_split (or to entq_decode with ENTQ_OUT_CODES,
+ * which returns the codes in tile order) and are refused by the row-major
+ * calls (ENTQ_OUT_BF16, entq_decode_bf16_split, entq_decode_gemm*). */
 #define ENTQ_LAYOUT_TILES 0x100u
 
 /* One tensor of a batch (40 bytes). rows x cols row-major; n_symbols must be
@@ -401,6 +402,19 @@ entq_status entq_decode_gemm_tiles(const entq_plan_t *plan, const void *d_compre
                                    const float *d_scales, const entq_gemm_io *io, int m,
                                    void *d_workspace, uint64_t workspace_bytes,
                                    int32_t *d_chunk_status, void *stream);
+
+/* The same product for BF16 weights stored as a coded exponent stream plus
+ * raw sign+mantissa bytes [DFloat11 write-up, "Formato DFloat11"], both in
+ * tile order: the tensors are ENTQ_SYM_BF16EXP | ENTQ_LAYOUT_TILES, d_signmant
+ * holds the tile-ordered sign+mantissa bytes indexed like the exponent
+ * symbols (out_elem_offset + stream position; any alignment), W_t is the
+ * original bf16 bit for bit. Other arguments, workspace and requirements as
+ * for entq_decode_gemm_tiles. */
+entq_status entq_decode_gemm_tiles_bf16_split(const entq_plan_t *plan, const void *d_exp_stream,
+                                              const uint8_t *d_signmant, const entq_gemm_io *io,
+                                              int m, void *d_workspace,
+                                              uint64_t workspace_bytes, int32_t *d_chunk_status,
+                                              void *stream);
 
 /* ---- On-device encoder (one wavefront per chunk; same regions as the
  * host encoder, byte for byte) ----

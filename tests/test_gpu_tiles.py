@@ -279,3 +279,69 @@ def test_lm_head_in_tile_order_every_row(E):
     ys = _run(E, p, blob, scales, [x], specs)
     W = _oracle_weights(b, tiled)
     assert oracle_rows.check_product(ys[0], x, W[0]) == specs[0]["rows"]
+
+
+# ---- BF16 exponent streams in tile order (entq_decode_gemm_tiles_bf16_split) ----
+
+def _split_tiled(E, w, rows, cols, C):
+    """bf16 words w [rows, cols]: exponent and sign+mantissa bytes, both in
+    tile order; the container, plan and device buffers. The oracle's decode
+    of the container, put back in row-major order and merged, must be w."""
+    import torch
+    e, sm = oracle.bf16_split(w.ravel())
+    e_t = E.tile_order(e, rows, cols, C)
+    sm_t = E.tile_order(sm, rows, cols, C)
+    spec = dict(kind=E.KIND_BF16EXP | E.LAYOUT_TILES, rows=rows, cols=cols, symbols=e_t,
+                chunk_symbols=16 * C)
+    b = E.encode_batch([spec])
+    p = E.plan(b.tensors, b.freq, b.chunks, b.blob.size)
+    sym, st = oracle.decode_tensor(b.blob, oracle_rows.desc_of(b.chunks), b.freq[0], rows * cols)
+    assert (st == 0).all()
+    merged = oracle.bf16_merge(oracle.untile(sym, rows, cols, C).ravel(),
+                               oracle.untile(sm_t, rows, cols, C).ravel())
+    assert np.array_equal(merged.reshape(rows, cols), w)
+    return p, torch.from_numpy(b.blob).cuda(), torch.from_numpy(sm_t).cuda()
+
+
+def _run_split(E, p, blob, sm, x, rows, workspace=None):
+    import torch
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    y = torch.full((x.shape[0] + 1, rows), float("nan"), dtype=torch.float32, device="cuda")
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode_gemm_tiles_bf16_split(p, blob, sm, [xd], [y[:x.shape[0]]], status,
+                                   workspace=workspace)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    out = y.cpu().numpy()
+    assert np.isnan(out[-1]).all()  # nothing written past m rows
+    return out[:-1]
+
+
+@pytest.mark.parametrize("rows,cols,C", [(48, 768, 256), (32, 512, 512), (64, 1792, 256)])
+def test_bf16_split_one_hot_returns_the_source_weights(E, rows, cols, C):
+    rng = np.random.default_rng(rows + cols)
+    w = rng.integers(0, 1 << 16, size=rows * cols, dtype=np.uint64).astype(np.uint16)
+    w[(w & 0x7F80) == 0x7F80] &= 0xBFFF  # finite weights, so that 1.0 * w is w
+    w[w == 0x8000] = 0  # a -0 weight would come out +0 (+0 + -0 = +0 in the sums)
+    w = w.reshape(rows, cols)
+    p, blob, sm = _split_tiled(E, w, rows, cols, C)
+    for m in (1, 3, 16, 40):
+        _say(f"bf16 split in tile order, {rows}x{cols}, C={C}, one-hot, m={m}")
+        c = rng.choice(cols, m, replace=False)
+        x = np.zeros((m, cols), np.float32)
+        x[np.arange(m), c] = 1.0
+        y = _run_split(E, p, blob, sm, x, rows)
+        assert np.array_equal(y.view(np.uint32), _f32(w[:, c]).T.view(np.uint32)), m
+
+
+def test_bf16_split_8192x8192_every_row(E):
+    rows = cols = 8192
+    w = synth.bf16_weights(rows, cols)[0]["bf16"].reshape(rows, cols)
+    p, blob, sm = _split_tiled(E, w, rows, cols, 2048)
+    rng = np.random.default_rng(47)
+    for m in (16, 1):
+        _say(f"bf16 split 8192x8192 in tile order, m = {m}, every row")
+        x = _f32(((rng.standard_normal((m, cols)) * 0.5).astype(np.float32).view(np.uint32)
+                  >> 16).astype(np.uint16))
+        y = _run_split(E, p, blob, sm, x, rows)
+        assert oracle_rows.check_product(y, x, w) == rows

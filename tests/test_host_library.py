@@ -211,8 +211,8 @@ def test_plan_rejects_bad_inputs(E):
 
 def test_plan_checks_the_tile_layout(E):
     """A tensor marked ENTQ_LAYOUT_TILES needs rows in 16-row bands, whole
-    16 x 16 tiles per chunk and a chunk width dividing the columns; exponent
-    streams and per-chunk tables do not take it."""
+    16 x 16 tiles per chunk and a chunk width dividing the columns (exponent
+    streams take it too)."""
     def tiled(rows, cols, C, kind=E.KIND_INT8, seed=11):
         sp = synth.random_int8_tensor(rows, cols, 1.5, seed, 16 * C)
         sp["kind"] = kind | E.LAYOUT_TILES
@@ -225,7 +225,7 @@ def test_plan_checks_the_tile_layout(E):
     b = tiled(32, 512, 256)
     t = b.tensors.copy()
     t[0]["kind"] = E.KIND_BF16EXP | E.LAYOUT_TILES
-    assert _try_plan(E, t, b.freq, b.chunks, b.blob.size) == -1
+    assert _try_plan(E, t, b.freq, b.chunks, b.blob.size, ws_bytes=1000) == -5
 
 
 def test_plan_rejects_overlapping_outputs(E):
