@@ -117,3 +117,57 @@ def test_static_fused_product_graph_replays(E, m):
         assert (status.cpu().numpy() == 0).all()
     del g
     p.close()
+
+
+def test_tiled_fused_product_graph_replays(E):
+    """entq_decode_gemm_tiles with its workspace given (activation copy,
+    product and the column chunks' reduction: three kernels, no memset)
+    captured and replayed, new activations between replays."""
+    import torch
+    specs = _specs(fused_only=True)
+    C = {0: 256, 1: 512}
+    tiled = [dict(sp, symbols=E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C[i]),
+                  chunk_symbols=16 * C[i], kind=sp["kind"] | E.LAYOUT_TILES)
+             for i, sp in enumerate(specs)]
+    b, p, blob, scales = _setup(E, tiled)
+    rng = np.random.default_rng(4)
+    m = 24
+    n = int(E.lib().entq_decode_gemm_tiles_workspace_bytes(p.handle, m))
+    raw = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
+    ws = raw[(-raw.data_ptr()) % 256:][:n]
+
+    def fill_activations(xs):
+        for x in xs:
+            bits = rng.integers(0, 65536, tuple(x.shape), dtype=np.uint64).astype(np.uint16)
+            bits &= np.uint16(0xBFFF)  # finite bf16 values
+            x.copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda())
+
+    xs = [torch.empty(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
+    ys = [torch.empty(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
+    ye = [torch.empty_like(y) for y in ys]
+    status = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    fill_activations(xs)
+    _say("eager tiled product")
+    E.decode_gemm_tiles(p, blob, scales, xs, ye, status, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("capture")
+    with torch.cuda.graph(g):
+        E.decode_gemm_tiles(p, blob, scales, xs, ys, status, workspace=ws)
+    for r in range(3):
+        if r:
+            fill_activations(xs)
+            E.decode_gemm_tiles(p, blob, scales, xs, ye, status, workspace=ws)
+        for y in ys:
+            y.fill_(float("nan"))
+        status.fill_(-7)
+        torch.cuda.synchronize()
+        want = [y.cpu().numpy().view(np.uint32).copy() for y in ye]
+        _say(f"replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(len(specs)):
+            assert np.array_equal(ys[t].cpu().numpy().view(np.uint32), want[t]), (r, t)
+        assert (status.cpu().numpy() == 0).all()
+    del g
+    p.close()
