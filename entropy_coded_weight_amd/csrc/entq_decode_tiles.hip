@@ -234,6 +234,131 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
     }
 }
 
+// ---------------------------------------------------------------------------
+// decode of tile-ordered tensors into their row-major outputs
+// ---------------------------------------------------------------------------
+//
+// The same walk over a chunk's tiles, each lane storing its 4 consecutive
+// outputs of one row per tile (codes: 4 bytes; bf16: 8 bytes; a wave's
+// store covers 16 rows x 16 columns), so that a tensor kept in tile order
+// for the fused product also decodes to the ordinary row-major weights.
+template <int MODE, bool E4M3, bool PRIO>
+__device__ __forceinline__ void tile_decode_chunk(const DevChunk &ch,
+                                                  const uint8_t *__restrict__ blob,
+                                                  const uint2 *T, uint16_t *ring_lds,
+                                                  uint32_t lane, const float *__restrict__ scales,
+                                                  const uint8_t *__restrict__ signmant,
+                                                  const TileTensor &gt, void *__restrict__ out,
+                                                  Prio &pr, int32_t *__restrict__ status) {
+    const uint8_t *region = blob + ch.byte_offset;
+    uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
+    Stream s;
+    ring_open(s, region + kStateBytes, lds_addr(ring_lds), ch.n_words, lane);
+    const uint32_t C = gt.chunk_cols;
+    const uint64_t k = (ch.out_elem - gt.out0) / (16ull * C);
+    const uint32_t band = (uint32_t)(k / gt.n_cc), cc = (uint32_t)(k % gt.n_cc);
+    const uint32_t r16 = lane & 15;
+    const uint64_t cols = (uint64_t)gt.n_cc * C;
+    const float scale = (MODE == kModeBf16) ? scales[gt.row0 + 16ull * band + r16] : 0.f;
+    const uint8_t *smc = (MODE == kModeSplit) ? signmant + ch.out_elem + lane : nullptr;
+    // this lane's first output: row 16 band + r16, column cC + 4 (lane / 16)
+    const uint64_t o0 = gt.out0 + (16ull * band + r16) * cols + (uint64_t)cc * C + 4u * (lane >> 4);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states, scale, first ring units
+    s.landed = s.issued;
+    ring_horizon(s);
+    const uint32_t blocks = ch.n_symbols / kBlockSyms;
+    for (uint32_t t = 0; t < blocks; ++t) {
+        if (PRIO) pr.tick();
+        if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
+        uint32_t sm0 = 0, sm1 = 0, sm2 = 0, sm3 = 0;
+        if (MODE == kModeSplit) {
+            const uint8_t *sp = smc + 256ull * t;
+            sm0 = sp[0];
+            sm1 = sp[64];
+            sm2 = sp[128];
+            sm3 = sp[192];
+        }
+        const uint32_t e0 = tile_step(x, s.pos, T, lane);
+        const uint32_t e1 = tile_step(x, s.pos, T, lane);
+        const uint32_t e2 = tile_step(x, s.pos, T, lane);
+        const uint32_t e3 = tile_step(x, s.pos, T, lane);
+        const uint64_t o = o0 + 16ull * t;
+        if (MODE == kModeCodes) {
+            // the four symbols (byte 3 of each entry) in column order
+            const uint32_t v = __builtin_amdgcn_perm(e1, e0, 0x0C0C0703u) |
+                               __builtin_amdgcn_perm(e3, e2, 0x07030C0Cu);
+            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(out) + o) = v;
+        } else {
+            const uint32_t d0 = __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
+            const uint32_t d1 = __builtin_amdgcn_perm(e3, e2, 0x070C030Cu);
+            uint2 w;
+            if (MODE == kModeSplit)
+                w = make_uint2(merge2((d0 & 0xFF00FF00u) | sm0 | (sm1 << 16)),
+                               merge2((d1 & 0xFF00FF00u) | sm2 | (sm3 << 16)));
+            else
+                w = make_uint2(dequant2_lane<E4M3>(d0, scale), dequant2_lane<E4M3>(d1, scale));
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = w;
+        }
+    }
+    const uint64_t bad_state = __ballot(x != kStateLow);
+    if (status && lane == 0)
+        status[ch.status_index] = (ring_consumed(s) != s.nw) ? ENTQ_CHUNK_BAD_WORDS
+                                  : (bad_state ? ENTQ_CHUNK_BAD_STATE : ENTQ_CHUNK_OK);
+    wait_vm<0>();  // no global->LDS load may outlive the chunk
+}
+
+template <int MODE, bool PRIO>
+__global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_tiles_rowmajor(
+    const SlotEntry *__restrict__ tables, const DevTensor *__restrict__ tensors,
+    const DevChunk *__restrict__ chunks, const DevTask *__restrict__ tasks,
+    const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
+    const uint8_t *__restrict__ signmant, int32_t *__restrict__ status, TileArgs args) {
+    __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
+    __shared__ uint2 T[kProbScale];
+
+    const DevTask task = tasks[blockIdx.x];
+    const bool e4m3 = tensors[task.tensor].kind == ENTQ_SYM_E4M3;
+    const TileTensor &gt = args.t[task.tensor];
+    load_table(T, tables, task.tensor);
+    __syncthreads();
+
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
+    const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    Prio pr = {};
+    if (PRIO) {
+        uint32_t my_blocks = 0;
+        for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
+            my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
+        pr.start(my_blocks);
+    }
+    for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
+        const DevChunk ch = chunks[task.first_chunk + c];
+        if (MODE == kModeBf16 && e4m3)
+            tile_decode_chunk<MODE, true, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant,
+                                                gt, out, pr, status);
+        else
+            tile_decode_chunk<MODE, false, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant,
+                                                 gt, out, pr, status);
+    }
+}
+
+template <int MODE>
+void launch_tiles_rowmajor(bool prio, dim3 grid, hipStream_t st, const entq_plan_t *plan,
+                           const uint8_t *blob, void *out, const float *scales,
+                           const uint8_t *signmant, int32_t *status, const TileArgs &args) {
+    const dim3 block(kThreads);
+    if (prio)
+        hipLaunchKernelGGL((decode_tiles_rowmajor<MODE, true>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           out, scales, signmant, status, args);
+    else
+        hipLaunchKernelGGL((decode_tiles_rowmajor<MODE, false>), grid, block, 0, st,
+                           plan->d_tables, plan->d_tensors, plan->d_chunks, plan->d_tasks, blob,
+                           out, scales, signmant, status, args);
+}
+
 // Y of the tensors whose chunks split the columns: the column chunks'
 // partial sums added in column order, one thread per result.
 struct ReduceTensor {
@@ -396,6 +521,42 @@ entq_status run_tiles(const entq_plan_t *plan, const void *d_compressed, const f
 }
 
 }  // namespace
+}  // namespace entq
+
+namespace entq {
+
+int launch_tile_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
+                       const float *scales, const uint8_t *signmant, int32_t *status,
+                       void *stream) {
+    if (plan->n_tensors > kTileMaxTensors || plan->n_tasks > 0x7FFFFFFF) return ENTQ_EINVAL;
+    if (plan->n_tasks == 0) return ENTQ_OK;
+    TileArgs args = {};
+    for (int t = 0; t < plan->n_tensors; ++t) {
+        const HostTensor &h = plan->host_tensors[(size_t)t];
+        if (h.n_symbols == 0) continue;
+        TileTensor &g = args.t[t];
+        g.out0 = h.out_elem_offset;
+        g.row0 = h.scale_row_offset;
+        g.rows = h.rows;
+        g.chunk_cols = h.chunk_symbols / 16;
+        g.n_cc = h.cols / g.chunk_cols;
+    }
+    const bool prio = plan->n_chunks > plan->n_tasks;
+    const dim3 grid((unsigned)plan->n_tasks);
+    const hipStream_t st = (hipStream_t)stream;
+    const uint8_t *b = static_cast<const uint8_t *>(blob);
+    if (mode == kModeCodes)
+        launch_tiles_rowmajor<kModeCodes>(prio, grid, st, plan, b, out, scales, signmant, status,
+                                          args);
+    else if (mode == kModeBf16)
+        launch_tiles_rowmajor<kModeBf16>(prio, grid, st, plan, b, out, scales, signmant, status,
+                                         args);
+    else
+        launch_tiles_rowmajor<kModeSplit>(prio, grid, st, plan, b, out, scales, signmant, status,
+                                          args);
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
+}
+
 }  // namespace entq
 
 extern "C" {

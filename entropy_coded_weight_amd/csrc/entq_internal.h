@@ -116,6 +116,7 @@ struct entq_plan_s {
     void *host_staging;         // kept alive until destroy (async copy source)
     std::vector<entq::HostTensor> host_tensors;
     bool adaptive = false;      // chunk regions carry their own tables
+    bool mixed_layouts = false; // tile-ordered and row-major tensors together
     void *upload_done = nullptr;  // hipEvent_t recorded after the workspace upload
 };
 
@@ -148,6 +149,11 @@ int launch_pack_activations(const entq_plan_t *plan, const entq_gemm_io *io, int
 // non-null for BF16 exponent streams.
 constexpr int kGemvMaxRows = 4;
 constexpr int kGemvMaxTensors = 16;
+// The decode of a plan whose tensors are all in tile order, into their
+// row-major outputs (entq_decode_tiles.hip); mode as for launch_decode.
+int launch_tile_decode(const entq_plan_t *plan, int mode, const void *blob, void *out,
+                       const float *scales, const uint8_t *signmant, int32_t *status,
+                       void *stream);
 int launch_decode_gemv(const entq_plan_t *plan, const void *blob, const float *scales,
                        const uint8_t *signmant, const entq_gemm_io *io, int n_rows,
                        int32_t *status, void *stream);

@@ -94,6 +94,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     // ---- tensors
     uint64_t out_elems = 0, scale_rows = 0;
     uint32_t kinds_mask = 0;
+    int n_tiled = 0, n_nonempty = 0;
     for (int t = 0; t < n_tensors; ++t) {
         const entq_tensor_desc &td = tensors[t];
         if (td.kind & ~(0xFFu | ENTQ_LAYOUT_TILES)) return ENTQ_EINVAL;
@@ -104,6 +105,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
             if (adaptive) return ENTQ_EINVAL;
             if (td.rows % 16 || td.chunk_symbols % entq::kBlockSyms) return ENTQ_EINVAL;
             if (td.cols % (td.chunk_symbols / 16)) return ENTQ_EINVAL;
+            if (td.out_elem_offset % 16) return ENTQ_EINVAL;  // 16-byte output rows
         }
         if (td.chunk_symbols == 0 || td.chunk_symbols % entq::kLanes ||
             td.chunk_symbols > entq::kMaxChunkSymbols)
@@ -121,6 +123,8 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
         }
         kinds_mask |= 1u << kind;
         if (td.kind & ENTQ_LAYOUT_TILES) kinds_mask |= entq::kTilesBit;
+        n_tiled += (td.kind & ENTQ_LAYOUT_TILES) ? 1 : 0;
+        ++n_nonempty;
         if (td.out_elem_offset > UINT64_MAX - td.n_symbols) return ENTQ_EINVAL;
         out_elems = std::max(out_elems, td.out_elem_offset + td.n_symbols);
         scale_rows = std::max(scale_rows, td.scale_row_offset + td.rows);
@@ -335,6 +339,7 @@ entq_status plan_impl(const entq_tensor_desc *tensors, int n_tensors, const uint
     p->out_elems = out_elems;
     p->scale_rows = scale_rows;
     p->kinds_mask = kinds_mask;
+    p->mixed_layouts = n_tiled > 0 && n_tiled < n_nonempty;
     p->d_tables = reinterpret_cast<const entq::SlotEntry *>(ws + lay.tables);
     p->d_tensors = reinterpret_cast<const entq::DevTensor *>(ws + lay.tensors);
     p->d_chunks = reinterpret_cast<const entq::DevChunk *>(ws + lay.chunks);
@@ -397,10 +402,15 @@ entq_status entq_decode(const entq_plan_t *plan, const void *d_compressed, void 
     if ((uintptr_t)d_compressed % ENTQ_REGION_ALIGN || (uintptr_t)d_out % 16) return ENTQ_EALIGN;
     int mode = entq::kModeCodes;
     if (out_kind == ENTQ_OUT_BF16) {
-        if (plan->kinds_mask & ((1u << ENTQ_SYM_BF16EXP) | entq::kTilesBit)) return ENTQ_EINVAL;
+        if (plan->kinds_mask & (1u << ENTQ_SYM_BF16EXP)) return ENTQ_EINVAL;
         if (!d_scales) return ENTQ_EINVAL;
         if ((uintptr_t)d_scales % 4) return ENTQ_EALIGN;
         mode = entq::kModeBf16;
+    }
+    if (plan->kinds_mask & entq::kTilesBit) {  // row-major outputs of tile-ordered tensors
+        if (plan->mixed_layouts) return ENTQ_EINVAL;
+        return (entq_status)entq::launch_tile_decode(plan, mode, d_compressed, d_out, d_scales,
+                                                     nullptr, d_chunk_status, stream);
     }
     if (plan->adaptive)
         return (entq_status)entq::launch_decode_adaptive(plan, mode, d_compressed, d_out,
@@ -414,12 +424,18 @@ entq_status entq_decode_bf16_split(const entq_plan_t *plan, const void *d_exp_st
                                    const uint8_t *d_signmant, uint16_t *d_out,
                                    int32_t *d_chunk_status, void *stream) {
     if (!plan) return ENTQ_EINVAL;
-    if (plan->kinds_mask & ~(1u << ENTQ_SYM_BF16EXP)) return ENTQ_EINVAL;
+    if (plan->kinds_mask & ~((1u << ENTQ_SYM_BF16EXP) | entq::kTilesBit)) return ENTQ_EINVAL;
     if (plan->n_chunks == 0) return ENTQ_OK;
     if (!d_exp_stream || !d_signmant || !d_out) return ENTQ_EINVAL;
     if ((uintptr_t)d_exp_stream % ENTQ_REGION_ALIGN || (uintptr_t)d_out % 16 ||
         (uintptr_t)d_signmant % 16)
         return ENTQ_EALIGN;
+    if (plan->kinds_mask & entq::kTilesBit) {  // row-major outputs of tile-ordered tensors
+        if (plan->mixed_layouts) return ENTQ_EINVAL;
+        return (entq_status)entq::launch_tile_decode(plan, entq::kModeSplit, d_exp_stream, d_out,
+                                                     nullptr, d_signmant, d_chunk_status,
+                                                     stream);
+    }
     if (plan->adaptive)
         return (entq_status)entq::launch_decode_adaptive(plan, entq::kModeSplit, d_exp_stream,
                                                          d_out, nullptr, d_signmant,

@@ -24,8 +24,7 @@ def linear(p: Plan, compressed, scales, xs, ys, weights=None, chunk_status=None,
     """Y_t = X_t . W_t^T for every tensor t of the plan (xs[t]: device
     bfloat16 [m, >= cols]; ys[t]: device float32 [m, >= rows]; the same m for
     all). m <= FUSED_MAX_ROWS: decode_gemm_tiles when the plan's tensors are
-    in tile order, else decode_gemm (workspace as there). More rows (row-major
-    tensors only):
+    in tile order, else decode_gemm (workspace as there). More rows:
     the bf16 decode into `weights` (a device tensor of 2-byte elements, at
     least out_elems; allocated when None), then per tensor one library GEMM
     of the bf16 operands with fp32 accumulation and fp32 results, all on
@@ -39,9 +38,6 @@ def linear(p: Plan, compressed, scales, xs, ys, weights=None, chunk_status=None,
         fused = decode_gemm_tiles if tiles else decode_gemm
         fused(p, compressed, scales, xs, ys, chunk_status, stream, workspace)
         return
-    if tiles:
-        raise EntqError(EINVAL, "linear takes at most 64 rows on tensors in tile order (their "
-                                "bf16 decode is not row-major)")
     if p.adaptive:
         raise EntqError(EINVAL, "linear takes plans with per-tensor tables")
     if np.any((p.tensors["kind"] & 0xFF) == KIND_BF16EXP):

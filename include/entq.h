@@ -103,11 +103,13 @@ typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
 /* A tensor whose symbols are in the library's tile order (entq_tile_order)
  * carries this flag in its kind: ENTQ_SYM_INT8 | ENTQ_LAYOUT_TILES, or E4M3,
  * or BF16EXP. The plan then requires rows a multiple of 16, chunk_symbols a
- * multiple of 256 and chunk_symbols / 16 dividing cols, and shared tables
- * (else ENTQ_EINVAL); such tensors go to entq_decode_gemm_tiles and
- * entq_decode_gemm_tiles_bf16_split (or to entq_decode with ENTQ_OUT_CODES,
- * which returns the codes in tile order) and are refused by the row-major
- * calls (ENTQ_OUT_BF16, entq_decode_bf16_split, entq_decode_gemm*). */
+ * multiple of 256, chunk_symbols / 16 dividing cols, out_elem_offset a
+ * multiple of 16 and shared tables (else ENTQ_EINVAL). Such tensors go to
+ * entq_decode_gemm_tiles / entq_decode_gemm_tiles_bf16_split, and
+ * entq_decode / entq_decode_bf16_split write their ordinary row-major
+ * outputs (codes, bf16 or the source bf16) when every tensor of the plan is
+ * in tile order (a plan mixing the layouts: ENTQ_EINVAL there). The
+ * row-major fused calls (entq_decode_gemm*) refuse them. */
 #define ENTQ_LAYOUT_TILES 0x100u
 
 /* One tensor of a batch (40 bytes). rows x cols row-major; n_symbols must be
@@ -360,9 +362,7 @@ entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_e
  * 16 b + l % 16, column c C + 16 t + 4 (l / 16) + s. Only the order of the
  * symbols changes; the table, coder and container are as for any tensor:
  * encode the reordered symbols with chunk_symbols = 16 C and mark the tensor
- * ENTQ_LAYOUT_TILES. entq_decode on such a tensor returns its codes in tile
- * order (ENTQ_OUT_CODES); the bf16 output, whose scale rows assume row-major
- * order, is refused. */
+ * ENTQ_LAYOUT_TILES. */
 
 /* The symbols of one row-major tensor (codes, rows x cols bytes) in tile
  * order with chunk_cols = C columns per chunk, into out (rows x cols bytes,

@@ -97,23 +97,51 @@ def _mixed():
     return specs, (lambda sp: Cs[sp["name"]])
 
 
-def test_codes_decode_in_tile_order(E):
-    """The container is an ordinary one: entq_decode returns its codes in
-    tile order, equal to the oracle's tile order of the source codes."""
+def test_decode_writes_the_row_major_tensors(E):
+    """entq_decode of tile-ordered tensors writes their ordinary row-major
+    outputs: the source codes, and bf16 equal to the oracle's dequantisation
+    of the source codes, every element (and every chunk status 0)."""
     import torch
     specs, C_of = _mixed()
     tiled, b, p, blob, scales = _tiled(E, specs, C_of)
-    out = torch.empty(p.out_elems, dtype=torch.uint8, device="cuda")
-    E.decode(p, blob, out, E.OUT_CODES)
+    codes = torch.empty(p.out_elems, dtype=torch.uint8, device="cuda")
+    bf = torch.full((p.out_elems,), 0x5A5A, dtype=torch.int16, device="cuda")
+    st = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode(p, blob, codes, E.OUT_CODES, None, st)
+    E.decode(p, blob, bf, E.OUT_BF16, scales, st)
     torch.cuda.synchronize()
-    got = out.cpu().numpy()
+    assert (st.cpu().numpy() == 0).all()
+    got_c, got_b = codes.cpu().numpy(), bf.cpu().numpy().view(np.uint16)
     off = 0
-    for sp, ts in zip(specs, tiled):
+    for sp in specs:
         n = sp["rows"] * sp["cols"]
-        want = oracle.tile_order(np.ascontiguousarray(sp["symbols"]).view(np.uint8),
-                                 sp["rows"], sp["cols"], ts["C"])
-        assert np.array_equal(got[off:off + n], want), sp["name"]
+        src = np.ascontiguousarray(sp["symbols"]).view(np.uint8)
+        assert np.array_equal(got_c[off:off + n], src), sp["name"]
+        want = oracle.dequant_tensor(src, sp["rows"], sp["cols"], sp["kind"], sp["scales"])
+        assert np.array_equal(got_b[off:off + n], want), sp["name"]
         off += n
+
+
+def test_linear_beyond_64_rows_on_tiles(E):
+    """linear() on a tiled plan: the tiled product up to 64 rows, above that
+    the row-major bf16 decode and library GEMMs; both within the bound."""
+    import torch
+    from entropy_coded_weight_amd.linear import linear
+    specs, C_of = _mixed()
+    tiled, b, p, blob, scales = _tiled(E, specs, C_of)
+    W = _oracle_weights(b, tiled)
+    rng = np.random.default_rng(48)
+    for m in (64, 80):
+        _say(f"linear on tiles, m={m}")
+        xs_h = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+                     & np.uint16(0xBFFF)) for sp in specs]
+        xs = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs_h]
+        ys = [torch.full((m, sp["rows"]), float("nan"), dtype=torch.float32, device="cuda")
+              for sp in specs]
+        linear(p, blob, scales, xs, ys)
+        torch.cuda.synchronize()
+        for t, sp in enumerate(specs):
+            assert oracle_rows.check_product(ys[t].cpu().numpy(), xs_h[t], W[t]) == sp["rows"]
 
 
 def test_one_hot_activations_return_the_oracle_weights_exactly(E):
@@ -186,33 +214,31 @@ def test_results_are_reproducible_and_the_workspace_is_checked(E):
 
 
 def test_layouts_are_kept_apart(E):
-    """A tensor marked as tile-ordered goes to the tiled product only (codes
-    out of entq_decode too); a row-major one is refused by it."""
+    """Tile-ordered tensors are refused by the row-major fused calls, row-major
+    ones by the tiled call, and a plan mixing the two layouts by the decode."""
     import torch
     specs, C_of = _mixed()
     tiled, b, p, blob, scales = _tiled(E, specs, C_of)
     m = 2
     xs = [torch.zeros(m, sp["cols"], dtype=torch.bfloat16, device="cuda") for sp in specs]
     ys = [torch.zeros(m, sp["rows"], dtype=torch.float32, device="cuda") for sp in specs]
-    out = torch.empty(p.out_elems, dtype=torch.int16, device="cuda")
-    with pytest.raises(E.EntqError):
-        E.decode(p, blob, out, E.OUT_BF16, scales)
     with pytest.raises(E.EntqError):
         E.decode_gemm(p, blob, scales, xs, ys)
     with pytest.raises(E.EntqError):
         E.decode_gemm_static(p, blob, scales, xs, ys)
-    from entropy_coded_weight_amd.linear import linear
-    with pytest.raises(E.EntqError):  # more than 64 rows: would need the bf16 decode
-        linear(p, blob, scales, [torch.zeros(65, sp["cols"], dtype=torch.bfloat16,
-                                             device="cuda") for sp in specs],
-               [torch.zeros(65, sp["rows"], dtype=torch.float32, device="cuda")
-                for sp in specs])
     # the same codes, row-major, in chunks of the same size: refused by the tiled call
     rm = [dict(sp, chunk_symbols=16 * C_of(sp)) for sp in specs]
     b2 = E.encode_batch(rm)
     p2 = E.plan(b2.tensors, b2.freq, b2.chunks, b2.blob.size)
     with pytest.raises(E.EntqError):
         E.decode_gemm_tiles(p2, torch.from_numpy(b2.blob).cuda(), scales, xs, ys)
+    # one tensor in tile order, the others row-major: the decode refuses the plan
+    mixed = [tiled[0]] + rm[1:]
+    b3 = E.encode_batch(mixed)
+    p3 = E.plan(b3.tensors, b3.freq, b3.chunks, b3.blob.size)
+    out = torch.empty(p3.out_elems, dtype=torch.int16, device="cuda")
+    with pytest.raises(E.EntqError):
+        E.decode(p3, torch.from_numpy(b3.blob).cuda(), out, E.OUT_BF16, scales)
 
 
 def test_corrupt_chunks_report_the_decodes_status(E):
@@ -332,6 +358,23 @@ def test_bf16_split_one_hot_returns_the_source_weights(E, rows, cols, C):
         x[np.arange(m), c] = 1.0
         y = _run_split(E, p, blob, sm, x, rows)
         assert np.array_equal(y.view(np.uint32), _f32(w[:, c]).T.view(np.uint32)), m
+
+
+def test_bf16_split_decode_rebuilds_the_source(E):
+    """entq_decode_bf16_split of tile-ordered exponent streams writes the
+    source bf16 in row-major order, every word."""
+    import torch
+    rng = np.random.default_rng(49)
+    rows, cols, C = 64, 1792, 256
+    w = rng.integers(0, 1 << 16, size=rows * cols, dtype=np.uint64).astype(np.uint16)
+    w = w.reshape(rows, cols)
+    p, blob, sm = _split_tiled(E, w, rows, cols, C)
+    out = torch.empty(rows * cols, dtype=torch.int16, device="cuda")
+    st = torch.full((p.n_chunks,), -7, dtype=torch.int32, device="cuda")
+    E.decode_bf16_split(p, blob, sm, out, st)
+    torch.cuda.synchronize()
+    assert (st.cpu().numpy() == 0).all()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w.ravel())
 
 
 def test_bf16_split_8192x8192_every_row(E):
