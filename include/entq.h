@@ -108,7 +108,8 @@ typedef enum { ENTQ_OUT_CODES = 0, ENTQ_OUT_BF16 = 1 } entq_outkind;
  * entq_decode_gemm_tiles / entq_decode_gemm_tiles_bf16_split, and
  * entq_decode / entq_decode_bf16_split write their ordinary row-major
  * outputs (codes, bf16 or the source bf16) when every tensor of the plan is
- * in tile order (a plan mixing the layouts: ENTQ_EINVAL there). The
+ * in tile order (at most 16 tensors; a plan mixing the layouts or with more
+ * tensors: ENTQ_EINVAL there). The
  * row-major fused calls (entq_decode_gemm*) refuse them. */
 #define ENTQ_LAYOUT_TILES 0x100u
 
