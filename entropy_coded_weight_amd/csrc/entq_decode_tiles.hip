@@ -238,15 +238,19 @@ __attribute__((amdgpu_waves_per_eu(8, 8))) void decode_tile_gemm(
 // decode of tile-ordered tensors into their row-major outputs
 // ---------------------------------------------------------------------------
 //
-// The same walk over a chunk's tiles, each lane storing its 4 consecutive
-// outputs of one row per tile (codes: 4 bytes; bf16: 8 bytes; a wave's
-// store covers 16 rows x 16 columns), so that a tensor kept in tile order
+// The same walk over a chunk's tiles, so that a tensor kept in tile order
 // for the fused product also decodes to the ordinary row-major weights.
+// After a tile each lane holds 4 consecutive outputs of one row; two tiles
+// are staged per wave in LDS (16 rows x 32 columns) and leave as 16 rows of
+// 64 contiguous bytes (bf16; 32 for codes), one 16-byte (8-byte) store per
+// lane. (Storing each tile straight from the lanes, 16 rows of 32 bytes:
+// 971 us per 70B-shaped layer against 456 us for the row-major decode.)
 template <int MODE, bool E4M3, bool PRIO>
 __device__ __forceinline__ void tile_decode_chunk(const DevChunk &ch,
                                                   const uint8_t *__restrict__ blob,
                                                   const uint2 *T, uint16_t *ring_lds,
-                                                  uint32_t lane, const float *__restrict__ scales,
+                                                  uint16_t *stage, uint32_t lane,
+                                                  const float *__restrict__ scales,
                                                   const uint8_t *__restrict__ signmant,
                                                   const TileTensor &gt, void *__restrict__ out,
                                                   Prio &pr, int32_t *__restrict__ status) {
@@ -261,8 +265,13 @@ __device__ __forceinline__ void tile_decode_chunk(const DevChunk &ch,
     const uint64_t cols = (uint64_t)gt.n_cc * C;
     const float scale = (MODE == kModeBf16) ? scales[gt.row0 + 16ull * band + r16] : 0.f;
     const uint8_t *smc = (MODE == kModeSplit) ? signmant + ch.out_elem + lane : nullptr;
-    // this lane's first output: row 16 band + r16, column cC + 4 (lane / 16)
+    // this lane's first output: row 16 band + r16, column cC + 4 (lane / 16);
+    // and its staged run of a pair of tiles: row lane / 4, columns 8 (lane % 4) ..
     const uint64_t o0 = gt.out0 + (16ull * band + r16) * cols + (uint64_t)cc * C + 4u * (lane >> 4);
+    const uint64_t p0 =
+        gt.out0 + (16ull * band + (lane >> 2)) * cols + (uint64_t)cc * C + 8u * (lane & 3);
+    // stage (16 rows x 32 columns): this lane's slot of tile j of a pair, and its run
+    const uint32_t put = r16 * 32u + 4u * (lane >> 4), get = (lane >> 2) * 32u + 8u * (lane & 3);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): states, scale, first ring units
     s.landed = s.issued;
     ring_horizon(s);
@@ -282,12 +291,21 @@ __device__ __forceinline__ void tile_decode_chunk(const DevChunk &ch,
         const uint32_t e1 = tile_step(x, s.pos, T, lane);
         const uint32_t e2 = tile_step(x, s.pos, T, lane);
         const uint32_t e3 = tile_step(x, s.pos, T, lane);
-        const uint64_t o = o0 + 16ull * t;
+        const uint32_t j = t & 1;                     // place in the pair
+        const bool last_single = (t + 1 == blocks) && j == 0;
         if (MODE == kModeCodes) {
             // the four symbols (byte 3 of each entry) in column order
             const uint32_t v = __builtin_amdgcn_perm(e1, e0, 0x0C0C0703u) |
                                __builtin_amdgcn_perm(e3, e2, 0x07030C0Cu);
-            *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(out) + o) = v;
+            uint8_t *st8 = reinterpret_cast<uint8_t *>(stage);
+            if (last_single) {
+                *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(out) + o0 + 16ull * t) = v;
+            } else {
+                *reinterpret_cast<uint32_t *>(st8 + put + 16u * j) = v;
+                if (j == 1)
+                    *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(out) + p0 + 16ull * (t - 1)) =
+                        *reinterpret_cast<const uint2 *>(st8 + get);
+            }
         } else {
             const uint32_t d0 = __builtin_amdgcn_perm(e1, e0, 0x070C030Cu);
             const uint32_t d1 = __builtin_amdgcn_perm(e3, e2, 0x070C030Cu);
@@ -297,7 +315,14 @@ __device__ __forceinline__ void tile_decode_chunk(const DevChunk &ch,
                                merge2((d1 & 0xFF00FF00u) | sm2 | (sm3 << 16)));
             else
                 w = make_uint2(dequant2_lane<E4M3>(d0, scale), dequant2_lane<E4M3>(d1, scale));
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o) = w;
+            if (last_single) {
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o0 + 16ull * t) = w;
+            } else {
+                *reinterpret_cast<uint2 *>(stage + put + 16u * j) = w;
+                if (j == 1)
+                    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + p0 + 16ull * (t - 1)) =
+                        *reinterpret_cast<const uint4 *>(stage + get);
+            }
         }
     }
     const uint64_t bad_state = __ballot(x != kStateLow);
@@ -315,6 +340,7 @@ __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_til
     const uint8_t *__restrict__ signmant, int32_t *__restrict__ status, TileArgs args) {
     __shared__ __attribute__((aligned(16))) uint16_t RING[kWaves][kRingWords];
     __shared__ uint2 T[kProbScale];
+    __shared__ __attribute__((aligned(16))) uint16_t STG[kWaves][16 * 32];  // two tiles
 
     const DevTask task = tasks[blockIdx.x];
     const bool e4m3 = tensors[task.tensor].kind == ENTQ_SYM_E4M3;
@@ -336,11 +362,11 @@ __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_til
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
         if (MODE == kModeBf16 && e4m3)
-            tile_decode_chunk<MODE, true, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant,
-                                                gt, out, pr, status);
+            tile_decode_chunk<MODE, true, PRIO>(ch, blob, T, RING[wave], STG[wave], lane, scales,
+                                                signmant, gt, out, pr, status);
         else
-            tile_decode_chunk<MODE, false, PRIO>(ch, blob, T, RING[wave], lane, scales, signmant,
-                                                 gt, out, pr, status);
+            tile_decode_chunk<MODE, false, PRIO>(ch, blob, T, RING[wave], STG[wave], lane, scales,
+                                                 signmant, gt, out, pr, status);
     }
 }
 

@@ -31,6 +31,7 @@ def _kernels(source):
 @pytest.mark.parametrize("source,kernel", [("entq_decode.hip", "decode_stream"),
                                            ("entq_decode_gemv.hip", "decode_gemv"),
                                            ("entq_decode_tiles.hip", "decode_tile_gemm"),
+                                           ("entq_decode_tiles.hip", "decode_tiles_rowmajor"),
                                            ("entq_decode_gemm.hip", "decode_gemm")])
 def test_two_workgroups_fit_per_compute_unit(source, kernel):
     ks = {n: v for n, v in _kernels(source).items() if kernel in n}
