@@ -388,3 +388,44 @@ def test_bf16_split_8192x8192_every_row(E):
                   >> 16).astype(np.uint16))
         y = _run_split(E, p, blob, sm, x, rows)
         assert oracle_rows.check_product(y, x, w) == rows
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103, 104])
+def test_random_batches(E, seed):
+    """Random plans in tile order: 1 to 5 tensors (int8 and e4m3), bands of
+    16 rows, chunk widths 16 to 512 columns dividing 1 to 5 column chunks,
+    random m; one-hot activations return the oracle's weights exactly and
+    random ones stay within the bound."""
+    rng = np.random.default_rng(seed)
+    specs, Cs = [], {}
+    for i in range(int(rng.integers(1, 6))):
+        C = int(rng.choice([16, 48, 256, 512]))
+        rows, cols = 16 * int(rng.integers(1, 9)), C * int(rng.integers(1, 6))
+        if i % 3 == 2:
+            sp = synth.e4m3_matrix(rows=rows, cols=cols)[0]
+            sp["name"] = f"e{seed}_{i}"
+        else:
+            sp = synth.random_int8_tensor(rows, cols, float(rng.uniform(0.8, 3.0)),
+                                          seed * 10 + i, 16 * C)
+        Cs[sp["name"]] = C
+        specs.append(sp)
+    tiled, b, p, blob, scales = _tiled(E, specs, lambda sp: Cs[sp["name"]])
+    W = _oracle_weights(b, tiled)
+    m = int(rng.integers(1, 65))
+    _say(f"random batch {seed}: {len(specs)} tensors, m={m}")
+    xs, hit = [], []
+    for sp in specs:
+        c = rng.choice(sp["cols"], m, replace=True)  # (a column may be hit twice)
+        x = np.zeros((m, sp["cols"]), np.float32)
+        x[np.arange(m), c] = 1.0
+        xs.append(x)
+        hit.append(c)
+    ys = _run(E, p, blob, scales, xs, specs, extra_rows=1)
+    for t in range(len(specs)):
+        want = _f32(W[t][:, hit[t]]).T
+        assert np.array_equal(ys[t][:m].view(np.uint32), want.view(np.uint32)), t
+    xs = [_f32(rng.integers(0, 65536, (m, sp["cols"]), dtype=np.uint64).astype(np.uint16)
+               & np.uint16(0xBFFF)) for sp in specs]
+    ys = _run(E, p, blob, scales, xs, specs, pad_x=4, pad_y=2)
+    for t, sp in enumerate(specs):
+        assert oracle_rows.check_product(ys[t][:, :sp["rows"]], xs[t], W[t]) == sp["rows"]
