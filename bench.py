@@ -700,7 +700,7 @@ def bench_overlap(args):
 
 
 FUSED_METRIC = ("tokens/s through the 80-layer 70B-shaped projection stack with each layer's "
-                "weights decoded inside the GEMM (entq_decode_gemm)")
+                "weights decoded inside the GEMM (entq_decode_gemm_tiles, tile-ordered chunks)")
 
 
 def oracle_tensor_sample(blob, chunks, freq, spec, n_chunks):
@@ -766,7 +766,7 @@ def tile_cols(cols, target):
 
 def compressed_layers_tiled(args, E, synth, dev, torch, target):
     """The 80 layers in tile order (chunks of 16 rows x tile_cols(cols,
-    target) columns), put in order on the host and encoded on the device."""
+    target) columns), put in order and encoded on the device."""
     nthreads = args.threads or synth.default_threads()
     t0 = time.time()
     layers, meta0 = [], None
@@ -775,9 +775,11 @@ def compressed_layers_tiled(args, E, synth, dev, torch, target):
         ds = []
         for sp in specs:
             C = tile_cols(sp["cols"], target)
-            st = E.tile_order(sp["symbols"], sp["rows"], sp["cols"], C, nthreads)
-            ds.append(dict(sp, symbols=torch.from_numpy(st).to(dev), chunk_symbols=16 * C, C=C,
+            src = torch.from_numpy(np.ascontiguousarray(sp["symbols"]).view(np.uint8)).to(dev)
+            st = E.tile_order_device(src, sp["rows"], sp["cols"], C)
+            ds.append(dict(sp, symbols=st, chunk_symbols=16 * C, C=C,
                            kind=sp["kind"] | E.LAYOUT_TILES))
+            del src
         b = E.encode_batch_device(ds)
         p = E.plan(b.tensors, b.freq, b.chunks, b.blob.numel())
         sc = torch.from_numpy(np.concatenate([s_["scales"] for s_ in specs])).to(dev)

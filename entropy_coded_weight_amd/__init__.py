@@ -119,6 +119,7 @@ def lib():
             "entq_build_freq_device": (c.c_int, [vp, c.c_uint32, u64, vp, vp]),
             "entq_decode_gemm_static": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, vp]),
             "entq_tile_order": (c.c_int, [vp, c.c_uint32, c.c_uint32, c.c_uint32, vp, c.c_int]),
+            "entq_tile_order_device": (c.c_int, [vp, c.c_uint32, c.c_uint32, c.c_uint32, vp, vp]),
             "entq_decode_gemm_tiles_workspace_bytes": (u64, [vp, c.c_int]),
             "entq_decode_gemm_tiles": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp, vp]),
             "entq_decode_gemm_tiles_bf16_split": (c.c_int, [vp, vp, vp, vp, c.c_int, vp, u64, vp,
@@ -145,7 +146,8 @@ EXPORTED = ["entq_plan_workspace_bytes", "entq_plan", "entq_decode", "entq_decod
             "entq_region_offsets_device_adaptive", "entq_pack_device_adaptive_batch",
             "entq_build_freq_device", "entq_decode_gemm_workspace_bytes",
             "entq_decode_gemm_static", "entq_tile_order", "entq_decode_gemm_tiles_workspace_bytes",
-            "entq_decode_gemm_tiles", "entq_decode_gemm_tiles_bf16_split"]
+            "entq_decode_gemm_tiles", "entq_decode_gemm_tiles_bf16_split",
+            "entq_tile_order_device"]
 
 
 def _str(status: int) -> str:
@@ -456,6 +458,22 @@ def _tiles_workspace(p: Plan, m: int, workspace, stream):
     else:
         _device_buffer(p, "workspace", workspace, need, elem_size=1)
     return workspace, (workspace.numel() if workspace is not None else 0)
+
+
+def tile_order_device(codes, rows: int, cols: int, chunk_cols: int, out=None, stream=None):
+    """tile_order on the device: codes a device tensor of rows x cols bytes
+    (row-major, 4-byte aligned); returns (or fills) a device uint8 tensor."""
+    import torch
+    if codes.numel() * codes.element_size() != rows * cols or not codes.is_contiguous():
+        raise EntqError(EINVAL, f"codes must be {rows} x {cols} contiguous bytes")
+    if out is None:
+        out = torch.empty(rows * cols, dtype=torch.uint8, device=codes.device)
+    elif out.numel() * out.element_size() < rows * cols or out.device != codes.device:
+        raise EntqError(EINVAL, "out must hold rows x cols bytes on the codes' device")
+    _check(lib().entq_tile_order_device(_ptr(codes) or None, rows, cols, chunk_cols,
+                                        _ptr(out) or None, _stream(stream)),
+           "entq_tile_order_device")
+    return out
 
 
 def decode_gemm_tiles(p: Plan, compressed, scales, xs, ys, chunk_status=None, stream=None,

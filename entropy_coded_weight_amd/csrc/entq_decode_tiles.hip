@@ -385,6 +385,33 @@ void launch_tiles_rowmajor(bool prio, dim3 grid, hipStream_t st, const entq_plan
                            out, scales, signmant, status, args);
 }
 
+// The tile order on the device: one thread per 4 bytes of the output (a
+// lane's 4 consecutive columns of one row, stream positions 64 s + l of a
+// tile, s = 0..3), reading the row-major source (4 contiguous bytes) and
+// writing the 4 bytes to their 4 stream positions.
+__global__ __launch_bounds__(256) void tile_order_bytes(const uint8_t *__restrict__ in,
+                                                        uint8_t *__restrict__ out,
+                                                        uint32_t cols, uint32_t chunk_cols,
+                                                        uint64_t n_quads) {
+    const uint64_t q = (uint64_t)blockIdx.x * 256 + threadIdx.x;  // quad = tile, lane
+    if (q >= n_quads) return;
+    const uint64_t tile = q >> 6;        // tiles in stream order
+    const uint32_t l = (uint32_t)(q & 63);
+    const uint32_t tiles_per_chunk = chunk_cols / 16;
+    const uint64_t k = tile / tiles_per_chunk;  // chunk
+    const uint32_t t = (uint32_t)(tile % tiles_per_chunk);
+    const uint32_t n_cc = cols / chunk_cols;
+    const uint64_t band = k / n_cc, cc = k % n_cc;
+    const uint64_t row = 16 * band + (l & 15);
+    const uint64_t col = cc * chunk_cols + 16u * t + 4u * (l >> 4);
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(in + row * cols + col);
+    uint8_t *dst = out + tile * 256 + l;
+    dst[0] = (uint8_t)v;
+    dst[64] = (uint8_t)(v >> 8);
+    dst[128] = (uint8_t)(v >> 16);
+    dst[192] = (uint8_t)(v >> 24);
+}
+
 // Y of the tensors whose chunks split the columns: the column chunks'
 // partial sums added in column order, one thread per result.
 struct ReduceTensor {
@@ -614,6 +641,20 @@ entq_status entq_decode_gemm_tiles_bf16_split(const entq_plan_t *plan, const voi
     if (plan->n_chunks && (!d_exp_stream || !d_signmant)) return ENTQ_EINVAL;
     return entq::run_tiles(plan, d_exp_stream, nullptr, d_signmant, io, m, d_workspace,
                            workspace_bytes, d_chunk_status, stream);
+}
+
+entq_status entq_tile_order_device(const uint8_t *d_codes, uint32_t rows, uint32_t cols,
+                                   uint32_t chunk_cols, uint8_t *d_out, void *stream) {
+    if (rows % 16 || chunk_cols == 0 || chunk_cols % 16 || cols % chunk_cols) return ENTQ_EINVAL;
+    const uint64_t n = (uint64_t)rows * cols;
+    if (n == 0) return ENTQ_OK;
+    if (!d_codes || !d_out) return ENTQ_EINVAL;
+    if ((uintptr_t)d_codes % 4) return ENTQ_EALIGN;
+    const uint64_t quads = n / 4, blocks = (quads + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return ENTQ_EINVAL;
+    hipLaunchKernelGGL(entq::tile_order_bytes, dim3((unsigned)blocks), dim3(256), 0,
+                       (hipStream_t)stream, d_codes, d_out, cols, chunk_cols, quads);
+    return hipGetLastError() == hipSuccess ? ENTQ_OK : ENTQ_EHIP;
 }
 
 }  // extern "C"

@@ -372,6 +372,12 @@ entq_status entq_decode_gemm_bf16_split(const entq_plan_t *plan, const void *d_e
 entq_status entq_tile_order(const uint8_t *codes, uint32_t rows, uint32_t cols,
                             uint32_t chunk_cols, uint8_t *out, int n_threads);
 
+/* The same on the device: d_codes (4-byte aligned) and d_out (rows x cols
+ * bytes each, not overlapping) in device memory; enqueued on stream, for
+ * the device encoder (entq_encode_device_batch) to code the result. */
+entq_status entq_tile_order_device(const uint8_t *d_codes, uint32_t rows, uint32_t cols,
+                                   uint32_t chunk_cols, uint8_t *d_out, void *stream);
+
 /* Bytes of workspace entq_decode_gemm_tiles needs for this plan and m (0 for
  * invalid arguments): the activations packed in the order the waves read
  * them (as entq_decode_gemm_workspace_bytes counts them), and for each

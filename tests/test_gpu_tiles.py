@@ -429,3 +429,14 @@ def test_random_batches(E, seed):
     ys = _run(E, p, blob, scales, xs, specs, pad_x=4, pad_y=2)
     for t, sp in enumerate(specs):
         assert oracle_rows.check_product(ys[t][:, :sp["rows"]], xs[t], W[t]) == sp["rows"]
+
+
+@pytest.mark.parametrize("rows,cols,C", [(16, 16, 16), (48, 768, 256), (64, 2816, 256),
+                                         (32, 28672, 7168)])
+def test_tile_order_on_the_device_matches_the_oracle(E, rows, cols, C):
+    import torch
+    rng = np.random.default_rng(rows + cols)
+    w = rng.integers(0, 256, rows * cols, dtype=np.uint8)
+    got = E.tile_order_device(torch.from_numpy(w).cuda(), rows, cols, C)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.tile_order(w, rows, cols, C))
