@@ -10,10 +10,13 @@
 // per workgroup; with a table per chunk every wave needs its own, so the
 // slot table is split into a 4 KB slot -> symbol map and a 1 KB symbol ->
 // (f, cum) map, built by the wave from its chunk's 512-byte header before it
-// decodes the chunk: a wave scan of the frequencies gives the cumulative
-// starts, then each lane fills 64 consecutive slots (a binary search for the
-// symbol of its first slot, then a walk). A decode step reads both maps (two
-// dependent LDS reads instead of one); the word ring, the staged 4-step
+// decodes the chunk, with no data-dependent branch: a wave scan of the
+// frequencies gives the cumulative starts, every present symbol writes its
+// byte at its first slot into the cleared map, and each lane turns its 64
+// slots into a running maximum that starts from the symbol of its first slot
+// (a binary search) -- slots are owned in ascending symbol order, so the
+// running maximum of the start marks is the owner. A decode step reads both
+// maps (two dependent LDS reads instead of one); the word ring, the staged 4-step
 // blocks and the fused scale/bf16 store are the streaming decoder's
 // (entq_stream.h). Waves share nothing, so no workgroup barrier is needed;
 // wave g of the grid decodes chunks g, g + G, g + 2G, ...
@@ -31,24 +34,36 @@ namespace {
 constexpr int kAdWaves = 7;  // 7.5 KB of LDS each: three workgroups per CU
 constexpr int kAdThreads = kAdWaves * 64;
 
+// Per wave, besides its 4 KB slot -> symbol map (kept apart, 4096-byte
+// aligned, so that a slot's LDS address is the map's base OR the slot).
 struct alignas(16) AdaptiveWave {
-    uint8_t sym[kProbScale];     // slot -> symbol
-    uint32_t ent[256];           // symbol -> f | cum << 16
-    uint16_t stage[kBlockSyms];  // one block of staged symbols (symbol << 8)
+    uint32_t ent[256];           // symbol -> f | (cum + map base) << 16
+    uint16_t stage[kBlockSyms];  // one block of staged symbols (symbol in byte 0)
 };
 
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+
 // One decode step with the chunk's own maps; otherwise as stream_step.
+// map_base: LDS address of the wave's slot -> symbol map (a multiple of
+// 4096, below 61440), so the map byte of slot x mod 4096 sits at
+// map_base | slot, and (that address) - (cum + map_base) = slot - cum.
+// slot_mask holds kProbScale - 1 (a register: the three-operand form takes no
+// literal). The stage slot holds the symbol itself (byte 0), the map byte
+// as loaded (zero-extended by the load) serving as table index and stage value.
 template <bool PARTIAL>
-__device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &pos, const uint8_t *SYM,
-                                              const uint32_t *ENT, uint16_t *stage_row,
-                                              uint32_t lane, bool active) {
+__device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &pos, uint32_t map_base,
+                                              uint32_t slot_mask, const uint32_t *ENT,
+                                              uint16_t *stage_row, uint32_t lane, bool active) {
     bool need = false;
     if (!PARTIAL || active) {
-        const uint32_t slot = x & (kProbScale - 1);
-        const uint32_t s = SYM[slot];
+        uint32_t at;
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(at) : "v"(x), "v"(slot_mask), "s"(map_base));
+        const uint32_t xs = x >> kProbBits;  // computed while the map byte loads
+        uint32_t s = *reinterpret_cast<lds_u8 *>(at);
+        asm("" : "+v"(s) : "v"(xs));  // one 32-bit value for both uses below, no re-masking
         const uint32_t e = ENT[s];
-        x = __umul24(e & 0x1FFFu, x >> kProbBits) + slot - (e >> 16);
-        stage_row[lane] = (uint16_t)(s << 8);
+        x = __umul24(e & 0x1FFFu, xs) + (at - (e >> 16));
+        stage_row[lane] = (uint16_t)s;
         need = x < kStateLow;
     }
     const uint64_t mask = __ballot(need);
@@ -57,16 +72,32 @@ __device__ __forceinline__ void adaptive_step(uint32_t &x, uint32_t &pos, const 
     pos += (uint32_t)__popcll(mask);
 }
 
+// bf16 of (value of a code byte) * scale for the codes in bytes 0 and 2 of d
+// (this kernel's stage layout), as dequant2 gives for bytes 1 and 3.
+template <bool E4M3>
+__device__ __forceinline__ uint32_t dequant2_lo(uint32_t d, float scale) {
+    float v0, v1;
+    if (E4M3) {
+        v0 = __builtin_amdgcn_cvt_f32_fp8((int)d, 0);
+        v1 = __builtin_amdgcn_cvt_f32_fp8((int)d, 2);
+    } else {
+        v0 = (float)((int32_t)(d << 24) >> 24);
+        v1 = (float)((int32_t)(d << 8) >> 24);
+    }
+    const uint32_t r = bf16x2_bits(mul_value_uscale(v0, scale), mul_value_uscale(v1, scale));
+    return E4M3 ? e4m3_nan_patch2(d << 8, r) : r;
+}
+
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Builds the wave's maps from a chunk's table; false if it does not sum to
-// 4096.
-__device__ __forceinline__ bool build_maps(const uint8_t *table, AdaptiveWave &W, uint32_t lane) {
-    const uint2 fr = *reinterpret_cast<const uint2 *>(table + 8u * lane);  // entries 4l .. 4l+3
+// Builds the wave's maps from a chunk's table (fr: the lane's entries
+// 4l .. 4l+3); false if it does not sum to 4096.
+__device__ __forceinline__ bool build_maps(const uint2 fr, AdaptiveWave &W, uint8_t *SYM,
+                                           uint32_t map_base, uint32_t lane) {
     const uint32_t f0 = fr.x & 0xFFFFu, f1 = fr.x >> 16, f2 = fr.y & 0xFFFFu, f3 = fr.y >> 16;
     const uint32_t own = f0 + f1 + f2 + f3;
     uint32_t incl = own;  // inclusive scan over the lanes
@@ -77,32 +108,48 @@ __device__ __forceinline__ bool build_maps(const uint8_t *table, AdaptiveWave &W
     }
     const uint32_t total = __shfl(incl, 63);
     if (total != kProbScale) return false;
-    const uint32_t c0 = incl - own;
-    W.ent[4u * lane + 0] = f0 | (c0 << 16);
-    W.ent[4u * lane + 1] = f1 | ((c0 + f0) << 16);
-    W.ent[4u * lane + 2] = f2 | ((c0 + f0 + f1) << 16);
-    W.ent[4u * lane + 3] = f3 | ((c0 + f0 + f1 + f2) << 16);
+    const uint32_t c0 = incl - own, c1 = c0 + f0, c2 = c1 + f1, c3 = c2 + f2;
+    W.ent[4u * lane + 0] = f0 | ((c0 + map_base) << 16);
+    W.ent[4u * lane + 1] = f1 | ((c1 + map_base) << 16);
+    W.ent[4u * lane + 2] = f2 | ((c2 + map_base) << 16);
+    W.ent[4u * lane + 3] = f3 | ((c3 + map_base) << 16);
+    uint4 *mine = reinterpret_cast<uint4 *>(SYM + 64u * lane);  // slots 64 l .. 64 l + 63
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) mine[k] = make_uint4(0, 0, 0, 0);
     wave_sync();
-    // lane l fills slots 64 l .. 64 l + 63: the symbol of a slot is the last
-    // one whose cumulative start is at or below it
-    const uint32_t j0 = 64u * lane;
+    // each present symbol marks its first slot (distinct slots: f >= 1)
+    if (f0) SYM[c0] = (uint8_t)(4u * lane + 0);
+    if (f1) SYM[c1] = (uint8_t)(4u * lane + 1);
+    if (f2) SYM[c2] = (uint8_t)(4u * lane + 2);
+    if (f3) SYM[c3] = (uint8_t)(4u * lane + 3);
+    // the symbol of the lane's first slot: the last one whose start is at or
+    // below it (a symbol of frequency 0 shares its start with the next one,
+    // so the last such symbol is a present one)
+    const uint32_t j0 = 64u * lane + map_base;
     uint32_t s = 0;
 #pragma unroll
     for (uint32_t step = 128; step; step >>= 1)
         if ((W.ent[s + step] >> 16) <= j0) s += step;  // s + step <= 255
-    uint32_t next = s < 255 ? (W.ent[s + 1] >> 16) : kProbScale;
-    for (uint32_t k = 0; k < 64; k += 4) {
-        uint32_t packed = 0;
+    wave_sync();
+    // owner of each slot = running maximum of the marks from the lane's
+    // first slot on (a later mark is a larger symbol than every owner before)
+    uint32_t m = s;
 #pragma unroll
-        for (uint32_t q = 0; q < 4; ++q) {
-            const uint32_t j = j0 + k + q;
-            while (next <= j) {
-                ++s;
-                next = s < 255 ? (W.ent[s + 1] >> 16) : kProbScale;
+    for (uint32_t k = 0; k < 4; ++k) {
+        uint4 v = mine[k];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i) {
+            uint32_t r = 0;
+#pragma unroll
+            for (uint32_t b = 0; b < 4; ++b) {
+                const uint32_t mark = (w[i] >> (8 * b)) & 0xFFu;
+                m = m > mark ? m : mark;
+                r |= m << (8 * b);
             }
-            packed |= s << (8 * q);
+            w[i] = r;
         }
-        *reinterpret_cast<uint32_t *>(W.sym + j0 + k) = packed;
+        mine[k] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     wave_sync();
     return true;
@@ -113,18 +160,23 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
     const DevTensor *__restrict__ tensors, const DevChunk *__restrict__ chunks, uint32_t n_chunks,
     const uint8_t *__restrict__ blob, void *__restrict__ out, const float *__restrict__ scales,
     const uint8_t *__restrict__ signmant, int32_t *__restrict__ status) {
+    __shared__ __attribute__((aligned(kProbScale))) uint8_t MAPS[kAdWaves][kProbScale];
     __shared__ __attribute__((aligned(16))) uint16_t RING[kAdWaves][kRingWords];
     __shared__ AdaptiveWave WV[kAdWaves];
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
     AdaptiveWave &W = WV[wave];
+    uint8_t *SYM = MAPS[wave];
+    const uint32_t map_base = __builtin_amdgcn_readfirstlane(lds_addr(SYM));
+    const uint32_t slot_mask = kProbScale - 1;
     const uint32_t waves = gridDim.x * kAdWaves;
     for (uint32_t c = blockIdx.x * kAdWaves + wave; c < n_chunks; c += waves) {
         const DevChunk ch = chunks[c];
         const DevTensor td = tensors[ch.tensor];
         const uint8_t *region = blob + ch.byte_offset;
-        if (!build_maps(region, W, lane)) {
+        if (!build_maps(*reinterpret_cast<const uint2 *>(region + 8u * lane), W, SYM, map_base,
+                        lane)) {
             if (status && lane == 0) status[ch.status_index] = ENTQ_CHUNK_BAD_TABLE;
             continue;
         }
@@ -154,15 +206,15 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
             if (MODE == kModeSplit) sm4 = *reinterpret_cast<const uint32_t *>(sm_g + 4u * lane);
 #pragma unroll
             for (uint32_t t = 0; t < kBlockSteps; ++t)
-                adaptive_step<false>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane, true);
+                adaptive_step<false>(x, s.pos, map_base, slot_mask, W.ent, W.stage + 64u * t, lane, true);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
             if (MODE == kModeCodes) {
-                reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
+                reinterpret_cast<uint32_t *>(o8)[lane] = __builtin_amdgcn_perm(d.y, d.x, 0x06040200u);
                 o8 += kBlockSyms;
             } else if (MODE == kModeSplit) {
                 // per 16-bit half: exponent << 8 | sign+mantissa
-                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x07010500u)),
-                                           merge2(__builtin_amdgcn_perm(d.y, sm4, 0x07030502u)));
+                const uint2 w = make_uint2(merge2(__builtin_amdgcn_perm(d.x, sm4, 0x06010400u)),
+                                           merge2(__builtin_amdgcn_perm(d.y, sm4, 0x06030402u)));
                 reinterpret_cast<uint2 *>(o16)[lane] = w;
                 o16 += kBlockSyms;
                 sm_g += kBlockSyms;
@@ -172,8 +224,8 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
                     ++scale_row;
                     scale = *scale_row;
                 }
-                const uint2 w = e4m3 ? make_uint2(dequant2<true>(d.x, scale), dequant2<true>(d.y, scale))
-                                     : make_uint2(dequant2<false>(d.x, scale), dequant2<false>(d.y, scale));
+                const uint2 w = e4m3 ? make_uint2(dequant2_lo<true>(d.x, scale), dequant2_lo<true>(d.y, scale))
+                                     : make_uint2(dequant2_lo<false>(d.x, scale), dequant2_lo<false>(d.y, scale));
                 reinterpret_cast<uint2 *>(o16)[lane] = w;
                 o16 += kBlockSyms;
                 col += kBlockSyms;
@@ -188,10 +240,10 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
                 scale = *scale_row;
             }
             for (uint32_t t = 0; 64u * t < rest; ++t)
-                adaptive_step<true>(x, s.pos, W.sym, W.ent, W.stage + 64u * t, lane,
+                adaptive_step<true>(x, s.pos, map_base, slot_mask, W.ent, W.stage + 64u * t, lane,
                                     64u * t + lane < rest);
             const uint2 d = *reinterpret_cast<const uint2 *>(W.stage + 4u * lane);
-            const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x07050301u);
+            const uint32_t sym4 = __builtin_amdgcn_perm(d.y, d.x, 0x06040200u);
             for (uint32_t m = 0; m < 4; ++m) {
                 const uint32_t i = 4u * lane + m;
                 if (i >= rest) break;
