@@ -287,6 +287,46 @@ def _device_buffer(p: Plan, name: str, t, min_elems: int, elem_size: int | None 
         raise EntqError(EINVAL, f"{name} holds {t.numel()} elements, the plan needs {min_elems}")
 
 
+def _dev(name: str, t, min_elems: int = 0, dtypes=None, device=None):
+    """Checks a device buffer of a call that has no plan (the device
+    encoder, the device tile order): a contiguous torch tensor on a GPU (on
+    ``device`` when given), of one of ``dtypes``, with at least
+    ``min_elems`` elements -- the kernels dereference its raw pointer, so a
+    host tensor or a short buffer must be refused before the launch."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise EntqError(EINVAL, f"{name}: a torch tensor on a GPU is required")
+    if device is not None and t.device != device:
+        raise EntqError(EINVAL, f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise EntqError(EINVAL, f"{name} is not contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise EntqError(EINVAL, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() < min_elems:
+        raise EntqError(EINVAL, f"{name} holds {t.numel()} elements, {min_elems} needed")
+
+
+def _bytes_dtypes():
+    import torch
+    return (torch.uint8, torch.int8)
+
+
+def _freq_dtypes():
+    import torch
+    return tuple(d for d in (torch.int16, getattr(torch, "uint16", None)) if d is not None)
+
+
+def _n_chunks(n: int, chunk_symbols: int) -> int:
+    if chunk_symbols <= 0:
+        raise EntqError(EINVAL, f"chunk_symbols {chunk_symbols}")
+    return -(-int(n) // int(chunk_symbols))
+
+
+def _check_symbols(name: str, sym):
+    _dev(name, sym, dtypes=_bytes_dtypes())
+    return sym.device
+
+
 def _status_buffer(p: Plan, chunk_status):
     import torch
     if chunk_status is not None:
@@ -464,12 +504,15 @@ def tile_order_device(codes, rows: int, cols: int, chunk_cols: int, out=None, st
     """tile_order on the device: codes a device tensor of rows x cols bytes
     (row-major, 4-byte aligned); returns (or fills) a device uint8 tensor."""
     import torch
-    if codes.numel() * codes.element_size() != rows * cols or not codes.is_contiguous():
+    _dev("codes", codes)
+    if codes.numel() * codes.element_size() != rows * cols:
         raise EntqError(EINVAL, f"codes must be {rows} x {cols} contiguous bytes")
     if out is None:
         out = torch.empty(rows * cols, dtype=torch.uint8, device=codes.device)
-    elif out.numel() * out.element_size() < rows * cols or out.device != codes.device:
-        raise EntqError(EINVAL, "out must hold rows x cols bytes on the codes' device")
+    else:
+        _dev("out", out, 0, None, codes.device)
+        if out.numel() * out.element_size() < rows * cols:
+            raise EntqError(EINVAL, "out must hold rows x cols bytes on the codes' device")
     _check(lib().entq_tile_order_device(_ptr(codes) or None, rows, cols, chunk_cols,
                                         _ptr(out) or None, _stream(stream)),
            "entq_tile_order_device")
@@ -667,12 +710,39 @@ def encode_batch_adaptive(specs, n_threads: int | None = None) -> Batch:
 # on-device encoder
 # --------------------------------------------------------------------------
 
+def _check_pack_job(scratch, n, C, nw, offs, blob, what=""):
+    import torch
+    _dev(what + "blob", blob, 0, _bytes_dtypes())
+    k = _n_chunks(n, C)
+    _dev(what + "scratch", scratch, 0, _bytes_dtypes(), blob.device)
+    _dev(what + "n_words", nw, k, (torch.int32,), blob.device)
+    _dev(what + "offsets", offs, k, (torch.int64,), blob.device)
+
+
+def _check_encode_job(sym, C, freq, scratch, nw, freq_entries, what=""):
+    import torch
+    dev = _check_symbols(what + "symbols", sym)
+    k = _n_chunks(sym.numel(), C)
+    _dev(what + "freq", freq, freq_entries, _freq_dtypes(), dev)
+    _dev(what + "scratch", scratch, 0, _bytes_dtypes(), dev)
+    _dev(what + "n_words", nw, k, (torch.int32,), dev)
+
+
+def _check_offsets_args(n_words, offsets, end):
+    import torch
+    _dev("n_words", n_words, 0, (torch.int32,))
+    _dev("offsets", offsets, n_words.numel(), (torch.int64,), n_words.device)
+    _dev("end", end, 1, (torch.int64,), n_words.device)
+
+
 def count_symbols_device(symbols, counts=None, stream=None):
     """Byte counts of a device uint8 tensor (16-byte aligned) into a device
     uint64 tensor [256] (zeroed here unless given)."""
     import torch
+    dev = _check_symbols("symbols", symbols)
     if counts is None:
         counts = torch.zeros(256, dtype=torch.int64, device=symbols.device)
+    _dev("counts", counts, 256, (torch.int64,), dev)
     _check(lib().entq_count_symbols_device(_ptr(symbols) or None, symbols.numel(), _ptr(counts),
                                            _stream(stream)), "entq_count_symbols_device")
     return counts
@@ -687,7 +757,14 @@ def encode_device(symbols, chunk_symbols: int, freq: np.ndarray, scratch, n_word
     entq_encode_device_scratch_bytes long); word counts to ``n_words``
     (device int32 [n_chunks], 0xFFFFFFFF marks a chunk with a frequency-0
     symbol)."""
+    import torch
+    dev = _check_symbols("symbols", symbols)
+    k = _n_chunks(symbols.numel(), chunk_symbols)
+    _dev("scratch", scratch, 0, _bytes_dtypes(), dev)
+    _dev("n_words", n_words, k, (torch.int32,), dev)
     freq = np.ascontiguousarray(freq, dtype=np.uint16)
+    if freq.size < 256:
+        raise EntqError(EINVAL, f"freq holds {freq.size} entries, 256 needed")
     _check(lib().entq_encode_device(_ptr(symbols) or None, symbols.numel(), int(chunk_symbols),
                                     _ptr(freq), _ptr(scratch) or None,
                                     scratch.numel() if scratch is not None else 0,
@@ -695,6 +772,10 @@ def encode_device(symbols, chunk_symbols: int, freq: np.ndarray, scratch, n_word
 
 
 def pack_device(scratch, n: int, chunk_symbols: int, n_words, offsets, blob, stream=None):
+    """Copies each chunk's states and words from ``scratch`` into its region
+    of ``blob`` at ``offsets`` (device int64 [k], from region_offsets_device);
+    blob must hold the regions up to the end that call reported."""
+    _check_pack_job(scratch, n, chunk_symbols, n_words, offsets, blob)
     _check(lib().entq_pack_device(_ptr(scratch) or None, int(n), int(chunk_symbols),
                                   _ptr(n_words) or None, _ptr(offsets) or None,
                                   _ptr(blob) or None, _stream(stream)), "entq_pack_device")
@@ -703,8 +784,11 @@ def pack_device(scratch, n: int, chunk_symbols: int, n_words, offsets, blob, str
 def count_symbols_device_batch(jobs, stream=None):
     """jobs: list of (symbols, counts) device tensors (counts int64 [256],
     zeroed by the caller); one launch per 16 arrays."""
+    import torch
     arr = np.zeros(len(jobs), COUNT_JOB)
     for i, (sym, counts) in enumerate(jobs):
+        dev = _check_symbols(f"jobs[{i}] symbols", sym)
+        _dev(f"jobs[{i}] counts", counts, 256, (torch.int64,), dev)
         arr[i] = (_ptr(sym), sym.numel(), _ptr(counts))
     _check(lib().entq_count_symbols_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
                                                  _stream(stream)),
@@ -716,6 +800,7 @@ def pack_device_batch(jobs, blob, stream=None):
     pack_device; all write into blob; one launch per 16 tensors."""
     arr = np.zeros(len(jobs), PACK_JOB)
     for i, (scratch, n, C, nw, offs) in enumerate(jobs):
+        _check_pack_job(scratch, n, C, nw, offs, blob, f"jobs[{i}] ")
         arr[i] = (_ptr(scratch), int(n), int(C), 0, _ptr(nw), _ptr(offs))
     _check(lib().entq_pack_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
                                         _ptr(blob), _stream(stream)), "entq_pack_device_batch")
@@ -728,6 +813,7 @@ def encode_device_batch(jobs, stream=None):
     frequency-0 symbol gets word count 0xFFFFFFFF."""
     arr = np.zeros(len(jobs), ENCODE_JOB)
     for i, (sym, C, freq, scratch, nw) in enumerate(jobs):
+        _check_encode_job(sym, C, freq, scratch, nw, 256, f"jobs[{i}] ")
         arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(freq), _ptr(scratch),
                   scratch.numel(), _ptr(nw))
     _check(lib().entq_encode_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
@@ -738,6 +824,7 @@ def region_offsets_device(n_words, offsets, end, base_offset: int = 0, stream=No
     """Region byte offsets of consecutive chunks from their device word
     counts (int32 [k]) into ``offsets`` (device int64 [k]); ``end`` (device
     int64 [1]) gets base_offset + all their bytes."""
+    _check_offsets_args(n_words, offsets, end)
     _check(lib().entq_region_offsets_device(_ptr(n_words) or None, n_words.numel(),
                                             int(base_offset), _ptr(offsets) or None, _ptr(end),
                                             _stream(stream)), "entq_region_offsets_device")
@@ -747,8 +834,11 @@ def count_chunks_device_batch(jobs, stream=None):
     """jobs: list of (symbols, chunk_symbols, counts) with device tensors;
     counts int32 [ceil(n / chunk_symbols), 256] receives each chunk's byte
     counts. One launch per 16 arrays."""
+    import torch
     arr = np.zeros(len(jobs), CHUNK_COUNT_JOB)
     for i, (sym, C, counts) in enumerate(jobs):
+        dev = _check_symbols(f"jobs[{i}] symbols", sym)
+        _dev(f"jobs[{i}] counts", counts, 256 * _n_chunks(sym.numel(), C), (torch.int32,), dev)
         arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(counts))
     _check(lib().entq_count_chunks_device_batch(_ptr(arr) if len(jobs) else None, len(jobs),
                                                 _stream(stream)),
@@ -770,9 +860,9 @@ def build_freq_device(counts, freq, stream=None):
     """Tables from counts on the device: counts int32 or int64 [k, 256]
     (device), freq int16/uint16 [k, 256] (device)."""
     import torch
-    assert counts.dtype in (torch.int32, torch.int64) and counts.is_contiguous()
+    _dev("counts", counts, 0, (torch.int32, torch.int64))
     k = counts.numel() // 256
-    assert freq.numel() >= k * 256
+    _dev("freq", freq, k * 256, _freq_dtypes(), counts.device)
     _check(lib().entq_build_freq_device(_ptr(counts) or None, counts.element_size(), k,
                                         _ptr(freq) or None, _stream(stream)),
            "entq_build_freq_device")
@@ -784,6 +874,8 @@ def encode_device_adaptive_batch(jobs, stream=None):
     [n_chunks, 256]."""
     arr = np.zeros(len(jobs), ENCODE_JOB)
     for i, (sym, C, freq, scratch, nw) in enumerate(jobs):
+        _check_encode_job(sym, C, freq, scratch, nw, 256 * _n_chunks(sym.numel(), C),
+                          f"jobs[{i}] ")
         arr[i] = (_ptr(sym), sym.numel(), int(C), 0, _ptr(freq), _ptr(scratch),
                   scratch.numel(), _ptr(nw))
     _check(lib().entq_encode_device_adaptive_batch(_ptr(arr) if len(jobs) else None, len(jobs),
@@ -793,6 +885,7 @@ def encode_device_adaptive_batch(jobs, stream=None):
 
 def region_offsets_device_adaptive(n_words, offsets, end, base_offset: int = 0, stream=None):
     """region_offsets_device for regions headed by their table."""
+    _check_offsets_args(n_words, offsets, end)
     _check(lib().entq_region_offsets_device_adaptive(_ptr(n_words) or None, n_words.numel(),
                                                      int(base_offset), _ptr(offsets) or None,
                                                      _ptr(end), _stream(stream)),
@@ -802,8 +895,11 @@ def region_offsets_device_adaptive(n_words, offsets, end, base_offset: int = 0, 
 def pack_device_adaptive_batch(jobs, blob, stream=None):
     """pack_device_batch for regions headed by their table: jobs are
     (scratch, n, chunk_symbols, n_words, offsets, freq)."""
+    import torch
     arr = np.zeros(len(jobs), PACK_ADAPTIVE_JOB)
     for i, (scratch, n, C, nw, offs, freq) in enumerate(jobs):
+        _check_pack_job(scratch, n, C, nw, offs, blob, f"jobs[{i}] ")
+        _dev(f"jobs[{i}] freq", freq, 256 * _n_chunks(n, C), _freq_dtypes(), blob.device)
         arr[i] = (_ptr(scratch), int(n), int(C), 0, _ptr(nw), _ptr(offs), _ptr(freq))
     _check(lib().entq_pack_device_adaptive_batch(_ptr(arr) if len(jobs) else None, len(jobs),
                                                  _ptr(blob), _stream(stream)),

@@ -169,3 +169,46 @@ def test_linear_refuses(E, P):
     xs, ys = _xy(64, [(4, 256), (3, 512)])
     P.tensors["kind"][1] = E.KIND_INT8
     _rejects(E, linear, P, blob[:899], sc, xs, ys, stream=0, match="compressed holds")
+
+
+# ---- calls without a plan: the device encoder and the device tile order ----
+
+def _cpu(n, dtype=torch.uint8):
+    return torch.zeros(n, dtype=dtype)
+
+
+@pytest.mark.parametrize("call", [
+    lambda E: E.count_symbols_device(_cpu(64)),
+    lambda E: E.encode_device(_cpu(4096), 4096, np.full(256, 16, np.uint16), _cpu(1 << 16),
+                              _cpu(1, torch.int32)),
+    lambda E: E.pack_device(_cpu(1 << 16), 4096, 4096, _cpu(1, torch.int32),
+                            _cpu(1, torch.int64), _cpu(1 << 16)),
+    lambda E: E.count_symbols_device_batch([(_cpu(64), _cpu(256, torch.int64))]),
+    lambda E: E.pack_device_batch([(_cpu(1 << 16), 4096, 4096, _cpu(1, torch.int32),
+                                    _cpu(1, torch.int64))], _cpu(1 << 16)),
+    lambda E: E.encode_device_batch([(_cpu(4096), 4096, _cpu(256, torch.int16), _cpu(1 << 16),
+                                      _cpu(1, torch.int32))]),
+    lambda E: E.region_offsets_device(_cpu(4, torch.int32), _cpu(4, torch.int64),
+                                      _cpu(1, torch.int64)),
+    lambda E: E.count_chunks_device_batch([(_cpu(4096), 4096, _cpu(256, torch.int32))]),
+    lambda E: E.build_freq_device(_cpu(256, torch.int64), _cpu(256, torch.int16)),
+    lambda E: E.encode_device_adaptive_batch([(_cpu(4096), 4096, _cpu(256, torch.int16),
+                                               _cpu(1 << 16), _cpu(1, torch.int32))]),
+    lambda E: E.region_offsets_device_adaptive(_cpu(4, torch.int32), _cpu(4, torch.int64),
+                                               _cpu(1, torch.int64)),
+    lambda E: E.pack_device_adaptive_batch([(_cpu(1 << 16), 4096, 4096, _cpu(1, torch.int32),
+                                             _cpu(1, torch.int64), _cpu(256, torch.int16))],
+                                           _cpu(1 << 16)),
+    lambda E: E.tile_order_device(_cpu(16 * 64), 16, 64, 16),
+], ids=["count", "encode", "pack", "count_batch", "pack_batch", "encode_batch", "offsets",
+        "count_chunks", "build_freq", "encode_adaptive", "offsets_adaptive", "pack_adaptive",
+        "tile_order"])
+def test_plan_free_device_calls_refuse_host_tensors(E, call):
+    """A host tensor's address handed to a kernel would be dereferenced on
+    the GPU: each device call refuses one before reaching the library."""
+    _rejects(E, call, E, match="on a GPU is required")
+
+
+def test_chunk_count_refuses_a_zero_chunk_size(E):
+    assert E._n_chunks(4097, 4096) == 2 and E._n_chunks(0, 64) == 0
+    _rejects(E, E._n_chunks, 10, 0, match="chunk_symbols 0")

@@ -290,3 +290,45 @@ def test_device_tables_equal_the_oracle_rule(E):
         E.build_freq_device(cd, fd)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(fd.cpu().numpy().view(np.uint16), want[rows_ok])
+
+
+def test_device_calls_refuse_short_buffers(E):
+    """Buffers a kernel would overrun are refused before the launch (no
+    kernel runs in this test): word counts and offsets short of the chunk
+    count, a count table short of 256 entries, a per-chunk table array short
+    of 256 per chunk, the wrong element types, a buffer on another device."""
+    import torch
+    cuda = dict(device="cuda")
+    sym = torch.zeros(8192, dtype=torch.uint8, **cuda)            # 2 chunks of 4096
+    scratch = torch.empty(int(E.lib().entq_encode_device_scratch_bytes(8192, 4096)),
+                          dtype=torch.uint8, **cuda)
+    freq = np.zeros(256, np.uint16)
+    freq[0] = 4096
+    nw1 = torch.zeros(1, dtype=torch.int32, **cuda)
+    nw2 = torch.zeros(2, dtype=torch.int32, **cuda)
+    offs1 = torch.zeros(1, dtype=torch.int64, **cuda)
+    blob = torch.zeros(1 << 16, dtype=torch.uint8, **cuda)
+    cases = [
+        (lambda: E.encode_device(sym, 4096, freq, scratch, nw1), "n_words holds 1"),
+        (lambda: E.encode_device(sym, 4096, freq, scratch, nw2.to(torch.int64)), "dtype"),
+        (lambda: E.count_symbols_device(sym, torch.zeros(255, dtype=torch.int64, **cuda)),
+         "counts holds 255"),
+        (lambda: E.pack_device(scratch, 8192, 4096, nw2, offs1, blob), "offsets holds 1"),
+        (lambda: E.region_offsets_device(nw2, offs1, torch.zeros(1, dtype=torch.int64, **cuda)),
+         "offsets holds 1"),
+        (lambda: E.encode_device_adaptive_batch(
+            [(sym, 4096, torch.zeros(256, dtype=torch.int16, **cuda), scratch, nw2)]),
+         "freq holds 256"),
+        (lambda: E.count_chunks_device_batch([(sym, 4096, torch.zeros(256, dtype=torch.int32,
+                                                                      **cuda))]),
+         "counts holds 256"),
+        (lambda: E.build_freq_device(torch.zeros(512, dtype=torch.int64, **cuda),
+                                     torch.zeros(256, dtype=torch.int16, **cuda)),
+         "freq holds 256"),
+        (lambda: E.tile_order_device(sym, 16, 512, 16, out=torch.zeros(8192, dtype=torch.uint8)),
+         "on a GPU is required"),
+    ]
+    for call, match in cases:
+        with pytest.raises(E.EntqError, match=match):
+            call()
+    torch.cuda.synchronize()
