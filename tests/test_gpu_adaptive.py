@@ -85,6 +85,29 @@ def test_codes_and_bf16_match_the_oracle(E):
     np.testing.assert_array_equal(gst, st)
 
 
+def test_e4m3_every_code_including_nan(E):
+    """Every e4m3 code, the two NaN codes included, through the per-chunk-table
+    bf16 path (its stage holds each code in the low byte of a 16-bit slot):
+    equal to the oracle bit for bit, with negative, huge and small scales."""
+    _say("per-chunk tables: e4m3 all 256 codes incl. NaN")
+    sym = synth.random_bytes(64 * 512, 12)
+    sym[:256] = np.arange(256, dtype=np.uint8)
+    sym[4096:4352] = np.arange(256, dtype=np.uint8)[::-1]
+    sc = synth.uniform_f32(1e-3, 4.0, 64, synth.key(98, 3, 0, 1))
+    sc[:3] = np.array([1.0, -1.0, 3.0e38], np.float32)
+    sp = dict(name="e", kind=oracle.KIND_E4M3, rows=64, cols=512, chunk_symbols=4096,
+              symbols=sym, scales=sc)
+    c = oracle.encode_container_adaptive([sp])
+    p, blob = _plan(E, c)
+    want, st = oracle.decode_container_adaptive_bf16(c, sc)
+    assert (st == 0).all()
+    got, gst = _decode(E, p, blob, sym.size, E.OUT_BF16, sc)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(gst, st)
+    codes, _ = _decode(E, p, blob, sym.size, E.OUT_CODES)
+    np.testing.assert_array_equal(codes, sym)
+
+
 def test_corrupt_table_is_reported_per_chunk(E):
     sp = synth.random_int8_tensor(32, 512, 1.5, 152, 1024)
     c = oracle.encode_container_adaptive([sp])
