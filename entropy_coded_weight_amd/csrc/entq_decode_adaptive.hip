@@ -43,9 +43,15 @@ struct alignas(16) AdaptiveWave {
 
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
+// The kernel's whole LDS (maps, word rings, AdaptiveWave records) stays below
+// 61,440 bytes, so every map base (4096-aligned by its declaration) is at most
+// 57,344 and cum + map base (cum <= 4096) fits the entry's 16-bit high half.
+static_assert(kAdWaves * (kProbScale + 2 * kRingWords + sizeof(AdaptiveWave)) <= 61440,
+              "map bases and cum + map base must fit 16 bits");
+
 // One decode step with the chunk's own maps; otherwise as stream_step.
 // map_base: LDS address of the wave's slot -> symbol map (a multiple of
-// 4096, below 61440), so the map byte of slot x mod 4096 sits at
+// 4096, at most 57,344), so the map byte of slot x mod 4096 sits at
 // map_base | slot, and (that address) - (cum + map_base) = slot - cum.
 // slot_mask holds kProbScale - 1 (a register: the three-operand form takes no
 // literal). The stage slot holds the symbol itself (byte 0), the map byte
