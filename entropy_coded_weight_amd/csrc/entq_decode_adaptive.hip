@@ -177,8 +177,14 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
     const uint32_t map_base = __builtin_amdgcn_readfirstlane(lds_addr(SYM));
     const uint32_t slot_mask = kProbScale - 1;
     const uint32_t waves = gridDim.x * kAdWaves;
+    // Wave priority restarts at the top for each chunk and drops at a half,
+    // three quarters and seven eighths of its blocks, so the waves further
+    // behind in their chunks win issue (a priority over a wave's whole run
+    // of chunks, as in the shared-table kernel, was slower here).
+    Prio pr = {};
     for (uint32_t c = blockIdx.x * kAdWaves + wave; c < n_chunks; c += waves) {
         const DevChunk ch = chunks[c];
+        pr.start(ch.n_symbols / kBlockSyms);
         const DevTensor td = tensors[ch.tensor];
         const uint8_t *region = blob + ch.byte_offset;
         if (!build_maps(*reinterpret_cast<const uint2 *>(region + 8u * lane), W, SYM, map_base,
@@ -205,6 +211,7 @@ __global__ __launch_bounds__(kAdThreads) void decode_adaptive(
         const uint8_t *sm_g = (MODE == kModeSplit) ? signmant + ch.out_elem : nullptr;
         const uint32_t full_blocks = n / kBlockSyms;
         for (uint32_t b = 0; b < full_blocks; ++b) {
+            pr.tick();
             if (__builtin_expect(s.pos > s.hpos, 0)) ring_service(s, lane);
             // this lane's four sign+mantissa bytes of the block, in flight
             // while the block decodes
