@@ -198,15 +198,14 @@ __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_str
     // number of waves busy
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
     const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    // progress-based priority, restarted for each chunk: a wave starts each
+    // of its chunks at the top level and drops at a half, three quarters and
+    // seven eighths of that chunk's blocks (one countdown over the wave's
+    // whole run of chunks was 1 % slower)
     Prio pr = {};
-    if (PRIO) {
-        uint32_t my_blocks = 0;
-        for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width)
-            my_blocks += chunks[task.first_chunk + c].n_symbols / kBlockSyms;
-        pr.start(my_blocks);
-    }
     for (uint32_t c = wave; wave < width && c < task.n_chunks; c += width) {
         const DevChunk ch = chunks[task.first_chunk + c];
+        if (PRIO) pr.start(ch.n_symbols / kBlockSyms);
         const uint8_t *region = blob + ch.byte_offset;
         const uint32_t n = ch.n_symbols;
         uint32_t x = reinterpret_cast<const uint32_t *>(region)[lane];
