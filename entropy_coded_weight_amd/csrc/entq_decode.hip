@@ -194,10 +194,14 @@ __global__ __launch_bounds__(kThreads) ENTQ_TWO_WORKGROUPS_SGPRS void decode_str
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
     WaveStage &G = STG[wave];
-    // the task's chunks in rounds of equal width: every round keeps the same
-    // number of waves busy
+    // the task's chunks in rounds: every round keeps the same number of waves
+    // busy, except that a run of two or more rounds that 14 waves finish in as
+    // many rounds goes to 14 waves (on runs of 25-26 chunks, 14 busy waves
+    // decode 0.4 % faster than two equal rounds of 13; 15 or 16 are slower)
     const uint32_t rounds = (task.n_chunks + kWaves - 1) / kWaves;
-    const uint32_t width = (task.n_chunks + rounds - 1) / rounds;
+    const uint32_t even = (task.n_chunks + rounds - 1) / rounds;
+    const uint32_t width = (rounds > 1 && (task.n_chunks + 13) / 14 == rounds && even < 14) ? 14u
+                                                                                          : even;
     // progress-based priority, restarted for each chunk: a wave starts each
     // of its chunks at the top level and drops at a half, three quarters and
     // seven eighths of that chunk's blocks (one countdown over the wave's
